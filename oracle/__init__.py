@@ -1,0 +1,329 @@
+"""Plain CPU oracle for the fine-grained FP8 linear-layer path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``fine_grained_block_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``fgb_oracle.c`` (plain loops, fp64 where the method
+leaves the precision free); this module only marshals numpy arrays.  What each
+function computes, with the passage it follows:
+
+* ``e4m3_decode`` / ``e4m3_encode`` -- the E4M3 element format.  prime-rl
+  PR #4073, conventions table: scales divide by 448 and -0 (0x80) is kept apart
+  from +0; "RN" cast.  Read as OCP E4M3FN with ties-to-even and saturation.
+* ``quantize_1x128`` / ``quantize_128x128`` -- dynamic tile quantization with
+  scale = tile absmax / 448.  "scratch: the backward pass, unrolled", section
+  "What is asserted, and from where" (1x128 activation tiles, 128x128 weight
+  tiles); partial-sum-drift notes, section 3, row (a) (per-block absmax scale,
+  N_c = 128).
+* ``quantize_128x1`` / ``requant_128x1`` -- the 128x1 re-tiling of Wgrad's
+  transposed operands: same section of the "scratch" page (re-quantized 128x1
+  from the saved tensors; backward casts emit both tile orientations).
+* ``gemm_fprop`` / ``gemm_dgrad`` / ``gemm_wgrad`` -- block-scaled GEMM: each
+  128-long contraction segment's partial sum times s_a*s_b, accumulated at high
+  precision.  Partial-sum-drift notes, section 3 rows (a)-(b) and section 5;
+  output dtypes from the "scratch" page (Fprop/Dgrad BF16, Wgrad FP32).
+* ``*_grouped`` -- the same per expert over 128-aligned row segments (grouped
+  expert GEMMs with empty experts, prime-rl PR #4073 "Validation completed").
+
+The GEMM functions return the exact-to-fp64 value ``r`` and the absolute sum
+``aabs`` (sum of |terms|), not a rounded output; callers compare the GPU's
+BF16/FP32 output against ``r``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fgb_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+TILE = 128
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", "-fexcess-precision=standard",
+               "-Wall", "-Wextra", "-Wno-unused-parameter",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    F = ctypes.c_float
+    lib.orc_e4m3_decode.restype = ctypes.c_double
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_e4m3_encode.argtypes = [F]
+    lib.orc_bf16_round.restype = ctypes.c_uint16
+    lib.orc_bf16_round.argtypes = [ctypes.c_double]
+    lib.orc_quantize_1x128.argtypes = [P, I64, I64, I64, F, P, I64, P, I64]
+    lib.orc_quantize_128x1.argtypes = [P, I64, I64, I64, F, P, I64, P, I64]
+    lib.orc_quantize_128x128.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, P]
+    lib.orc_requant_128x1.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64]
+    lib.orc_gemm_block_scaled.argtypes = [I64, P, I64, P, I64, I64, I64,
+                                          P, I64, P, I64, I64, I64,
+                                          P, I64, P, I64, P, P]
+    lib.orc_e4m3_encode_array.argtypes = [P, I64, P]
+    lib.orc_e4m3_encode_bits_range.argtypes = [ctypes.c_uint32, I64, P]
+    lib.orc_e4m3_decode_array.argtypes = [P, I64, P]
+    lib.orc_bf16_round_array.argtypes = [P, I64, P]
+    lib.orc_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().orc_e4m3_decode_array(_ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(f) -> np.ndarray:
+    f = _c(f, np.float32)
+    out = np.empty(f.shape, np.uint8)
+    _load().orc_e4m3_encode_array(_ptr(f), f.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_bits_range(start: int, n: int) -> np.ndarray:
+    """Encode the fp32 values with bit patterns start .. start+n-1."""
+    out = np.empty(n, np.uint8)
+    _load().orc_e4m3_encode_bits_range(ctypes.c_uint32(start), n, _ptr(out))
+    return out
+
+
+def bf16_round(r) -> np.ndarray:
+    """Round float64 values to bfloat16 (RNE, one rounding); returns uint16 bits."""
+    r = _c(r, np.float64)
+    out = np.empty(r.shape, np.uint16)
+    _load().orc_bf16_round_array(_ptr(r), r.size, _ptr(out))
+    return out
+
+
+def bf16_to_float(bits) -> np.ndarray:
+    bits = _c(bits, np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Quantizers
+# --------------------------------------------------------------------------
+
+def quantize_1x128(x_bits, amax_floor: float = 0.0):
+    """x_bits: bf16 bit patterns [R, C].  Returns (q [R, C] uint8, s [ceil(C/128), R] float32)."""
+    x = _c(x_bits, np.uint16)
+    R, C = x.shape
+    q = np.empty((R, C), np.uint8)
+    s = np.empty((_cdiv(C, TILE), R), np.float32)
+    _load().orc_quantize_1x128(_ptr(x), R, C, C, ctypes.c_float(amax_floor),
+                               _ptr(q), C, _ptr(s), R)
+    return q, s
+
+
+def quantize_128x1(x_bits, amax_floor: float = 0.0):
+    """x_bits [R, C] -> (qT [C, roundup(R,128)] uint8 zero-padded, sT [ceil(R/128), C] float32)."""
+    x = _c(x_bits, np.uint16)
+    R, C = x.shape
+    Rp = _cdiv(R, TILE) * TILE
+    qT = np.empty((C, Rp), np.uint8)
+    sT = np.empty((_cdiv(R, TILE), C), np.float32)
+    _load().orc_quantize_128x1(_ptr(x), R, C, C, ctypes.c_float(amax_floor),
+                               _ptr(qT), Rp, _ptr(sT), C)
+    return qT, sT
+
+
+def quantize_128x128(w_bits, amax_floor: float = 0.0):
+    """w_bits [K, N] -> (q [K, N], qT [N, K], s [ceil(K/128), ceil(N/128)] float32)."""
+    w = _c(w_bits, np.uint16)
+    K, N = w.shape
+    q = np.empty((K, N), np.uint8)
+    qT = np.empty((N, K), np.uint8)
+    s = np.empty((_cdiv(K, TILE), _cdiv(N, TILE)), np.float32)
+    _load().orc_quantize_128x128(_ptr(w), K, N, N, ctypes.c_float(amax_floor),
+                                 _ptr(q), N, _ptr(qT), K, _ptr(s))
+    return q, qT, s
+
+
+def requant_128x1(q, s):
+    """1x128 codes q [R, C] with scales s [ceil(C/128), R] -> (qT [C, roundup(R,128)], sT [ceil(R/128), C])."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    R, C = q.shape
+    assert s.shape == (_cdiv(C, TILE), R)
+    Rp = _cdiv(R, TILE) * TILE
+    qT = np.empty((C, Rp), np.uint8)
+    sT = np.empty((_cdiv(R, TILE), C), np.float32)
+    _load().orc_requant_128x1(_ptr(q), R, C, C, _ptr(s), R, _ptr(qT), Rp, _ptr(sT), C)
+    return qT, sT
+
+
+# --------------------------------------------------------------------------
+# Block-scaled GEMMs
+# --------------------------------------------------------------------------
+
+def _sel(idx, n):
+    if idx is None:
+        return np.arange(n, dtype=np.int64)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert idx.ndim == 1 and (idx.size == 0 or (idx.min() >= 0 and idx.max() < n))
+    return idx
+
+
+def _gemm(Kc, A, sa, sa_sb, sa_si, sa_group, B, sb, sb_sb, sb_sj, sb_group, rows, cols):
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    sa = _c(sa, np.float32)
+    sb = _c(sb, np.float32)
+    rows = _sel(rows, A.shape[0])
+    cols = _sel(cols, B.shape[0])
+    out = np.empty((rows.size, cols.size), np.float64)
+    aabs = np.empty((rows.size, cols.size), np.float64)
+    if rows.size and cols.size:
+        _load().orc_gemm_block_scaled(Kc, _ptr(A), A.shape[1], _ptr(sa), sa_sb, sa_si, sa_group,
+                                      _ptr(B), B.shape[1], _ptr(sb), sb_sb, sb_sj, sb_group,
+                                      _ptr(rows), rows.size, _ptr(cols), cols.size,
+                                      _ptr(out), _ptr(aabs))
+    return out, aabs
+
+
+def gemm_fprop(qx, sx, qwT, sw, rows=None, cols=None):
+    """Y = X W.  qx [M, K] (1x128 scales sx [K/128, M]); qwT [N, K] (W's codes
+    transposed, 128x128 scales sw [K/128, N/128]).  Returns (r [m, n], aabs)."""
+    M, K = qx.shape
+    N = qwT.shape[0]
+    assert qwT.shape[1] == K and K % TILE == 0 and N % TILE == 0
+    assert sx.shape == (K // TILE, M) and sw.shape == (K // TILE, N // TILE)
+    return _gemm(K, qx, sx, M, 1, 1, qwT, sw, N // TILE, 1, TILE, rows, cols)
+
+
+def gemm_dgrad(qdy, sdy, qw, sw, rows=None, cols=None):
+    """dX = dY W^T.  qdy [M, N] (1x128 scales sdy [N/128, M]); qw [K, N] (W's
+    codes, scales sw [K/128, N/128]).  Returns (r [m, k], aabs)."""
+    M, N = qdy.shape
+    K = qw.shape[0]
+    assert qw.shape[1] == N and K % TILE == 0 and N % TILE == 0
+    assert sdy.shape == (N // TILE, M) and sw.shape == (K // TILE, N // TILE)
+    return _gemm(N, qdy, sdy, M, 1, 1, qw, sw, 1, N // TILE, TILE, rows, cols)
+
+
+def gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows=None, cols=None):
+    """dW = X^T dY in W's [K, N] shape.  qxT [K, Mp], sxT [ceil(M/128), K];
+    qdyT [N, Mp], sdyT [ceil(M/128), N]; contraction over the first M of Mp
+    columns (the rest is zero padding).  Returns (r [k, n], aabs)."""
+    K, Mp = qxT.shape
+    N = qdyT.shape[0]
+    assert qdyT.shape[1] == Mp and M <= Mp
+    nb = _cdiv(M, TILE)
+    assert sxT.shape[0] >= nb and sdyT.shape[0] >= nb
+    return _gemm(M, qxT, sxT, sxT.shape[1], 1, 1, qdyT, sdyT, sdyT.shape[1], 1, 1, rows, cols)
+
+
+# --------------------------------------------------------------------------
+# Grouped (MoE expert) GEMMs: the dense oracle applied per expert segment
+# --------------------------------------------------------------------------
+
+def _segments(offsets):
+    offsets = np.asarray(offsets, dtype=np.int64)
+    return [(int(offsets[e]), int(offsets[e + 1])) for e in range(offsets.size - 1)]
+
+
+def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, rows=None, cols=None):
+    """Per expert e: Y[o_e:o_{e+1}] = X[o_e:o_{e+1}] W_e.  qwT [E, N, K], sw [E, K/128, N/128].
+    Rows outside every segment give r = 0."""
+    R, K = qx.shape
+    N = qwT.shape[1]
+    rows = _sel(rows, R)
+    cols = _sel(cols, N)
+    out = np.zeros((rows.size, cols.size))
+    aabs = np.zeros((rows.size, cols.size))
+    for e, (a, b) in enumerate(_segments(offsets)):
+        pick = np.nonzero((rows >= a) & (rows < b))[0]
+        if pick.size == 0:
+            continue
+        r, aa = gemm_fprop(qx[a:b], sx[:, a:b], qwT[e], sw[e], rows[pick] - a, cols)
+        out[pick] = r
+        aabs[pick] = aa
+    return out, aabs
+
+
+def gemm_dgrad_grouped(offsets, qdy, sdy, qw, sw, rows=None, cols=None):
+    """Per expert e: dX[o_e:o_{e+1}] = dY[o_e:o_{e+1}] W_e^T.  qw [E, K, N], sw [E, K/128, N/128]."""
+    R, N = qdy.shape
+    K = qw.shape[1]
+    rows = _sel(rows, R)
+    cols = _sel(cols, K)
+    out = np.zeros((rows.size, cols.size))
+    aabs = np.zeros((rows.size, cols.size))
+    for e, (a, b) in enumerate(_segments(offsets)):
+        pick = np.nonzero((rows >= a) & (rows < b))[0]
+        if pick.size == 0:
+            continue
+        r, aa = gemm_dgrad(qdy[a:b], sdy[:, a:b], qw[e], sw[e], rows[pick] - a, cols)
+        out[pick] = r
+        aabs[pick] = aa
+    return out, aabs
+
+
+def gemm_wgrad_grouped(offsets, qxT, sxT, qdyT, sdyT, experts=None, rows=None, cols=None):
+    """Per expert e: dW_e = X_e^T dY_e over the segment's rows (128-aligned, zero padded).
+    qxT [K, R_pad], sxT [R_pad/128, K], qdyT [N, R_pad], sdyT [R_pad/128, N].
+    Returns (r [len(experts), k, n], aabs); an empty expert gives zeros."""
+    K = qxT.shape[0]
+    N = qdyT.shape[0]
+    segs = _segments(offsets)
+    experts = range(len(segs)) if experts is None else experts
+    rows = _sel(rows, K)
+    cols = _sel(cols, N)
+    out = np.zeros((len(experts), rows.size, cols.size))
+    aabs = np.zeros_like(out)
+    for i, e in enumerate(experts):
+        a, b = segs[e]
+        if b == a:
+            continue
+        assert a % TILE == 0 and b % TILE == 0
+        r, aa = gemm_wgrad(qxT[:, a:b], sxT[a // TILE:b // TILE], qdyT[:, a:b],
+                           sdyT[a // TILE:b // TILE], b - a, rows, cols)
+        out[i] = r
+        aabs[i] = aa
+    return out, aabs

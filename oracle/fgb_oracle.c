@@ -1,0 +1,375 @@
+/*
+ * Plain CPU oracle for the fine-grained FP8 linear-layer path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant generator with the GPU library, and the GPU
+ * library never calls it.
+ *
+ * Everything here is written for a reader to check against the method by
+ * eye: one element, one tile, one output at a time, in double precision
+ * wherever the method leaves the precision free.  Sources, by page:
+ *
+ *  - "scratch: the backward pass, unrolled" (deepseek-v3.ezyang.com),
+ *    section "What is asserted, and from where": all three GEMMs of a
+ *    linear take E4M3 operands with 1x128 activation tiles and 128x128
+ *    weight tiles and FP32-promoted accumulation; Fprop/Dgrad write BF16,
+ *    Wgrad writes FP32; the Wgrad operands are re-tiled 128x1 from the
+ *    saved tensors.
+ *  - "FP8 dynamic quantization partial-sum drift" (foosynaptic deepseek
+ *    tech notes), section 3 table row (a): per-block dynamic scales from the
+ *    in-block absmax, N_c = 128, partial sums multiplied by s_x*s_w; row (b)
+ *    and section 5: the partial sum of each 128-long segment is promoted
+ *    into an FP32 accumulator.
+ *  - prime-rl PR #4073, table "Trainer / vLLM quantization conventions":
+ *    scale denominator 448, negative zero 0x80 kept distinct from +0,
+ *    round-to-nearest online cast, FP32 scale containers on Hopper.
+ *
+ * The E4M3 element format is OCP E4M3FN (bias 7, no infinities, NaN =
+ * S.1111.111, largest finite 448): the only variant with both the 448 bound
+ * and a distinct -0 = 0x80 that the prime-rl conventions table states.
+ *
+ * Readings where the pages are silent (each is restated in the design
+ * notes): ties round to even; |x| > 448 saturates to +-448; the cast
+ * multiplies by fl32(448/amax) (one division per tile); an all-zero tile
+ * gets scale +0 and codes +-0; a partial edge tile takes the absmax over
+ * its valid elements; an optional amax floor is applied before /448.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_TILE 128
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                      */
+/* ------------------------------------------------------------------ */
+
+/* Round a double to the nearest integer, ties to the even integer. */
+static double rne_integer(double x)
+{
+    double lo = floor(x);
+    double frac = x - lo; /* exact for |x| < 2^52 */
+    if (frac > 0.5) return lo + 1.0;
+    if (frac < 0.5) return lo;
+    return (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;
+}
+
+/* E4M3FN decode: S EEEE MMM with bias 7.
+ *   E == 0           -> (-1)^S * M * 2^-9              (subnormal, includes +-0)
+ *   E == 15, M == 7  -> NaN
+ *   otherwise        -> (-1)^S * (1 + M/8) * 2^(E-7)                         */
+double orc_e4m3_decode(uint8_t u)
+{
+    int sign = (u >> 7) & 1;
+    int e = (u >> 3) & 15;
+    int m = u & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        mag = (double)m * ldexp(1.0, -9);
+    else
+        mag = (1.0 + (double)m / 8.0) * ldexp(1.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* E4M3FN encode of one fp32 value: round to nearest, ties to even;
+ * magnitudes above 448 (and infinities) saturate to 448; NaN -> S.1111.111;
+ * the sign bit of the input is always kept, so -0 and negative values that
+ * round to zero give 0x80. */
+uint8_t orc_e4m3_encode(float f)
+{
+    uint8_t sign = signbit(f) ? 0x80 : 0x00;
+    double a = fabs((double)f);
+    if (isnan(f)) return sign | 0x7F;
+    if (a > 448.0) return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: integer multiples of 2^-9; 8 * 2^-9 is the
+         * smallest normal 2^-6 whose code is 0x08, so m = 8 needs no carry */
+        double m = rne_integer(a * 512.0);
+        return sign | (uint8_t)m;
+    }
+    int e2;
+    frexp(a, &e2);       /* a = f * 2^e2, f in [0.5, 1) */
+    int ex = e2 - 1;     /* a in [2^ex, 2^(ex+1)) */
+    double m = rne_integer((a / ldexp(1.0, ex) - 1.0) * 8.0);
+    if (m == 8.0) {      /* rounding carried into the next binade */
+        m = 0.0;
+        ex += 1;
+    }
+    return sign | (uint8_t)(((ex + 7) << 3) | (int)m);
+}
+
+/* bfloat16 (8 significant bits, fp32 exponent range) -> float: exact. */
+float orc_bf16_to_float(uint16_t b)
+{
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* Round a double to bfloat16, to nearest with ties to even, in one step. */
+uint16_t orc_bf16_round(double r)
+{
+    uint16_t sign = signbit(r) ? 0x8000 : 0x0000;
+    double a = fabs(r);
+    if (isnan(r)) return sign | 0x7FC0;
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;             /* a in [2^ex, 2^(ex+1)) */
+    if (ex < -126) ex = -126;    /* subnormal bf16: quantum 2^-133 */
+    double ulp = ldexp(1.0, ex - 7);
+    double v = rne_integer(a / ulp) * ulp;
+    if (v >= ldexp(1.0, 128)) return sign | 0x7F80; /* overflow -> Inf */
+    float fv = (float)v;         /* exact: v has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &fv, sizeof bits);
+    return sign | (uint16_t)(bits >> 16);
+}
+
+/* ------------------------------------------------------------------ */
+/* One tile of dynamic quantization                                    */
+/* ------------------------------------------------------------------ */
+
+/* Quantize the n fp32 values of one tile.
+ *   a   = max |v|                        (exact)
+ *   a'  = max(a, amax_floor)
+ *   s   = fl32(a' / 448)                 (stored scale; dequant = s * dec(q))
+ *   inv = a' == 0 ? 0 : min(fl32(448 / a'), FLT_MAX)
+ *   q_i = enc(fl32(v_i * inv))
+ * A NaN anywhere in the tile makes a NaN.                              */
+static void quantize_tile(const float* v, int64_t n, float amax_floor,
+                          float* s_out, uint8_t* q_out)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float av = fabsf(v[i]);
+        if (isnan(av) || av > a) a = av;
+        if (isnan(a)) break;
+    }
+    if (amax_floor > a) a = amax_floor;
+    float s = a / 448.0f;
+    float inv;
+    if (a == 0.0f) {
+        inv = 0.0f;
+    } else {
+        inv = 448.0f / a;
+        if (inv > FLT_MAX) inv = FLT_MAX;
+    }
+    *s_out = s;
+    for (int64_t i = 0; i < n; ++i) {
+        float t = v[i] * inv;
+        q_out[i] = orc_e4m3_encode(t);
+    }
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+/* 1x128 tiling of a row-major bf16 matrix x[R][C] (leading dim ldx):
+ * tile (r, j) is x[r][128j .. min(128j+128, C)).
+ * q[r][c] (leading dim ldq) holds the codes; s[j][r] (leading dim lds)
+ * the scale of tile (r, j).                                           */
+void orc_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                        float amax_floor, uint8_t* q, int64_t ldq,
+                        float* s, int64_t lds)
+{
+    int64_t nb = ceil_div(C, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        float v[ORC_TILE];
+        uint8_t code[ORC_TILE];
+        for (int64_t j = 0; j < nb; ++j) {
+            int64_t c0 = j * ORC_TILE;
+            int64_t n = (C - c0 < ORC_TILE) ? C - c0 : ORC_TILE;
+            for (int64_t i = 0; i < n; ++i) v[i] = orc_bf16_to_float(x[r * ldx + c0 + i]);
+            quantize_tile(v, n, amax_floor, &s[j * lds + r], code);
+            for (int64_t i = 0; i < n; ++i) q[r * ldq + c0 + i] = code[i];
+        }
+    }
+}
+
+/* 128x1 tiling of x[R][C]: tile (i, c) is column c, rows 128i .. min(128i+128, R).
+ * The codes are written transposed, qT[c][r] (leading dim ldqT >= roundup(R,128)),
+ * with qT[c][r] = 0x00 for R <= r < roundup(R,128); sT[i][c] (leading dim ldsT)
+ * holds the scale of tile (i, c).                                      */
+static void quantize_128x1_f32(const float* xf, int64_t R, int64_t C, int64_t ldxf,
+                               float amax_floor, uint8_t* qT, int64_t ldqT,
+                               float* sT, int64_t ldsT)
+{
+    int64_t nb = ceil_div(R, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        float v[ORC_TILE];
+        uint8_t code[ORC_TILE];
+        for (int64_t i = 0; i < nb; ++i) {
+            int64_t r0 = i * ORC_TILE;
+            int64_t n = (R - r0 < ORC_TILE) ? R - r0 : ORC_TILE;
+            for (int64_t k = 0; k < n; ++k) v[k] = xf[(r0 + k) * ldxf + c];
+            quantize_tile(v, n, amax_floor, &sT[i * ldsT + c], code);
+            for (int64_t k = 0; k < ORC_TILE; ++k)
+                qT[c * ldqT + r0 + k] = (k < n) ? code[k] : 0x00;
+        }
+    }
+}
+
+void orc_quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                        float amax_floor, uint8_t* qT, int64_t ldqT,
+                        float* sT, int64_t ldsT)
+{
+    float* xf = (float*)malloc((size_t)(R * C > 0 ? R * C : 1) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) xf[r * C + c] = orc_bf16_to_float(x[r * ldx + c]);
+    quantize_128x1_f32(xf, R, C, C, amax_floor, qT, ldqT, sT, ldsT);
+    free(xf);
+}
+
+/* 128x128 tiling of a weight w[K][N] (K, N multiples of 128 not required
+ * here; edge tiles take the absmax over their valid elements).  Writes
+ * q[k][n] (if q != NULL), its transpose qT[n][k] (if qT != NULL) and
+ * s[i][j] = scale of tile (rows 128i.., cols 128j..), row length ceil(N/128). */
+void orc_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
+                          float amax_floor, uint8_t* q, int64_t ldq,
+                          uint8_t* qT, int64_t ldqT, float* s)
+{
+    int64_t kb = ceil_div(K, ORC_TILE), nb = ceil_div(N, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < kb * nb; ++t) {
+        int64_t i = t / nb, j = t % nb;
+        int64_t k0 = i * ORC_TILE, n0 = j * ORC_TILE;
+        int64_t kn = (K - k0 < ORC_TILE) ? K - k0 : ORC_TILE;
+        int64_t nn = (N - n0 < ORC_TILE) ? N - n0 : ORC_TILE;
+        float v[ORC_TILE * ORC_TILE];
+        uint8_t code[ORC_TILE * ORC_TILE];
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b)
+                v[a * nn + b] = orc_bf16_to_float(w[(k0 + a) * ldw + n0 + b]);
+        quantize_tile(v, kn * nn, amax_floor, &s[i * nb + j], code);
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b) {
+                if (q) q[(k0 + a) * ldq + n0 + b] = code[a * nn + b];
+                if (qT) qT[(n0 + b) * ldqT + k0 + a] = code[a * nn + b];
+            }
+    }
+}
+
+/* Re-tile a 1x128-quantized tensor (codes q[R][C], scales s[ceil(C/128)][R])
+ * to 128x1: dequantize v = fl32(dec(q) * s) (one fp32 rounding), then
+ * quantize v with 128x1 tiles exactly as orc_quantize_128x1 does.      */
+void orc_requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
+                       const float* s, int64_t lds,
+                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT)
+{
+    float* v = (float*)malloc((size_t)(R * C > 0 ? R * C : 1) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            double d = orc_e4m3_decode(q[r * ldq + c]);
+            float sc = s[(c / ORC_TILE) * lds + r];
+            v[r * C + c] = (float)(d * (double)sc); /* exact product, one rounding */
+        }
+    quantize_128x1_f32(v, R, C, C, 0.0f, qT, ldqT, sT, ldsT);
+    free(v);
+}
+
+/* ------------------------------------------------------------------ */
+/* Block-scaled GEMM                                                   */
+/* ------------------------------------------------------------------ */
+
+/* out[i][j] = sum_b  SA(i,b) * SB(j,b) * S_b(i,j),
+ *   S_b(i,j) = sum_{t in block b, t < K} dec(A[i][t]) * dec(B[j][t])
+ * with blocks of 128 along the contraction index t.  Both operands are
+ * stored contraction-contiguous: A[i][t] = A[i*lda + t], B[j][t] = B[j*ldb + t].
+ * Scales: SA(i,b) = sa[b*sa_sb + (i/sa_group)*sa_si], likewise SB.
+ *
+ * Every E4M3 value is an integer multiple of 2^-9 below 2^9, so every
+ * product is a multiple of 2^-18 below 2^18 and a 128-term S_b is exact
+ * in double.  The sum over blocks is in double (error ~1e-16 * aabs).
+ * aabs[i][j] = sum_b |SA*SB| * sum_t |dec*dec| bounds cancellation.
+ *
+ * Only the sub-grid rows[0..nrows) x cols[0..ncols) is computed; out and
+ * aabs are [nrows][ncols].                                           */
+void orc_gemm_block_scaled(int64_t K,
+                           const uint8_t* A, int64_t lda,
+                           const float* sa, int64_t sa_sb, int64_t sa_si, int64_t sa_group,
+                           const uint8_t* B, int64_t ldb,
+                           const float* sb, int64_t sb_sb, int64_t sb_sj, int64_t sb_group,
+                           const int64_t* rows, int64_t nrows,
+                           const int64_t* cols, int64_t ncols,
+                           double* out, double* aabs)
+{
+    double dec[256];
+    for (int u = 0; u < 256; ++u) dec[u] = orc_e4m3_decode((uint8_t)u);
+    int64_t nblk = ceil_div(K, ORC_TILE);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ii = 0; ii < nrows; ++ii) {
+        int64_t i = rows[ii];
+        for (int64_t jj = 0; jj < ncols; ++jj) {
+            int64_t j = cols[jj];
+            double r = 0.0, ra = 0.0;
+            for (int64_t b = 0; b < nblk; ++b) {
+                double sblk = 0.0, sabs = 0.0;
+                int64_t t0 = b * ORC_TILE;
+                int64_t t1 = (t0 + ORC_TILE < K) ? t0 + ORC_TILE : K;
+                for (int64_t t = t0; t < t1; ++t) {
+                    double p = dec[A[i * lda + t]] * dec[B[j * ldb + t]];
+                    sblk += p;
+                    sabs += fabs(p);
+                }
+                double scale = (double)sa[b * sa_sb + (i / sa_group) * sa_si] *
+                               (double)sb[b * sb_sb + (j / sb_group) * sb_sj];
+                r += scale * sblk;
+                ra += fabs(scale) * sabs;
+            }
+            out[ii * ncols + jj] = r;
+            aabs[ii * ncols + jj] = ra;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Vector helpers for the tests (one call per element, no shortcuts)   */
+/* ------------------------------------------------------------------ */
+
+void orc_e4m3_encode_array(const float* f, int64_t n, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(f[i]);
+}
+
+/* Encode the fp32 values whose bit patterns are start, start+1, ..., start+n-1. */
+void orc_e4m3_encode_bits_range(uint32_t start, int64_t n, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t bits = start + (uint32_t)i;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        out[i] = orc_e4m3_encode(f);
+    }
+}
+
+void orc_e4m3_decode_array(const uint8_t* u, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(u[i]);
+}
+
+void orc_bf16_round_array(const double* r, int64_t n, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(r[i]);
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
