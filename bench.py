@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = the whole FP8 linear-layer path, forward and backward,
+at the DeepSeek-V3 attention-projection shape X [4096, 7168], W [7168, 7168],
+dY [4096, 7168] (synthetic, seeded; inputs resident in HBM):
+
+  quantize X 1x128 -> quantize W 128x128 (both layouts) -> Fprop Y = X W (bf16)
+  -> quantize dY 1x128 -> Dgrad dX = dY W^T (bf16)
+  -> quantize dY 128x1 -> requant X 128x1 -> Wgrad dW = X^T dY (fp32)
+
+Prints one JSON line.  `value` is the step's GEMM throughput (3 x 2*M*N*K
+FLOP over the whole step time, quantization included) in TFLOP/s.  Per-kernel
+durations come from HIP events recorded around every launch on the stream the
+kernels run on, over the timed steps; `roofline` prices the dominant kernel
+against MI355X's dense FP8 MFMA peak, and `kernels` lists every kernel's rate
+against its own roofline (HBM for the quantizers).  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+FP8_PEAK = 5.0e15          # FLOP/s, MI355X dense FP8 MFMA
+T = 128
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="output rows per GEMM in the CPU-baseline sample (0 = auto, ~10-30 s)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(M, K, N):
+    """Bytes each kernel must move: every input read once, every output written once."""
+    nbK, nbN, nbM = K // T, N // T, -(-M // T)
+    Mp = nbM * T
+    return {
+        "quantize_1x128_x": M * K * 2 + M * K + nbK * M * 4,
+        "quantize_128x128_w": K * N * 2 + 2 * K * N + nbK * nbN * 4,
+        "quantize_1x128_dy": M * N * 2 + M * N + nbN * M * 4,
+        "quantize_128x1_dy": M * N * 2 + N * Mp + nbM * N * 4,
+        "requant_128x1_x": M * K + nbK * M * 4 + K * Mp + nbM * K * 4,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fine_grained_block_amd as fgb
+    from fine_grained_block_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    d = wl.linear_dsv3_attn()
+    M, K, N = d["M"], d["K"], d["N"]
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w, dy = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    Mp = -(-M // T) * T
+    buf = {
+        "qx": torch.empty((M, K), **u8), "sx": torch.empty((K // T, M), **f32),
+        "qw": torch.empty((K, N), **u8), "qwT": torch.empty((N, K), **u8), "sw": torch.empty((K // T, N // T), **f32),
+        "y": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        "qdy": torch.empty((M, N), **u8), "sdy": torch.empty((N // T, M), **f32),
+        "dx": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+        "qdyT": torch.empty((N, Mp), **u8), "sdyT": torch.empty((Mp // T, N), **f32),
+        "qxT": torch.empty((K, Mp), **u8), "sxT": torch.empty((Mp // T, K), **f32),
+        "dw": torch.empty((K, N), **f32),
+    }
+    b = buf
+    kernels = [
+        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"])),
+        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"])),
+        ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"])),
+        ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"])),
+        ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"])),
+        ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"])),
+        ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"])),
+        ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"])),
+    ]
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(kernels):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: per-kernel HIP events on the kernels' stream (torch's current stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in kernels] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(ev[s])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    per_kernel_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+                     for i, (name, _) in enumerate(kernels)}
+
+    gemm_flop = 2.0 * M * N * K
+    step_flop = 3 * gemm_flop
+    value = step_flop / (ms_per_step * 1e-3) / 1e12
+    abytes = algorithmic_bytes(M, K, N)
+    kinfo = {}
+    for name, ms in per_kernel_ms.items():
+        if name.startswith("gemm"):
+            rate = gemm_flop / (ms * 1e-3)
+            kinfo[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(rate / 1e12, 1),
+                           "frac_fp8_peak": round(rate / FP8_PEAK, 4)}
+        else:
+            rate = abytes[name] / (ms * 1e-3)
+            kinfo[name] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
+                           "frac_hbm_peak": round(rate / HBM_PEAK, 4), "bytes": abytes[name]}
+    gemms = {k: v for k, v in per_kernel_ms.items() if k.startswith("gemm")}
+    dom = max(gemms, key=gemms.get)
+    dom_rate = gemm_flop / (gemms[dom] * 1e-3)
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_rate / 1e12, 1),
+                "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(dom_rate / FP8_PEAK, 4),
+                "traffic": None}
+    quant_ms = sum(v for k, v in per_kernel_ms.items() if not k.startswith("gemm"))
+    quant_bytes = sum(abytes.values())
+
+    out = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak) + quant GB/s (% HBM) at 1 GPU",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 x e4m3 -> fp32 accumulate (bf16 in/out, fp32 dW)",
+        "data": "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)",
+        "config": {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]",
+                   "M": M, "K": K, "N": N, "gemm_flop_per_step": step_flop,
+                   "quant_bytes_per_step": quant_bytes},
+        "quant_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quant_frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / HBM_PEAK, 4),
+        "roofline": roofline,
+        "kernels": kinfo,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(d, rows_arg):
+    """The CPU oracle, as it stands, on a bounded sample of the same step: the
+    three quantizers of X/dY and W on full tensors, then Fprop, Dgrad and Wgrad
+    on a sample of output rows (all columns, full contraction).  Reported as the
+    oracle's GEMM throughput in TFLOP/s over the sample, plus its quant GB/s."""
+    import numpy as np
+
+    import oracle
+    M, K, N = d["M"], d["K"], d["N"]
+    t0 = time.perf_counter()
+    qx, sx = oracle.quantize_1x128(d["x"])
+    q, qT, sw = oracle.quantize_128x128(d["w"])
+    qdy, sdy = oracle.quantize_1x128(d["dy"])
+    qdyT, sdyT = oracle.quantize_128x1(d["dy"])
+    qxT, sxT = oracle.requant_128x1(qx, sx)
+    tq = time.perf_counter() - t0
+    qbytes = sum(algorithmic_bytes(M, K, N).values())
+    # size the GEMM sample so the oracle works ~10-30 s: probe one row first
+    rows_n = rows_arg
+    if rows_n <= 0:
+        t1 = time.perf_counter()
+        oracle.gemm_fprop(qx, sx, qT, sw, rows=np.array([0]))
+        per_row = max(time.perf_counter() - t1, 1e-4)
+        rows_n = int(max(8, min(512, 5.0 / per_row)))
+    g = np.random.default_rng(0)
+    rows = np.sort(g.choice(M, size=rows_n, replace=False))
+    rowsK = np.sort(g.choice(K, size=rows_n, replace=False))
+    t2 = time.perf_counter()
+    oracle.gemm_fprop(qx, sx, qT, sw, rows=rows)
+    oracle.gemm_dgrad(qdy, sdy, q, sw, rows=rows)
+    oracle.gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows=rowsK)
+    tg = time.perf_counter() - t2
+    flop = 2.0 * rows_n * N * K + 2.0 * rows_n * K * N + 2.0 * rows_n * N * M
+    return {"value": round(flop / tg / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"Fprop/Dgrad/Wgrad on {rows_n} output rows each (all columns, full contraction) "
+                      f"of the same step; {tg:.1f} s",
+            "quant_GBps": round(qbytes / tq / 1e9, 3), "quant_s": round(tq, 2)}
+
+
+if __name__ == "__main__":
+    main()

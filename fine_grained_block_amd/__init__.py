@@ -1,0 +1,252 @@
+"""fine_grained_block_amd -- fine-grained block-scaled FP8 linear layers on MI355X.
+
+Thin Python binding over ``libfgb.so`` (C ABI in ``include/fgb.h``).  Every
+function here only marshals torch tensors into pointers, leading dimensions
+and the current HIP stream; all computation runs in the library's HIP kernels.
+There is no fallback: if ``libfgb.so`` is missing or a call fails, an
+exception is raised.
+
+Layouts (all row-major, bf16 = ``torch.bfloat16``, E4M3 codes = ``torch.uint8``,
+scales = ``torch.float32``):
+
+* ``quantize_1x128(x[R, C])`` -> ``q[R, C]``, ``s[ceil(C/128), R]``
+* ``quantize_128x1(x[R, C])`` -> ``qT[C, roundup(R,128)]``, ``sT[ceil(R/128), C]``
+* ``quantize_128x128(w[K, N])`` -> ``q[K, N]``, ``qT[N, K]``, ``s[K/128, N/128]``
+* ``requant_128x1(q[R, C], s)`` -> ``qT``, ``sT`` as ``quantize_128x1``
+* ``gemm_fprop(qx, sx, qwT, sw)`` -> ``y[M, N]`` bf16 (Y = X W)
+* ``gemm_dgrad(qdy, sdy, qw, sw)`` -> ``dx[M, K]`` bf16 (dX = dY W^T)
+* ``gemm_wgrad(qxT, sxT, qdyT, sdyT, M)`` -> ``dw[K, N]`` fp32 (dW = X^T dY)
+* ``gemm_*_grouped(offsets, ...)`` -- the same per expert segment.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfgb.so")
+TILE = 128
+
+STATUS = {0: "FGB_OK", -1: "FGB_E_NULL", -2: "FGB_E_SHAPE", -3: "FGB_E_ALIGN", -4: "FGB_E_LD",
+          -5: "FGB_E_UNSUPPORTED", -6: "FGB_E_HIP", -7: "FGB_E_ARG"}
+
+# name -> ctypes argument types (P = pointer, I = int64, F = float, N = int)
+_P, _I, _F, _N = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+SIGNATURES = {
+    "fgb_quantize_1x128": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
+    "fgb_quantize_128x1": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
+    "fgb_quantize_128x128": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _P],
+    "fgb_requant_128x1": [_P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P],
+    "fgb_gemm_fprop": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
+    "fgb_gemm_dgrad": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
+    "fgb_gemm_wgrad": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _N, _P],
+    "fgb_gemm_fprop_grouped": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
+    "fgb_gemm_dgrad_grouped": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
+    "fgb_gemm_wgrad_grouped": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _N, _P],
+    "fgb_status_string": [_N],
+    "fgb_version": [],
+}
+
+
+class FgbError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfgb.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FgbError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m fine_grained_block_amd.build` (no fallback path exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.fgb_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        msg = lib().fgb_status_string(status).decode()
+        raise FgbError(f"{name}: {STATUS.get(status, status)} ({msg})")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _rows(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise FgbError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise FgbError(f"{name}: expected a device tensor")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise FgbError(f"{name}: expected a 2-D row-major tensor")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def version() -> int:
+    return lib().fgb_version()
+
+
+# ---------------------------------------------------------------------------
+# Quantizers
+# ---------------------------------------------------------------------------
+
+def quantize_1x128(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None):
+    R, C = x.shape
+    ldx = _rows(x, torch.bfloat16, "x")
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device)
+    _check(lib().fgb_quantize_1x128(_ptr(x), R, C, ldx, amax_floor, _ptr(q), _rows(q, torch.uint8, "q"),
+                                    _ptr(s), _rows(s, torch.float32, "s"), _stream(x)), "quantize_1x128")
+    return q, s
+
+
+def quantize_128x1(x: torch.Tensor, amax_floor: float = 0.0, qT=None, sT=None):
+    R, C = x.shape
+    ldx = _rows(x, torch.bfloat16, "x")
+    if qT is None:
+        qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=x.device)
+    if sT is None:
+        sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=x.device)
+    _check(lib().fgb_quantize_128x1(_ptr(x), R, C, ldx, amax_floor, _ptr(qT), _rows(qT, torch.uint8, "qT"),
+                                    _ptr(sT), _rows(sT, torch.float32, "sT"), _stream(x)), "quantize_128x1")
+    return qT, sT
+
+
+def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = True, want_qT: bool = True,
+                     q=None, qT=None, s=None):
+    K, N = w.shape
+    ldw = _rows(w, torch.bfloat16, "w")
+    if want_q and q is None:
+        q = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+    if want_qT and qT is None:
+        qT = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty((_cdiv(K, TILE), _cdiv(N, TILE)), dtype=torch.float32, device=w.device)
+    ldq = _rows(q, torch.uint8, "q") if q is not None else 0
+    ldqT = _rows(qT, torch.uint8, "qT") if qT is not None else 0
+    _check(lib().fgb_quantize_128x128(_ptr(w), K, N, ldw, amax_floor, _ptr(q), ldq, _ptr(qT), ldqT,
+                                      _ptr(s), _stream(w)), "quantize_128x128")
+    return q, qT, s
+
+
+def requant_128x1(q: torch.Tensor, s: torch.Tensor, qT=None, sT=None):
+    R, C = q.shape
+    ldq = _rows(q, torch.uint8, "q")
+    if qT is None:
+        qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=q.device)
+    if sT is None:
+        sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=q.device)
+    _check(lib().fgb_requant_128x1(_ptr(q), R, C, ldq, _ptr(s), _rows(s, torch.float32, "s"),
+                                   _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT),
+                                   _rows(sT, torch.float32, "sT"), _stream(q)), "requant_128x1")
+    return qT, sT
+
+
+# ---------------------------------------------------------------------------
+# GEMMs
+# ---------------------------------------------------------------------------
+
+def gemm_fprop(qx, sx, qwT, sw, y=None):
+    M, K = qx.shape
+    N = qwT.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
+    _check(lib().fgb_gemm_fprop(M, N, K, _ptr(qx), _rows(qx, torch.uint8, "qx"), _ptr(sx),
+                                _rows(sx, torch.float32, "sx") if K else M, _ptr(qwT),
+                                _rows(qwT, torch.uint8, "qwT"), _ptr(sw), _ptr(y),
+                                _rows(y, torch.bfloat16, "y"), _stream(qx)), "gemm_fprop")
+    return y
+
+
+def gemm_dgrad(qdy, sdy, qw, sw, dx=None):
+    M, N = qdy.shape
+    K = qw.shape[0]
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=qdy.device)
+    _check(lib().fgb_gemm_dgrad(M, K, N, _ptr(qdy), _rows(qdy, torch.uint8, "qdy"), _ptr(sdy),
+                                _rows(sdy, torch.float32, "sdy") if N else M, _ptr(qw),
+                                _rows(qw, torch.uint8, "qw"), _ptr(sw), _ptr(dx),
+                                _rows(dx, torch.bfloat16, "dx"), _stream(qdy)), "gemm_dgrad")
+    return dx
+
+
+def gemm_wgrad(qxT, sxT, qdyT, sdyT, M: int, dw=None, accumulate: bool = False):
+    K = qxT.shape[0]
+    N = qdyT.shape[0]
+    if dw is None:
+        dw = torch.empty((K, N), dtype=torch.float32, device=qxT.device)
+    _check(lib().fgb_gemm_wgrad(K, N, M, _ptr(qxT), _rows(qxT, torch.uint8, "qxT"), _ptr(sxT),
+                                _rows(sxT, torch.float32, "sxT") if M else K, _ptr(qdyT),
+                                _rows(qdyT, torch.uint8, "qdyT"), _ptr(sdyT),
+                                _rows(sdyT, torch.float32, "sdyT") if M else N, _ptr(dw),
+                                _rows(dw, torch.float32, "dw"), 1 if accumulate else 0,
+                                _stream(qxT)), "gemm_wgrad")
+    return dw
+
+
+def _offsets(offsets: torch.Tensor):
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
+        raise FgbError("offsets: expected a 1-D int32 device tensor of E+1 entries")
+    return offsets.numel() - 1
+
+
+def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, y=None):
+    E = _offsets(offsets)
+    R_pad, K = qx.shape
+    N = qwT.shape[1]
+    if y is None:
+        y = torch.empty((R_pad, N), dtype=torch.bfloat16, device=qx.device)
+    for t in (qx, sx, qwT, sw, y):
+        assert t.is_contiguous()
+    _check(lib().fgb_gemm_fprop_grouped(E, _ptr(offsets), R_pad, N, K, _ptr(qx), _ptr(sx), _ptr(qwT),
+                                        _ptr(sw), _ptr(y), _stream(qx)), "gemm_fprop_grouped")
+    return y
+
+
+def gemm_dgrad_grouped(offsets, qdy, sdy, qw, sw, dx=None):
+    E = _offsets(offsets)
+    R_pad, N = qdy.shape
+    K = qw.shape[1]
+    if dx is None:
+        dx = torch.empty((R_pad, K), dtype=torch.bfloat16, device=qdy.device)
+    for t in (qdy, sdy, qw, sw, dx):
+        assert t.is_contiguous()
+    _check(lib().fgb_gemm_dgrad_grouped(E, _ptr(offsets), R_pad, K, N, _ptr(qdy), _ptr(sdy), _ptr(qw),
+                                        _ptr(sw), _ptr(dx), _stream(qdy)), "gemm_dgrad_grouped")
+    return dx
+
+
+def gemm_wgrad_grouped(offsets, qxT, sxT, qdyT, sdyT, dw=None, accumulate: bool = False):
+    E = _offsets(offsets)
+    K, R_pad = qxT.shape
+    N = qdyT.shape[0]
+    if dw is None:
+        dw = torch.empty((E, K, N), dtype=torch.float32, device=qxT.device)
+    for t in (qxT, sxT, qdyT, sdyT, dw):
+        assert t.is_contiguous()
+    _check(lib().fgb_gemm_wgrad_grouped(E, _ptr(offsets), R_pad, K, N, _ptr(qxT), _ptr(sxT), _ptr(qdyT),
+                                        _ptr(sdyT), _ptr(dw), 1 if accumulate else 0, _stream(qxT)),
+           "gemm_wgrad_grouped")
+    return dw

@@ -1,0 +1,53 @@
+// Internal launch interface of libfgb: the C ABI (abi.cpp) validates arguments
+// and calls these; the kernels live in quant.hip and gemm.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgb {
+
+// ----------------------------- quantizers ---------------------------------
+hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                                 float amax_floor, uint8_t* q, int64_t ldq,
+                                 float* s, int64_t lds, hipStream_t stream);
+
+enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2 };
+
+// 128x128 tile kernels over a [R][C] input:
+//   kTile128x1:   bf16 in, per-column 128-row scales, transposed codes out (qT, sT)
+//   kTile128x128: bf16 in, one scale per tile, q and/or qT out, s [R/128][C/128]
+//   kTileRequant: E4M3 + 1x128 scales in, then as kTile128x1
+hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
+                          const float* s_in, int64_t lds_in, float amax_floor,
+                          uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                          float* s_out, int64_t lds_out, hipStream_t stream);
+
+// ------------------------------- GEMMs -------------------------------------
+// out[m][n] = sum_b SA(m,b) * SB(n,b) * sum_{t in block b} dec(A[m][t]) dec(B[n][t])
+//   A [M][lda], B [N][ldb]: both contraction-contiguous E4M3 codes
+//   SA(m,b) = sa[b*sa_ld + m]
+//   SB(n,b) = sb[b*sb_kb + n]                 (outer-product scales, Wgrad)
+//           = sb[b*sb_kb + (n/128)*sb_n]      (128x128 weight tiles, Fprop/Dgrad)
+enum GemmKind { kFprop = 0, kDgrad = 1, kWgrad = 2 };
+
+struct GemmArgs {
+    int64_t M = 0, N = 0;       // output rows / columns
+    int64_t nkb = 0;            // number of 128-long contraction blocks
+    const uint8_t* A = nullptr; int64_t lda = 0;
+    const uint8_t* B = nullptr; int64_t ldb = 0;
+    const float* sa = nullptr;  int64_t sa_ld = 0;
+    const float* sb = nullptr;  int64_t sb_kb = 0, sb_n = 0;
+    void* out = nullptr;        int64_t ldo = 0;
+    int accumulate = 0;         // Wgrad: out += result
+    // grouped forms
+    const int32_t* offsets = nullptr;  // device, E+1 entries
+    int64_t E = 0;
+    int64_t b_expert_stride = 0;       // elements of B per expert   (M-grouped)
+    int64_t sb_expert_stride = 0;      // floats of sb per expert    (M-grouped)
+    int64_t out_expert_stride = 0;     // elements of out per expert (K-grouped)
+};
+
+hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& args, hipStream_t stream);
+
+}  // namespace fgb

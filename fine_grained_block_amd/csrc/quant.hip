@@ -1,0 +1,234 @@
+// Dynamic E4M3 tile quantization kernels for gfx950.
+//
+// Tile rule ("scratch: the backward pass, unrolled", section "What is asserted,
+// and from where": 1x128 activation tiles, 128x128 weight tiles, Wgrad
+// operands re-tiled 128x1; partial-sum-drift notes, section 3 row (a): scale
+// from the in-block absmax; prime-rl PR #4073 conventions table: /448, -0):
+//   a = max(absmax(tile), floor); s = fl32(a/448); inv = a ? min(fl32(448/a), FLT_MAX) : 0
+//   q = e4m3_rne_sat(fl32(x * inv))
+//
+// All kernels are HBM-bound.  The absmax is an integer max over |bits|
+// (exact, independent of denormal modes); scale and inverse are IEEE fp32
+// divisions, one pair per tile; the cast is the hardware v_cvt_pk_fp8_f32.
+
+#include "device_common.hpp"
+#include "fgb_internal.hpp"
+
+namespace fgb {
+
+// ---------------------------------------------------------------------------
+// 1x128.  A block of 256 threads covers 64 rows of one 128-column block; each
+// group of 16 lanes owns one row at a time (8 bf16 = 16 B per lane, so a
+// group reads the tile's 256 contiguous bytes) and reduces its absmax with
+// DPP inside the 16-lane row.
+// ---------------------------------------------------------------------------
+constexpr int kQ1Rows = 64;
+
+__global__ __launch_bounds__(256) void k_quantize_1x128(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds)
+{
+    const int lane16 = threadIdx.x & 15;
+    const int grp = threadIdx.x >> 4;
+    const int64_t rb = (int64_t)blockIdx.x * kQ1Rows;
+    const int64_t j = blockIdx.y;
+    const int64_t c = j * kTile + lane16 * 8;
+    const bool cok = c < C;
+
+    uint4 v[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int64_t r = rb + grp + 16 * it;
+        v[it] = (cok && r < R) ? ld16(x + r * ldx + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int64_t r = rb + grp + 16 * it;
+        const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+        u16x2 m2 = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
+        uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
+        m = max16(m);
+        const float a = fmaxf(__uint_as_float(m << 16), amax_floor);
+        float sc, inv;
+        tile_scale(a, sc, inv);
+        const uint32_t o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv,
+                                   bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
+        const uint32_t o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv,
+                                   bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
+        if (cok && r < R) {
+            st8(q + r * ldq + c, make_uint2(o0, o1));
+            if (lane16 == 0) s[j * lds + r] = sc;
+        }
+    }
+}
+
+hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                                 float amax_floor, uint8_t* q, int64_t ldq,
+                                 float* s, int64_t lds, hipStream_t stream)
+{
+    dim3 grid((unsigned)((R + kQ1Rows - 1) / kQ1Rows), (unsigned)((C + kTile - 1) / kTile));
+    hipLaunchKernelGGL(k_quantize_1x128, grid, dim3(256), 0, stream,
+                       x, R, C, ldx, amax_floor, q, ldq, s, lds);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 128x128-element tile kernels (128x1 columns, 128x128 weight tiles, requant).
+// Block = 256 threads over rows [r0, r0+128) x columns [c0, c0+128).  Thread t
+// holds an 8x8 patch: columns c0 + 8*(t%16) .. +8, rows r0 + 8*(t/16) .. +8.
+// Column maxima combine the 4 patches of a wave with lane swizzles and the 4
+// waves through LDS.  Transposed codes are staged in LDS as [column][row] so
+// every global store writes whole 16-byte pieces of 128-byte qT rows.
+// ---------------------------------------------------------------------------
+constexpr int kTrStride = 136;   // bytes per staged qT row (128 + 8 to spread banks)
+
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_tile128(
+    const void* __restrict__ in, int64_t R, int64_t C, int64_t ldin,
+    const float* __restrict__ s_in, int64_t lds_in, float amax_floor,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
+    float* __restrict__ s_out, int64_t lds_out)
+{
+    __shared__ uint32_t red[4][kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kTrStride];
+
+    const int t = threadIdx.x;
+    const int cg = t & 15, rg = t >> 4, wave = t >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * kTile;
+    const int64_t c0 = (int64_t)blockIdx.y * kTile;
+    const int64_t cc = c0 + cg * 8;
+    const bool cok = cc < C;
+
+    float v[8][8];  // [row i][column k]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + rg * 8 + i;
+        const bool ok = cok && r < R;
+        if constexpr (MODE == kTileRequant) {
+            const uint8_t* p = static_cast<const uint8_t*>(in);
+            const uint2 w = ok ? ld8(p + r * ldin + cc) : make_uint2(0u, 0u);
+            const float sr = ok ? s_in[(int64_t)blockIdx.y * lds_in + r] : 0.0f;
+            const float2 d0 = e4m3x2_decode<false>(w.x), d1 = e4m3x2_decode<true>(w.x);
+            const float2 d2 = e4m3x2_decode<false>(w.y), d3 = e4m3x2_decode<true>(w.y);
+            v[i][0] = d0.x * sr; v[i][1] = d0.y * sr; v[i][2] = d1.x * sr; v[i][3] = d1.y * sr;
+            v[i][4] = d2.x * sr; v[i][5] = d2.y * sr; v[i][6] = d3.x * sr; v[i][7] = d3.y * sr;
+        } else {
+            const uint16_t* p = static_cast<const uint16_t*>(in);
+            const uint4 w = ok ? ld16(p + r * ldin + cc) : make_uint4(0u, 0u, 0u, 0u);
+            v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x); v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
+            v[i][4] = bf16_lo(w.z); v[i][5] = bf16_hi(w.z); v[i][6] = bf16_lo(w.w); v[i][7] = bf16_hi(w.w);
+        }
+    }
+
+    float inv[8];
+    if constexpr (MODE == kTile128x128) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
+        m = max16(m);
+        m = max(m, shfl_xor_u32(m, 16));
+        m = max(m, shfl_xor_u32(m, 32));
+        if ((t & 63) == 0) red[wave][0] = m;
+        __syncthreads();
+        m = max(max(red[0][0], red[1][0]), max(red[2][0], red[3][0]));
+        const float a = fmaxf(__uint_as_float(m), amax_floor);
+        float sc, iv;
+        tile_scale(a, sc, iv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) inv[k] = iv;
+        if (t == 0) s_out[(int64_t)blockIdx.x * lds_out + blockIdx.y] = sc;
+    } else {
+        uint32_t mc[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i][k]));
+            m = max(m, shfl_xor_u32(m, 16));
+            m = max(m, shfl_xor_u32(m, 32));
+            mc[k] = m;
+        }
+        if ((t & 63) < 16) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) red[wave][cg * 8 + k] = mc[k];
+        }
+        __syncthreads();
+        float sc[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int col = cg * 8 + k;
+            const uint32_t m = max(max(red[0][col], red[1][col]), max(red[2][col], red[3][col]));
+            const float a = fmaxf(__uint_as_float(m), amax_floor);
+            tile_scale(a, sc[k], inv[k]);
+        }
+        if (rg == 0 && cok) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s_out[(int64_t)blockIdx.x * lds_out + cc + k] = sc[k];
+        }
+    }
+
+    // Row-major codes (128x128 weights, q != nullptr): 8 bytes per patch row.
+    if constexpr (MODE == kTile128x128) {
+        if (q != nullptr) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t r = r0 + rg * 8 + i;
+                const uint32_t o0 = e4m3x4(v[i][0] * inv[0], v[i][1] * inv[1], v[i][2] * inv[2], v[i][3] * inv[3]);
+                const uint32_t o1 = e4m3x4(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7]);
+                if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
+            }
+        }
+        if (qT == nullptr) return;
+    }
+
+    // Transposed codes: column k of the patch -> 8 row bytes, staged in LDS.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
+        const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
+        *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+    // 128 staged rows of 128 bytes; 8 threads per row, 16 bytes each, 4 passes.
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = p * 32 + (t >> 3);
+        const int seg = t & 7;
+        const int64_t c = c0 + row;
+        const uint2 a = *reinterpret_cast<const uint2*>(&tr[row * kTrStride + seg * 16]);
+        const uint2 b = *reinterpret_cast<const uint2*>(&tr[row * kTrStride + seg * 16 + 8]);
+        if (c < C) st16(qT + c * ldqT + r0 + seg * 16, make_uint4(a.x, a.y, b.x, b.y));
+    }
+}
+
+hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
+                          const float* s_in, int64_t lds_in, float amax_floor,
+                          uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                          float* s_out, int64_t lds_out, hipStream_t stream)
+{
+    dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
+    switch (mode) {
+    case kTile128x1:
+        hipLaunchKernelGGL(k_tile128<kTile128x1>, grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out);
+        break;
+    case kTile128x128:
+        hipLaunchKernelGGL(k_tile128<kTile128x128>, grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out);
+        break;
+    case kTileRequant:
+        hipLaunchKernelGGL(k_tile128<kTileRequant>, grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fgb

@@ -1,0 +1,216 @@
+/*
+ * fgb.h -- fine-grained block-scaled FP8 linear layers on MI355X (gfx950).
+ *
+ * C ABI of libfgb.so.  The library computes the FP8 path of one linear layer:
+ * dynamic E4M3 tile quantization (1x128 activation/gradient tiles, 128x128
+ * weight tiles, 128x1 re-tiling of Wgrad's transposed operands) and the
+ * block-scaled GEMM that multiplies each 128-long contraction segment's FP8
+ * partial sum by s_a * s_b and accumulates in FP32, for Fprop (Y = X W, BF16),
+ * Dgrad (dX = dY W^T, BF16) and Wgrad (dW = X^T dY, FP32), dense and grouped
+ * per MoE expert.
+ *
+ * Sources (by page and section):
+ *   [scratch]  "scratch: the backward pass, unrolled" (deepseek-v3.ezyang.com),
+ *              section "What is asserted, and from where".
+ *   [drift]    "FP8 dynamic quantization partial-sum drift" (foosynaptic
+ *              deepseek tech notes), section 3 table rows (a)/(b), section 5.
+ *   [conv]     prime-rl PR #4073, table "Trainer / vLLM quantization
+ *              conventions" (448 denominator, -0 = 0x80, RN cast, FP32
+ *              scale containers).
+ *   [grouped]  prime-rl PR #4073, "Validation completed" (grouped/empty
+ *              experts) and TransformerEngine PR #3573 "Changes" (per-group
+ *              GEMM paths).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers on the current HIP device; the
+ *     caller owns every buffer.  No call allocates, frees, synchronizes or
+ *     keeps state between calls; calls are reentrant and thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; the call returns before the work finishes.
+ *   - Matrices are row-major with an explicit leading dimension in ELEMENTS
+ *     (bf16 = uint16_t bit patterns, E4M3 codes = uint8_t, scales = float).
+ *   - Element format: E4M3 = OCP E4M3FN (bias 7, max 448, no infinities,
+ *     NaN = S.1111.111, -0 = 0x80 distinct from +0).  Casts round to nearest,
+ *     ties to even, and saturate to +-448; the sign of zero is kept.
+ *   - Tile quantization of a tile T (128, or 128x128 elements; fewer for a
+ *     partial edge tile, over its valid elements only):
+ *         a   = max(max_{x in T} |x|, amax_floor)
+ *         s   = fl32(a / 448)                        (the stored scale)
+ *         inv = (a == 0) ? 0 : min(fl32(448 / a), FLT_MAX)
+ *         q   = e4m3(fl32(x * inv))                  (dequant: s * q)
+ *     Inputs must be finite; a non-finite input makes its tile unspecified.
+ *   - Scale arrays are FP32, one per tile ([conv] "FP32 scale containers"),
+ *     laid out block-major: the scales of consecutive rows (or columns) of
+ *     one 128-block are contiguous.
+ *   - Alignment: every pointer to bf16 or E4M3 data is 16-byte aligned and
+ *     every such leading dimension is a multiple of 16 bytes (8 bf16 or 16
+ *     codes); scale pointers are 4-byte aligned.
+ *   - Errors: argument errors return a negative fgb_status synchronously and
+ *     launch nothing; a launch failure returns FGB_E_HIP.  Faults during
+ *     execution surface at the caller's next synchronization (HIP semantics).
+ */
+#ifndef FGB_H
+#define FGB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FGB_OK = 0,
+    FGB_E_NULL = -1,        /* a required pointer is NULL                        */
+    FGB_E_SHAPE = -2,       /* a dimension is negative or violates a multiple-of rule */
+    FGB_E_ALIGN = -3,       /* a pointer or leading dimension is misaligned      */
+    FGB_E_LD = -4,          /* a leading dimension is smaller than required     */
+    FGB_E_UNSUPPORTED = -5, /* a valid request this build does not implement    */
+    FGB_E_HIP = -6,         /* the HIP runtime reported an error at launch      */
+    FGB_E_ARG = -7          /* another invalid argument (e.g. a negative floor)  */
+} fgb_status;
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int fgb_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* fgb_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Quantizers  ([scratch]: 1x128 activation / 128x128 weight tiles, Wgrad
+ * operands re-tiled 128x1, backward casts emitting both orientations;
+ * [drift] section 3 row (a): scale from the in-block absmax, N_c = 128;
+ * [conv]: /448, -0 kept, RN cast.)
+ * ---------------------------------------------------------------------- */
+
+/* 1x128 tiles of x [R][C] (bf16, leading dim ldx >= C): tile (r, j) covers
+ * x[r][128j .. min(128j+128, C)).  Writes the codes q [R][C] (ldq >= C) and
+ * the scales s [ceil(C/128)][lds] with s[j*lds + r] the scale of tile (r, j),
+ * lds >= R.  Requires C % 8 == 0.  R == 0 or C == 0 is a no-op.
+ * amax_floor >= 0 (0 = no floor). */
+int fgb_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                       float amax_floor,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                       void* stream);
+
+/* 128x1 tiles of x [R][C] (bf16): tile (i, c) covers column c, rows
+ * 128i .. min(128i+128, R).  Writes the codes TRANSPOSED, qT [C][ldqT] with
+ * ldqT >= roundup(R, 128): qT[c*ldqT + r] is the code of x[r][c], and the
+ * padding qT[c*ldqT + r] for R <= r < roundup(R,128) is 0x00.  Scales
+ * sT [ceil(R/128)][ldsT], sT[i*ldsT + c], ldsT >= C.  Equals
+ * fgb_quantize_1x128 of x^T.  Requires C % 8 == 0. */
+int fgb_quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                       float amax_floor,
+                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                       void* stream);
+
+/* 128x128 tiles of a weight w [K][N] (bf16, ldw >= N), K and N multiples of
+ * 128.  Writes q [K][N] (ldq >= N) and/or its transpose qT [N][K]
+ * (ldqT >= K); either may be NULL but not both.  Scales s [K/128][N/128]
+ * (dense), s[i*(N/128) + j] for rows 128i.., columns 128j...  One scale grid
+ * serves both layouts (a tile's absmax does not depend on orientation). */
+int fgb_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
+                         float amax_floor,
+                         uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                         float* s, void* stream);
+
+/* Re-tile a 1x128-quantized tensor to 128x1 ([scratch]: the Wgrad operand
+ * is re-quantized 128x1 from the saved tensor by a small requant box).
+ * Input codes q [R][C] (ldq >= C) with scales s [ceil(C/128)][lds],
+ * lds >= R, as written by fgb_quantize_1x128.  Each element is dequantized
+ * v = fl32(dec(q) * s) and v is quantized with 128x1 tiles exactly as
+ * fgb_quantize_128x1 (no floor), writing qT [C][ldqT] (ldqT >=
+ * roundup(R,128), zero padded) and sT [ceil(R/128)][ldsT] (ldsT >= C).
+ * Requires C % 8 == 0. */
+int fgb_requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
+                      const float* s, int64_t lds,
+                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block-scaled GEMMs ([drift] section 3 rows (a)/(b) and section 5: the
+ * partial sum of every 128-long contraction segment is multiplied by
+ * s_a * s_b and promoted into an FP32 accumulator; [scratch]: all three
+ * GEMMs of a linear in E4M3, Fprop/Dgrad to BF16, Wgrad to FP32).
+ * Output BF16 is rounded to nearest even from the FP32 accumulator.
+ * ---------------------------------------------------------------------- */
+
+/* Fprop: Y[m][n] = bf16( sum_b sx[b][m] * sw[b][n/128] *
+ *                         sum_{k in b} dec(qx[m][k]) * dec(qwT[n][k]) ).
+ * qx [M][K] (ldqx >= K), 1x128 scales sx [K/128][ldsx] (ldsx >= M);
+ * qwT [N][K] (ldqwT >= K) = W's codes transposed (fgb_quantize_128x128 qT),
+ * sw [K/128][N/128] dense; y [M][N] bf16 (ldy >= N).
+ * Requires K % 128 == 0 and N % 128 == 0; M is free.  K == 0 writes zeros. */
+int fgb_gemm_fprop(int64_t M, int64_t N, int64_t K,
+                   const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx,
+                   const uint8_t* qwT, int64_t ldqwT, const float* sw,
+                   uint16_t* y, int64_t ldy, void* stream);
+
+/* Dgrad: dX[m][k] = bf16( sum_b sdy[b][m] * sw[k/128][b] *
+ *                          sum_{n in b} dec(qdy[m][n]) * dec(qw[k][n]) ).
+ * qdy [M][N] (ldqdy >= N), 1x128 scales sdy [N/128][ldsdy] (ldsdy >= M);
+ * qw [K][N] (ldqw >= N) = W's codes (fgb_quantize_128x128 q), sw [K/128][N/128];
+ * dx [M][K] bf16 (lddx >= K).  The 128x128 weight tiles are reused
+ * transposed.  Requires K % 128 == 0 and N % 128 == 0. */
+int fgb_gemm_dgrad(int64_t M, int64_t K, int64_t N,
+                   const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy,
+                   const uint8_t* qw, int64_t ldqw, const float* sw,
+                   uint16_t* dx, int64_t lddx, void* stream);
+
+/* Wgrad: dW[k][n] (W's [K][N] shape, i.e. (dY^T X)^T) =
+ *     (accumulate ? dW[k][n] : 0) + sum_b sxT[b][k] * sdyT[b][n] *
+ *                                   sum_{m in b} dec(qxT[k][m]) * dec(qdyT[n][m])
+ * over b < ceil(M/128).  qxT [K][ldqxT] and qdyT [N][ldqdyT] are 128x1
+ * operands (fgb_requant_128x1 / fgb_quantize_128x1) with
+ * ld >= roundup(M,128) and zero padding beyond M; sxT [ceil(M/128)][ldsxT]
+ * (ldsxT >= K), sdyT [ceil(M/128)][ldsdyT] (ldsdyT >= N); dw [K][N] fp32
+ * (lddw >= N).  Requires K % 128 == 0 and N % 128 == 0; M == 0 writes zeros
+ * (or leaves dW unchanged when accumulating). */
+int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M,
+                   const uint8_t* qxT, int64_t ldqxT, const float* sxT, int64_t ldsxT,
+                   const uint8_t* qdyT, int64_t ldqdyT, const float* sdyT, int64_t ldsdyT,
+                   float* dw, int64_t lddw, int accumulate, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped (MoE expert) GEMMs ([grouped]).  Rows are grouped per expert in
+ * segments [offsets[e], offsets[e+1]) of a padded tensor with R_pad rows;
+ * every offset is a multiple of 128, offsets[0] == 0, offsets are
+ * non-decreasing and offsets[E] <= R_pad; rows of a segment beyond the
+ * expert's tokens are zero.  With that layout, fgb_quantize_1x128 and
+ * fgb_quantize_128x1 over the whole padded tensor equal per-expert
+ * quantization, so no grouped quantizer is needed.  `offsets` is a DEVICE
+ * array of E+1 int32, read by the kernels (no host synchronization).  All
+ * operands are dense (leading dimension = row length).  Rows at or beyond
+ * offsets[E] are not written.
+ * ---------------------------------------------------------------------- */
+
+/* Y[r] = X[r] W_e for rows r of segment e.  qx [R_pad][K], sx [K/128][R_pad],
+ * qwT [E][N][K], sw [E][K/128][N/128], y [R_pad][N] bf16. */
+int fgb_gemm_fprop_grouped(int64_t E, const int32_t* offsets, int64_t R_pad,
+                           int64_t N, int64_t K,
+                           const uint8_t* qx, const float* sx,
+                           const uint8_t* qwT, const float* sw,
+                           uint16_t* y, void* stream);
+
+/* dX[r] = dY[r] W_e^T for rows r of segment e.  qdy [R_pad][N],
+ * sdy [N/128][R_pad], qw [E][K][N], sw [E][K/128][N/128], dx [R_pad][K] bf16. */
+int fgb_gemm_dgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad,
+                           int64_t K, int64_t N,
+                           const uint8_t* qdy, const float* sdy,
+                           const uint8_t* qw, const float* sw,
+                           uint16_t* dx, void* stream);
+
+/* dW_e = X_e^T dY_e over the rows of segment e (contraction blocks
+ * offsets[e]/128 .. offsets[e+1]/128).  qxT [K][R_pad], sxT [R_pad/128][K],
+ * qdyT [N][R_pad], sdyT [R_pad/128][N], dw [E][K][N] fp32.  An empty expert
+ * gets dW_e = 0 (unchanged when accumulating).  R_pad % 128 == 0. */
+int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad,
+                           int64_t K, int64_t N,
+                           const uint8_t* qxT, const float* sxT,
+                           const uint8_t* qdyT, const float* sdyT,
+                           float* dw, int accumulate, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGB_H */

@@ -10,6 +10,11 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # load what is built; build only when nothing is (hipcc cross-compiles without a GPU)
+    import fine_grained_block_amd as fgb
+    if not os.path.exists(fgb.LIB_PATH):
+        from fine_grained_block_amd import build
+        build.build_library()
 
 
 @pytest.fixture(scope="session")

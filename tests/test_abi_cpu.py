@@ -1,0 +1,156 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry point
+declared in include/fgb.h, and rejects invalid arguments with the documented
+status before any HIP call (only argument errors and empty no-ops are called
+here, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fine_grained_block_amd as fgb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_LD, E_UNSUP, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7
+P = ctypes.c_void_p
+A = P(0x10000)         # 16-byte aligned placeholder addresses (never dereferenced)
+B = P(0x20000)
+C_ = P(0x30000)
+D = P(0x40000)
+MIS = P(0x10004)       # misaligned
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fgb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fgb_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fgb.lib()
+    names = header_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(fgb.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    L = fgb.lib()
+    assert L.fgb_version() == 0x000100
+    for st in (OK, E_NULL, E_SHAPE, E_ALIGN, E_LD, E_UNSUP, E_HIP, E_ARG):
+        assert L.fgb_status_string(st)
+    assert L.fgb_status_string(12345) == b"unknown status"
+
+
+def q1(x=A, R=4, C=128, ldx=128, fl=0.0, q=B, ldq=128, s=C_, lds=4):
+    return fgb.lib().fgb_quantize_1x128(x, R, C, ldx, fl, q, ldq, s, lds, None)
+
+
+def test_quantize_1x128_validation():
+    assert q1(C=12) == E_SHAPE
+    assert q1(R=-1) == E_SHAPE
+    assert q1(x=P(0)) == E_NULL
+    assert q1(q=P(0)) == E_NULL
+    assert q1(s=P(0)) == E_NULL
+    assert q1(ldx=64) == E_LD
+    assert q1(ldq=64) == E_LD
+    assert q1(lds=3) == E_LD
+    assert q1(x=MIS) == E_ALIGN
+    assert q1(ldx=132) == E_ALIGN
+    assert q1(fl=-1.0) == E_ARG
+    assert q1(fl=float("nan")) == E_ARG
+    assert q1(fl=float("inf")) == E_ARG
+    assert q1(R=0, x=P(0), q=P(0), s=P(0)) == OK      # empty: no launch
+    assert q1(C=0, x=P(0), q=P(0), s=P(0)) == OK
+
+
+def test_quantize_128x1_validation():
+    L = fgb.lib()
+    f = lambda **k: L.fgb_quantize_128x1(k.get("x", A), k.get("R", 200), k.get("C", 128), k.get("ldx", 128),
+                                         k.get("fl", 0.0), k.get("q", B), k.get("ldq", 256), k.get("s", C_),
+                                         k.get("lds", 128), None)
+    assert f(ldq=200) == E_LD          # must cover roundup(200, 128) = 256
+    assert f(ldq=264, q=P(0x20008)) == E_ALIGN
+    assert f(C=100) == E_SHAPE
+    assert f(lds=127) == E_LD
+    assert f(R=0) == OK
+
+
+def test_quantize_128x128_validation():
+    L = fgb.lib()
+    f = lambda **k: L.fgb_quantize_128x128(k.get("w", A), k.get("K", 256), k.get("N", 128), k.get("ldw", 128),
+                                           0.0, k.get("q", B), k.get("ldq", 128), k.get("qT", C_),
+                                           k.get("ldqT", 256), k.get("s", D), None)
+    assert f(K=200) == E_SHAPE
+    assert f(N=100) == E_SHAPE
+    assert f(q=P(0), qT=P(0)) == E_NULL
+    assert f(ldqT=128) == E_LD
+    assert f(s=P(0)) == E_NULL
+    assert f(K=0) == OK
+
+
+def test_requant_validation():
+    L = fgb.lib()
+    f = lambda **k: L.fgb_requant_128x1(k.get("q", A), k.get("R", 128), k.get("C", 256), k.get("ldq", 256),
+                                        k.get("s", B), k.get("lds", 128), k.get("qT", C_), k.get("ldqT", 128),
+                                        k.get("sT", D), k.get("ldsT", 256), None)
+    assert f(s=P(0)) == E_NULL
+    assert f(lds=100) == E_LD
+    assert f(ldsT=255) == E_LD
+    assert f(C=20) == E_SHAPE
+    assert f(R=0) == OK
+
+
+def test_gemm_validation():
+    L = fgb.lib()
+    fp = lambda **k: L.fgb_gemm_fprop(k.get("M", 64), k.get("N", 128), k.get("K", 256), k.get("qx", A),
+                                      k.get("ldqx", 256), k.get("sx", B), k.get("ldsx", 64), k.get("qw", C_),
+                                      k.get("ldqw", 256), k.get("sw", D), k.get("y", P(0x50000)),
+                                      k.get("ldy", 128), None)
+    assert fp(K=200) == E_SHAPE
+    assert fp(N=64) == E_SHAPE
+    assert fp(qx=P(0)) == E_NULL
+    assert fp(y=P(0)) == E_NULL
+    assert fp(ldqx=128) == E_LD
+    assert fp(ldsx=63) == E_LD
+    assert fp(ldqx=264) == E_ALIGN
+    assert fp(qw=P(0x30008)) == E_ALIGN
+    assert fp(M=0) == OK
+    dg = lambda **k: L.fgb_gemm_dgrad(k.get("M", 64), k.get("K", 128), k.get("N", 256), A, 256, B,
+                                      k.get("ldsdy", 64), C_, 256, D, P(0x50000), k.get("lddx", 128), None)
+    assert dg(N=130) == E_SHAPE
+    assert dg(lddx=100) == E_LD
+    assert dg(M=0) == OK
+    wg = lambda **k: L.fgb_gemm_wgrad(k.get("K", 128), k.get("N", 128), k.get("M", 200), A, k.get("ldqx", 256),
+                                      B, 128, C_, 256, D, 128, P(0x50000), k.get("lddw", 128), 0, None)
+    assert wg(ldqx=200) == E_LD        # must cover roundup(200, 128)
+    assert wg(lddw=64) == E_LD
+    assert wg(K=100) == E_SHAPE
+    assert wg(M=-1) == E_SHAPE
+    assert wg(K=0) == OK
+
+
+def test_grouped_validation():
+    L = fgb.lib()
+    g = lambda **k: L.fgb_gemm_fprop_grouped(k.get("E", 4), k.get("off", P(0x60000)), k.get("R", 512),
+                                             k.get("N", 128), k.get("K", 256), A, B, C_, D,
+                                             k.get("y", P(0x50000)), None)
+    assert g(R=500) == E_SHAPE
+    assert g(off=P(0)) == E_NULL
+    assert g(off=P(0x60002)) == E_ALIGN
+    assert g(E=0) == OK
+    assert g(E=-1) == E_SHAPE
+    w = lambda **k: L.fgb_gemm_wgrad_grouped(k.get("E", 4), P(0x60000), k.get("R", 512), 128, 128, A, B, C_, D,
+                                             k.get("dw", P(0x50000)), 0, None)
+    assert w(dw=P(0)) == E_NULL
+    assert w(R=130) == E_SHAPE
+    assert w(E=0) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(fgb.FgbError):
+        fgb.quantize_1x128(x)

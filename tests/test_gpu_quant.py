@@ -1,0 +1,180 @@
+"""GPU quantizers against the CPU oracle: codes and scale bit patterns must be
+identical (padding bytes included).  Small ragged shapes first, then the full
+quant-stress and linear workloads."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_amd as fgb
+from fine_grained_block_amd import workloads as wl
+
+from parity import assert_codes_equal, assert_scales_equal, bf16_dev, u8_dev, f32_dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def stress(R, C, seed):
+    """Mixed magnitudes, signed zeros, zero tiles, tiny negatives, bf16 subnormals."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((R, C)).astype(np.float32) * np.power(10.0, g.uniform(-6, 3, (R, 1))).astype(np.float32)
+    x[g.random((R, C)) < 0.02] = -0.0
+    x[g.random((R, C)) < 0.02] = 0.0
+    x[: min(R, 3), : min(C, 128)] = 0.0
+    if R > 130 and C > 2:
+        x[:128, 1] = -0.0
+    tiny = g.random((R, C)) < 0.01
+    x[tiny] = -np.abs(x[tiny]) * 1e-7
+    bits = wl.bf16_bits(x)
+    sub = g.random((R, C)) < 0.001
+    bits[sub] = (0x8000 | g.integers(1, 0x80, int(sub.sum()))).astype(np.uint16)
+    return bits
+
+
+SMALL = [(1, 128), (3, 8), (130, 200), (64, 384), (257, 136), (128, 128), (5, 1024)]
+
+
+@pytest.mark.parametrize("R,C", SMALL)
+def test_1x128_small(orc, R, C):
+    x = stress(R, C, 1000 + R * 7 + C)
+    q, s = fgb.quantize_1x128(bf16_dev(x))
+    oq, os_ = orc.quantize_1x128(x)
+    assert_codes_equal(q, oq, f"q[{R}x{C}]")
+    assert_scales_equal(s, os_, f"s[{R}x{C}]")
+
+
+@pytest.mark.parametrize("R,C", SMALL)
+def test_128x1_small(orc, R, C):
+    x = stress(R, C, 2000 + R * 7 + C)
+    qT, sT = fgb.quantize_128x1(bf16_dev(x))
+    oqT, osT = orc.quantize_128x1(x)
+    assert_codes_equal(qT, oqT, f"qT[{R}x{C}]")
+    assert_scales_equal(sT, osT, f"sT[{R}x{C}]")
+
+
+@pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (384, 128)])
+def test_128x128_small(orc, K, N):
+    w = stress(K, N, 3000 + K + N)
+    q, qT, s = fgb.quantize_128x128(bf16_dev(w))
+    oq, oqT, os_ = orc.quantize_128x128(w)
+    assert_codes_equal(q, oq, "q")
+    assert_codes_equal(qT, oqT, "qT")
+    assert_scales_equal(s, os_, "s")
+    # one layout at a time
+    q1, qT1, s1 = fgb.quantize_128x128(bf16_dev(w), want_qT=False)
+    assert qT1 is None
+    assert_codes_equal(q1, oq, "q only")
+    q2, qT2, s2 = fgb.quantize_128x128(bf16_dev(w), want_q=False)
+    assert q2 is None
+    assert_codes_equal(qT2, oqT, "qT only")
+    assert_scales_equal(s2, os_, "s (qT only)")
+
+
+@pytest.mark.parametrize("R,C", [(200, 256), (300, 136), (1, 8), (128, 1024)])
+def test_requant_small(orc, R, C):
+    x = stress(R, C, 4000 + R + C)
+    oq, os_ = orc.quantize_1x128(x)
+    qT, sT = fgb.requant_128x1(u8_dev(oq), f32_dev(os_))
+    oqT, osT = orc.requant_128x1(oq, os_)
+    assert_codes_equal(qT, oqT, "qT")
+    assert_scales_equal(sT, osT, "sT")
+
+
+def test_amax_floor(orc):
+    x = stress(130, 256, 5)
+    for fl in (1e-4, 3.0):
+        q, s = fgb.quantize_1x128(bf16_dev(x), amax_floor=fl)
+        oq, os_ = orc.quantize_1x128(x, amax_floor=fl)
+        assert_codes_equal(q, oq, f"q floor {fl}")
+        assert_scales_equal(s, os_, f"s floor {fl}")
+        qT, sT = fgb.quantize_128x1(bf16_dev(x), amax_floor=fl)
+        oqT, osT = orc.quantize_128x1(x, amax_floor=fl)
+        assert_codes_equal(qT, oqT, f"qT floor {fl}")
+        assert_scales_equal(sT, osT, f"sT floor {fl}")
+    w = stress(256, 256, 6)
+    q, qT, s = fgb.quantize_128x128(bf16_dev(w), amax_floor=2.0)
+    oq, oqT, os_ = orc.quantize_128x128(w, amax_floor=2.0)
+    assert_codes_equal(q, oq, "q floor")
+    assert_scales_equal(s, os_, "s floor")
+
+
+def test_strided_operands(orc):
+    """Row strides larger than the row: inputs and outputs are views of wider buffers."""
+    R, C = 150, 256
+    x = stress(R, C, 7)
+    wide = torch.zeros((R, C + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, :C] = bf16_dev(x)
+    qbuf = torch.full((R, C + 32), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.zeros((2, R + 10), dtype=torch.float32, device="cuda")
+    fgb.quantize_1x128(wide[:, :C], q=qbuf[:, :C], s=sbuf[:, :R])
+    oq, os_ = orc.quantize_1x128(x)
+    assert_codes_equal(qbuf[:, :C], oq, "q strided")
+    assert np.all(host(qbuf[:, C:]) == 0xAB), "wrote outside the view"
+    assert_scales_equal(sbuf[:, :R], os_, "s strided")
+    qTbuf = torch.full((C, 384), 0xCD, dtype=torch.uint8, device="cuda")
+    fgb.quantize_128x1(wide[:, :C], qT=qTbuf[:, :256])
+    oqT, _ = orc.quantize_128x1(x)
+    assert_codes_equal(qTbuf[:, :256], oqT, "qT strided")
+    assert np.all(host(qTbuf[:, 256:]) == 0xCD)
+
+
+def test_deterministic_repeat():
+    x = bf16_dev(stress(512, 1024, 8))
+    a = [fgb.quantize_1x128(x), fgb.quantize_1x128(x)]
+    assert torch.equal(a[0][0], a[1][0]) and torch.equal(a[0][1], a[1][1])
+    b = [fgb.quantize_128x1(x), fgb.quantize_128x1(x)]
+    assert torch.equal(b[0][0], b[1][0]) and torch.equal(b[0][1], b[1][1])
+
+
+# ---------------------------------------------------------------------------
+# full workloads
+# ---------------------------------------------------------------------------
+
+def test_quant_stress_full(orc):
+    """Workload 5: [16384, 7168], all three tilings plus requant, bit-exact."""
+    d = wl.quant_stress()
+    x = d["x"]
+    xd = bf16_dev(x)
+    q, s = fgb.quantize_1x128(xd)
+    oq, os_ = orc.quantize_1x128(x)
+    assert_codes_equal(q, oq, "stress 1x128 q")
+    assert_scales_equal(s, os_, "stress 1x128 s")
+    assert int((oq == 0x80).sum()) > 0
+    qT, sT = fgb.quantize_128x1(xd)
+    oqT, osT = orc.quantize_128x1(x)
+    assert_codes_equal(qT, oqT, "stress 128x1 qT")
+    assert_scales_equal(sT, osT, "stress 128x1 sT")
+    del qT, sT, oqT, osT
+    qw, qwT, sw = fgb.quantize_128x128(xd)
+    oqw, oqwT, osw = orc.quantize_128x128(x)
+    assert_codes_equal(qw, oqw, "stress 128x128 q")
+    assert_codes_equal(qwT, oqwT, "stress 128x128 qT")
+    assert_scales_equal(sw, osw, "stress 128x128 s")
+    del qw, qwT, oqw, oqwT
+    rq, rs = fgb.requant_128x1(q, s)
+    orq, ors = orc.requant_128x1(oq, os_)
+    assert_codes_equal(rq, orq, "stress requant qT")
+    assert_scales_equal(rs, ors, "stress requant sT")
+
+
+def test_linear_workload_quantizers_full(orc):
+    """Workload 2 operands: X and dY 1x128, W 128x128 (both layouts), dY 128x1, requant X."""
+    d = wl.linear_dsv3_attn()
+    for name in ("x", "dy"):
+        q, s = fgb.quantize_1x128(bf16_dev(d[name]))
+        oq, os_ = orc.quantize_1x128(d[name])
+        assert_codes_equal(q, oq, f"{name} 1x128")
+        assert_scales_equal(s, os_, f"{name} 1x128 s")
+        if name == "x":
+            rq, rs = fgb.requant_128x1(q, s)
+            orq, ors = orc.requant_128x1(oq, os_)
+            assert_codes_equal(rq, orq, "x requant")
+            assert_scales_equal(rs, ors, "x requant s")
+    qT, sT = fgb.quantize_128x1(bf16_dev(d["dy"]))
+    oqT, osT = orc.quantize_128x1(d["dy"])
+    assert_codes_equal(qT, oqT, "dy 128x1")
+    assert_scales_equal(sT, osT, "dy 128x1 s")
+    q, qT, s = fgb.quantize_128x128(bf16_dev(d["w"]))
+    oq, oqT, os_ = orc.quantize_128x128(d["w"])
+    assert_codes_equal(q, oq, "w q")
+    assert_codes_equal(qT, oqT, "w qT")
+    assert_scales_equal(s, os_, "w s")
