@@ -165,21 +165,246 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g)
             }
 }
 
+// ===========================================================================
+// Dense kernel: 256x256 output tile per block of 8 waves (2 along M x 4 along N,
+// 128x64 per wave, two waves per SIMD so the 128 accumulator VGPRs of a wave fit
+// beside its fragments).  Per 128-block the A and B slices (32 KB each) and the
+// block's scales are brought into LDS by direct-to-LDS 16-byte loads, double
+// buffered: the loads of block kb+1 are in flight while block kb is computed.
+// The 16-byte chunk c of staged row r sits at slot c ^ (r & 7), which makes the
+// fragment reads (8 rows x 16 B per access group) bank-conflict free.
+// ===========================================================================
+constexpr int kTM = 256, kTN = 256;
+constexpr int kStageA = kTM * kTile;               // 32 KB
+constexpr int kStageB = kTN * kTile;               // 32 KB
+constexpr int kStageBytes = kStageA + kStageB + 2 * 1024;   // + SA, SB (256 floats each)
+constexpr int kV1Threads = 512;
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct-to-LDS loads (global_load_lds): 64 lanes x 16 B (or x 4 B) land at
+// consecutive addresses from the wave-uniform LDS byte address `lds`.  Issued
+// from inline assembly so that the compiler's wait insertion does not treat the
+// in-flight loads as pending writes to every LDS location (which would make
+// every LDS read wait for the prefetch); the kernel waits for each stage itself
+// with vmcnt.  M0 carries the LDS address and is restored afterwards.
+__device__ __forceinline__ void dma16(const void* g, const uint8_t* lds) {
+    const uint32_t a = (uint32_t)(uintptr_t)((const lds_u8*)lds);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(a) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
+    const uint32_t a = (uint32_t)(uintptr_t)((const lds_u8*)lds);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(g), "s"(a) : "memory");
+}
+
+__device__ __forceinline__ v8i frag_swz(const uint8_t* stage_rows, int row, int g) {
+    // 32 bytes = chunks 2g and 2g+1 of staged row `row`
+    const int sw = row & 7;
+    const uint4 lo = *reinterpret_cast<const uint4*>(stage_rows + row * kTile + (((2 * g) ^ sw) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(stage_rows + row * kTile + (((2 * g + 1) ^ sw) << 4));
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+// Map the linear block id to an output tile: consecutive ids go round-robin over
+// the 8 XCDs, so give each XCD a contiguous range of the tile order, and order
+// tiles in groups of 8 M-tiles (column-major inside a group) so that the tiles
+// an XCD runs together share A rows and B columns in its L2.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int total = tiles_m * tiles_n;
+    const int per = total / 8, rem = total % 8;
+    const int xcd = bid % 8, local = bid / 8;
+    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
+    constexpr int G = 8;
+    const int in_group = G * tiles_n;
+    const int first_m = (t / in_group) * G;
+    const int gsize = (tiles_m - first_m) < G ? (tiles_m - first_m) : G;
+    const int r = t % in_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+// Barrier between the waves of a block for LDS traffic: waits only for this
+// wave's own LDS operations (lgkmcnt), never for its global or direct-to-LDS
+// loads (the next stage's prefetch stays in flight; each stage is waited for
+// explicitly with vmcnt), and the memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <bool OUTER, bool BF16_OUT>
+__global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];   // two stages
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = wave & 1, wn = wave >> 1;
+
+    const int tiles_m = (int)((g.M + kTM - 1) / kTM), tiles_n = (int)((g.N + kTN - 1) / kTN);
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+
+    // ---- load plan: per stage 4 A and 4 B direct-to-LDS loads of 8 staged rows
+    // each, plus one 4-byte scale load: 9 vector-memory instructions per wave.
+    // lane -> staged row wave*32 + 8*i + lane/8, source chunk (lane&7) ^ (lane/8);
+    // 32-bit byte offsets from the (uniform) operand base.
+    const int lrow = lane >> 3;
+    const int lchunk = (lane & 7) ^ lrow;
+    uint32_t a_off[4], b_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wave * 32 + 8 * i + lrow;
+        int64_t ar = m0 + r; ar = ar < g.M ? ar : g.M - 1;
+        int64_t br = n0 + r; br = br < g.N ? br : g.N - 1;
+        a_off[i] = (uint32_t)(ar * g.lda) + lchunk * 16;
+        b_off[i] = (uint32_t)(br * g.ldb) + lchunk * 16;
+    }
+    // scales: waves 0..3 stage SA for the 256 rows; waves 4..7 stage SB: the 256
+    // column scales (Wgrad) or the block's two weight-tile scales (Fprop/Dgrad)
+    const float* s_base;
+    int64_t s_kb;
+    uint32_t s_off;
+    {
+        const int sidx = (wave & 3) * 64 + lane;
+        if (wave < 4) {
+            int64_t r = m0 + sidx; r = r < g.M ? r : g.M - 1;
+            s_base = g.sa; s_kb = g.sa_ld; s_off = (uint32_t)r;
+        } else if (OUTER) {
+            int64_t c = n0 + sidx; c = c < g.N ? c : g.N - 1;
+            s_base = g.sb; s_kb = g.sb_kb; s_off = (uint32_t)c;
+        } else {
+            int64_t t = n0 / kTile + (lane & 1);
+            const int64_t tmax = (g.N + kTile - 1) / kTile - 1;
+            t = t < tmax ? t : tmax;
+            s_base = g.sb; s_kb = g.sb_kb; s_off = (uint32_t)(t * g.sb_n);
+        }
+    }
+
+    auto issue = [&](int64_t kb, uint8_t* sbase) {
+        const uint8_t* A = g.A + kb * kTile;
+        const uint8_t* B = g.B + kb * kTile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dma16(A + a_off[i], sbase + (wave * 32 + 8 * i) * kTile);
+            dma16(B + b_off[i], sbase + kStageA + (wave * 32 + 8 * i) * kTile);
+        }
+        dma4(s_base + kb * s_kb + s_off, sbase + kStageA + kStageB + wave * 256);
+    };
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const int frow = lane & 15, fg = lane >> 4;
+
+    auto compute = [&](const uint8_t* sA) {
+        const uint8_t* sB = sA + kStageA;
+        const float* sSA = reinterpret_cast<const float*>(sB + kStageB);
+        const float* sSB = sSA + 4 * 64;           // region of wave 4
+
+        v8i bfr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bfr[j] = frag_swz(sB, wn * 64 + j * 16 + frow, fg);
+        float sbv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sbv[j] = OUTER ? sSB[wn * 64 + j * 16 + frow] : sSB[wn >> 1];
+
+        v8i afr = frag_swz(sA, wm * 128 + frow, fg);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 sa4 = *reinterpret_cast<const float4*>(sSA + wm * 128 + i * 16 + fg * 4);
+            v8i anext = afr;
+            if (i + 1 < 8) anext = frag_swz(sA, wm * 128 + (i + 1) * 16 + frow, fg);
+            const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+            float c[4];
+            if constexpr (!OUTER) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) c[r] = sa[r] * sbv[0];
+            }
+            v4f p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 0, 0, 0);
+                if (j > 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j - 1][r] = __builtin_fmaf(p[j - 1][r], OUTER ? sa[r] * sbv[j - 1] : c[r],
+                                                          acc[i][j - 1][r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[i][3][r] = __builtin_fmaf(p[3][r], OUTER ? sa[r] * sbv[3] : c[r], acc[i][3][r]);
+            afr = anext;
+        }
+    };
+
+    // K loop: the loads of block kb+1 fly while block kb is computed
+    const int64_t nkb = g.nkb;
+    if (nkb > 0) issue(0, smem);
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        const int st = (int)(kb & 1);
+        if (kb + 1 < nkb) {
+            issue(kb + 1, smem + (st ^ 1) * kStageBytes);
+            __builtin_amdgcn_s_waitcnt(0x0F79);    // vmcnt(9): this stage's 9 loads have landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
+        }
+        lds_barrier();
+        compute(smem + st * kStageBytes);
+        lds_barrier();
+    }
+
+    // epilogue: lane holds rows (fg*4 + r) and column frow of every 16x16 piece
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + wn * 64 + j * 16 + frow;
+            if (col >= g.N) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm * 128 + i * 16 + fg * 4 + r;
+                if (row >= g.M) continue;
+                if constexpr (BF16_OUT) {
+                    reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+                } else {
+                    float* o = reinterpret_cast<float*>(g.out) + row * g.ldo + col;
+                    *o = g.accumulate ? *o + acc[i][j][r] : acc[i][j][r];
+                }
+            }
+        }
+}
+
 hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
 {
+    if (!grouped) {
+        const int tiles = (int)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
+        if (kind == kWgrad)
+            hipLaunchKernelGGL((k_gemm_v1<true, false>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_gemm_v1<false, true>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+        return hipGetLastError();
+    }
     const dim3 block(256);
     if (kind == kWgrad) {
-        dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM), grouped ? (unsigned)a.E : 1u);
-        if (grouped)
-            hipLaunchKernelGGL((k_gemm<true, false, false, true>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((k_gemm<true, false, false, false>), grid, block, 0, stream, a);
+        dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM), (unsigned)a.E);
+        hipLaunchKernelGGL((k_gemm<true, false, false, true>), grid, block, 0, stream, a);
     } else {
         dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM));
-        if (grouped)
-            hipLaunchKernelGGL((k_gemm<false, true, true, false>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((k_gemm<false, true, false, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((k_gemm<false, true, true, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
