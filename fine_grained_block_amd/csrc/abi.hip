@@ -135,9 +135,7 @@ int fgb_gemm_fprop(int64_t M, int64_t N, int64_t K,
 {
     if (M < 0 || N < 0 || K < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (M == 0 || N == 0) return FGB_OK;
-    if (!y) return FGB_E_NULL;
-    if (ldy < N) return FGB_E_LD;
-    if (!aligned(y, 2)) return FGB_E_ALIGN;
+    FGB_TRY(check_bf16(y, ldy, N));
     if (K > 0) {
         FGB_TRY(check_codes(qx, ldqx, K, 16));
         FGB_TRY(check_scales(sx, ldsx, M));
@@ -159,9 +157,7 @@ int fgb_gemm_dgrad(int64_t M, int64_t K, int64_t N,
 {
     if (M < 0 || N < 0 || K < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (M == 0 || K == 0) return FGB_OK;
-    if (!dx) return FGB_E_NULL;
-    if (lddx < K) return FGB_E_LD;
-    if (!aligned(dx, 2)) return FGB_E_ALIGN;
+    FGB_TRY(check_bf16(dx, lddx, K));
     if (N > 0) {
         FGB_TRY(check_codes(qdy, ldqdy, N, 16));
         FGB_TRY(check_scales(sdy, ldsdy, M));
@@ -186,7 +182,7 @@ int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M,
     if (K == 0 || N == 0) return FGB_OK;
     if (!dw) return FGB_E_NULL;
     if (lddw < N) return FGB_E_LD;
-    if (!aligned(dw, 4)) return FGB_E_ALIGN;
+    if (!aligned(dw, 16) || lddw % 4 != 0) return FGB_E_ALIGN;
     if (M > 0) {
         FGB_TRY(check_codes(qxT, ldqxT, rup(M, T), 16));
         FGB_TRY(check_scales(sxT, ldsxT, K));
@@ -209,7 +205,7 @@ int fgb_gemm_fprop_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     if (R_pad % T != 0 || N % T != 0 || K % T != 0 || E > 65535) return FGB_E_SHAPE;
     if (E == 0 || R_pad == 0 || N == 0) return FGB_OK;
     if (!offsets || !y) return FGB_E_NULL;
-    if (!aligned(offsets, 4) || !aligned(y, 2)) return FGB_E_ALIGN;
+    if (!aligned(offsets, 4) || !aligned(y, 16)) return FGB_E_ALIGN;
     if (K > 0) {
         FGB_TRY(check_codes(qx, K, K, 16));
         FGB_TRY(check_scales(sx, R_pad, R_pad));
@@ -234,7 +230,7 @@ int fgb_gemm_dgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     if (R_pad % T != 0 || N % T != 0 || K % T != 0 || E > 65535) return FGB_E_SHAPE;
     if (E == 0 || R_pad == 0 || K == 0) return FGB_OK;
     if (!offsets || !dx) return FGB_E_NULL;
-    if (!aligned(offsets, 4) || !aligned(dx, 2)) return FGB_E_ALIGN;
+    if (!aligned(offsets, 4) || !aligned(dx, 16)) return FGB_E_ALIGN;
     if (N > 0) {
         FGB_TRY(check_codes(qdy, N, N, 16));
         FGB_TRY(check_scales(sdy, R_pad, R_pad));
@@ -259,7 +255,7 @@ int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     if (R_pad % T != 0 || N % T != 0 || K % T != 0 || E > 65535) return FGB_E_SHAPE;
     if (E == 0 || K == 0 || N == 0) return FGB_OK;
     if (!offsets || !dw) return FGB_E_NULL;
-    if (!aligned(offsets, 4) || !aligned(dw, 4)) return FGB_E_ALIGN;
+    if (!aligned(offsets, 4) || !aligned(dw, 16)) return FGB_E_ALIGN;
     if (R_pad > 0) {
         FGB_TRY(check_codes(qxT, R_pad, R_pad, 16));
         FGB_TRY(check_scales(sxT, K, K));

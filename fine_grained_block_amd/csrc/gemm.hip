@@ -203,9 +203,16 @@ __device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
                  : "=&s"(saved) : "v"(g), "s"(a) : "memory");
 }
 
+// Staged row r keeps its eight 16-byte chunks at slots c ^ swz(r), swz(r) =
+// (r >> 1) & 7.  A 16-byte LDS read serves 16 lanes per cycle across the 64
+// banks (256 B); the 16 rows of a fragment fall in the two 128-byte halves of
+// that window by parity and in eight distinct slots by (r >> 1) & 7, so the
+// fragment reads are free of bank conflicts.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
 __device__ __forceinline__ v8i frag_swz(const uint8_t* stage_rows, int row, int g) {
     // 32 bytes = chunks 2g and 2g+1 of staged row `row`
-    const int sw = row & 7;
+    const int sw = swz(row);
     const uint4 lo = *reinterpret_cast<const uint4*>(stage_rows + row * kTile + (((2 * g) ^ sw) << 4));
     const uint4 hi = *reinterpret_cast<const uint4*>(stage_rows + row * kTile + (((2 * g + 1) ^ sw) << 4));
     v8i r;
@@ -241,6 +248,10 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Each 16x16x128 MFMA takes the B fragment as its first operand, so a lane ends
+// up holding ONE output row (lane & 15) and FOUR consecutive output columns
+// (4 * (lane >> 4) .. +3) of every 16x16 piece: one row scale per piece, and
+// 8- or 16-byte vector stores in the epilogue.
 template <bool OUTER, bool BF16_OUT>
 __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
 {
@@ -256,28 +267,32 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
 
     // ---- load plan: per stage 4 A and 4 B direct-to-LDS loads of 8 staged rows
     // each, plus one 4-byte scale load: 9 vector-memory instructions per wave.
-    // lane -> staged row wave*32 + 8*i + lane/8, source chunk (lane&7) ^ (lane/8);
-    // 32-bit byte offsets from the (uniform) operand base.
-    const int lrow = lane >> 3;
-    const int lchunk = (lane & 7) ^ lrow;
+    // Lane -> staged row r = wave*32 + 8*i + lane/8 at slot lane&7, which holds
+    // source chunk (lane&7) ^ swz(r); 32-bit byte offsets from the operand base.
     uint32_t a_off[4], b_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wave * 32 + 8 * i + lrow;
+        const int r = wave * 32 + 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(r);
         int64_t ar = m0 + r; ar = ar < g.M ? ar : g.M - 1;
         int64_t br = n0 + r; br = br < g.N ? br : g.N - 1;
-        a_off[i] = (uint32_t)(ar * g.lda) + lchunk * 16;
-        b_off[i] = (uint32_t)(br * g.ldb) + lchunk * 16;
+        a_off[i] = (uint32_t)(ar * g.lda) + chunk * 16;
+        b_off[i] = (uint32_t)(br * g.ldb) + chunk * 16;
     }
-    // scales: waves 0..3 stage SA for the 256 rows; waves 4..7 stage SB: the 256
-    // column scales (Wgrad) or the block's two weight-tile scales (Fprop/Dgrad)
+    // Scales.  Waves 0..3 stage SA, permuted so that a lane can fetch the scales
+    // of its row in all eight 16-row pieces with two 16-byte reads: float p of
+    // the SA area holds row 128*h + 16*i + q, p = 128*h + 64*(i>>2) + 4*q + (i&3).
+    // Waves 4..7 stage SB: the 256 column scales (Wgrad) or, in the first two
+    // floats, the block's two weight-tile scales (Fprop/Dgrad).
     const float* s_base;
     int64_t s_kb;
     uint32_t s_off;
     {
         const int sidx = (wave & 3) * 64 + lane;
         if (wave < 4) {
-            int64_t r = m0 + sidx; r = r < g.M ? r : g.M - 1;
+            const int h = sidx >> 7, q7 = sidx & 127;
+            const int i = ((q7 >> 6) << 2) | (q7 & 3), q = (q7 >> 2) & 15;
+            int64_t r = m0 + h * 128 + 16 * i + q; r = r < g.M ? r : g.M - 1;
             s_base = g.sa; s_kb = g.sa_ld; s_off = (uint32_t)r;
         } else if (OUTER) {
             int64_t c = n0 + sidx; c = c < g.N ? c : g.N - 1;
@@ -309,83 +324,102 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int frow = lane & 15, fg = lane >> 4;
 
+    // One 128-block: 32 MFMAs (8 row pieces x 4 column pieces) in a flat
+    // schedule where step t issues MFMA t and folds the partial of MFMA t-2 (a
+    // ring of four partials), so no fold waits on a result still in the matrix
+    // pipeline.  The operands of the first MFMA are requested first, A fragments
+    // run two row pieces ahead.
     auto compute = [&](const uint8_t* sA) {
         const uint8_t* sB = sA + kStageA;
         const float* sSA = reinterpret_cast<const float*>(sB + kStageB);
-        const float* sSB = sSA + 4 * 64;           // region of wave 4
+        const float* sSB = sSA + 4 * 64;           // region of wave 4 onwards
 
         v8i bfr[4];
+        v8i af[3];
+        af[0] = frag_swz(sA, wm * 128 + frow, fg);
+        bfr[0] = frag_swz(sB, wn * 64 + frow, fg);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[j] = frag_swz(sB, wn * 64 + j * 16 + frow, fg);
-        float sbv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sbv[j] = OUTER ? sSB[wn * 64 + j * 16 + frow] : sSB[wn >> 1];
-
-        v8i afr = frag_swz(sA, wm * 128 + frow, fg);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 sa4 = *reinterpret_cast<const float4*>(sSA + wm * 128 + i * 16 + fg * 4);
-            v8i anext = afr;
-            if (i + 1 < 8) anext = frag_swz(sA, wm * 128 + (i + 1) * 16 + frow, fg);
-            const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-            float c[4];
-            if constexpr (!OUTER) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c[r] = sa[r] * sbv[0];
-            }
-            v4f p[4];
+        for (int j = 1; j < 4; ++j) bfr[j] = frag_swz(sB, wn * 64 + j * 16 + frow, fg);
+        af[1] = frag_swz(sA, wm * 128 + 16 + frow, fg);
+        // row scales of this lane's row in the eight pieces
+        const float4 sa_lo = *reinterpret_cast<const float4*>(sSA + wm * 128 + frow * 4);
+        const float4 sa_hi = *reinterpret_cast<const float4*>(sSA + wm * 128 + 64 + frow * 4);
+        const float sa[8] = {sa_lo.x, sa_lo.y, sa_lo.z, sa_lo.w, sa_hi.x, sa_hi.y, sa_hi.z, sa_hi.w};
+        float sbv[4][4];
+        if constexpr (OUTER) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 0, 0, 0);
-                if (j > 0) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[i][j - 1][r] = __builtin_fmaf(p[j - 1][r], OUTER ? sa[r] * sbv[j - 1] : c[r],
-                                                          acc[i][j - 1][r]);
-                }
+                const float4 t = *reinterpret_cast<const float4*>(sSB + wn * 64 + j * 16 + fg * 4);
+                sbv[j][0] = t.x; sbv[j][1] = t.y; sbv[j][2] = t.z; sbv[j][3] = t.w;
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[i][3][r] = __builtin_fmaf(p[3][r], OUTER ? sa[r] * sbv[3] : c[r], acc[i][3][r]);
-            afr = anext;
         }
+        const float s1 = OUTER ? 0.0f : sSB[wn >> 1];
+
+        v4f P[4];
+        auto fold = [&](int t) {
+            const int i = t >> 2, j = t & 3;
+            if constexpr (OUTER) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i] * sbv[j][r], acc[i][j][r]);
+            } else {
+                const float c = sa[i] * s1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[t & 3][r], c, acc[i][j][r]);
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int i = t >> 2, j = t & 3;
+            if (j == 0 && i + 2 < 8) af[(i + 2) % 3] = frag_swz(sA, wm * 128 + (i + 2) * 16 + frow, fg);
+            P[t & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], af[i % 3], zero, 0, 0, 0, 0, 0, 0);
+            if (t >= 2) fold(t - 2);
+            // keep the order: this MFMA, then the fold of MFMA t-2 (and the
+            // fragment reads of step t), instead of letting the scheduler pull
+            // each fold next to its own MFMA
+        }
+        fold(30);
+        fold(31);
     };
 
-    // K loop: the loads of block kb+1 fly while block kb is computed
+    // K loop, one barrier per block: wait for this wave's loads of block kb, then
+    // the barrier (all waves' loads of kb have landed, and all waves are done
+    // with block kb-1, so its stage can be refilled), then start the loads of
+    // kb+1 into that stage and compute kb while they fly.
     const int64_t nkb = g.nkb;
     if (nkb > 0) issue(0, smem);
     for (int64_t kb = 0; kb < nkb; ++kb) {
         const int st = (int)(kb & 1);
-        if (kb + 1 < nkb) {
-            issue(kb + 1, smem + (st ^ 1) * kStageBytes);
-            __builtin_amdgcn_s_waitcnt(0x0F79);    // vmcnt(9): this stage's 9 loads have landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of block kb
         lds_barrier();
+        if (kb + 1 < nkb) issue(kb + 1, smem + (st ^ 1) * kStageBytes);
         compute(smem + st * kStageBytes);
-        lds_barrier();
     }
 
-    // epilogue: lane holds rows (fg*4 + r) and column frow of every 16x16 piece
+    // epilogue: row m0 + wm*128 + 16*i + frow, columns n0 + wn*64 + 16*j + 4*fg .. +3
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = m0 + wm * 128 + i * 16 + frow;
+        if (row >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 16 + frow;
+            const int64_t col = n0 + wn * 64 + j * 16 + fg * 4;
             if (col >= g.N) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * 128 + i * 16 + fg * 4 + r;
-                if (row >= g.M) continue;
-                if constexpr (BF16_OUT) {
-                    reinterpret_cast<uint16_t*>(g.out)[row * g.ldo + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-                } else {
-                    float* o = reinterpret_cast<float*>(g.out) + row * g.ldo + col;
-                    *o = g.accumulate ? *o + acc[i][j][r] : acc[i][j][r];
+            if constexpr (BF16_OUT) {
+                const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+                const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+                st8(reinterpret_cast<uint16_t*>(g.out) + row * g.ldo + col, make_uint2(lo, hi));
+            } else {
+                float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(g.out) + row * g.ldo + col);
+                float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                if (g.accumulate) {
+                    const float4 pv = *o;
+                    v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
                 }
+                *o = v;
             }
         }
+    }
 }
 
 hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
