@@ -174,9 +174,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g)
 // The 16-byte chunk c of staged row r sits at slot c ^ (r & 7), which makes the
 // fragment reads (8 rows x 16 B per access group) bank-conflict free.
 // ===========================================================================
-constexpr int kTM = 256, kTN = 256;
+constexpr int kTM = 256;                           // output rows per block tile
 constexpr int kStageA = kTM * kTile;               // 32 KB
-constexpr int kStageB = kTN * kTile;               // 32 KB
+constexpr int kStageB = 256 * kTile;               // room for up to 256 B rows
 constexpr int kStageBytes = kStageA + kStageB + 2 * 1024;   // + SA, SB (256 floats each)
 constexpr int kV1Threads = 512;
 
@@ -248,57 +248,79 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Block tile kTM x TN with 8 waves.  TN = 256: waves 2 (M) x 4 (N), 128x64
+// per wave.  TN = 224: waves 4 x 2, 64x112 per wave (used where N is a multiple
+// of 224 and the tile count then fills whole waves of the GPU).
+template <int TN> struct TileShape {
+    static constexpr int WAVES_M = (TN == 256) ? 2 : 4;
+    static constexpr int WAVES_N = 8 / WAVES_M;
+    static constexpr int WTM = kTM / WAVES_M;     // rows per wave
+    static constexpr int WTN = TN / WAVES_N;      // columns per wave
+    static constexpr int MI = WTM / 16;           // 16-row pieces per wave
+    static constexpr int NJ = WTN / 16;           // 16-column pieces per wave
+    static_assert(WTN % 16 == 0 && WTM % 16 == 0, "wave tile");
+};
+
 // Each 16x16x128 MFMA takes the B fragment as its first operand, so a lane ends
 // up holding ONE output row (lane & 15) and FOUR consecutive output columns
 // (4 * (lane >> 4) .. +3) of every 16x16 piece: one row scale per piece, and
 // 8- or 16-byte vector stores in the epilogue.
-template <bool OUTER, bool BF16_OUT>
+template <int TN, bool OUTER, bool BF16_OUT>
 __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
 {
+    using S = TileShape<TN>;
+    constexpr int MI = S::MI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];   // two stages
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % S::WAVES_M, wn = wave / S::WAVES_M;
 
-    const int tiles_m = (int)((g.M + kTM - 1) / kTM), tiles_n = (int)((g.N + kTN - 1) / kTN);
+    const int tiles_m = (int)((g.M + kTM - 1) / kTM), tiles_n = (int)((g.N + TN - 1) / TN);
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * TN;
 
-    // ---- load plan: per stage 4 A and 4 B direct-to-LDS loads of 8 staged rows
-    // each, plus one 4-byte scale load: 9 vector-memory instructions per wave.
-    // Lane -> staged row r = wave*32 + 8*i + lane/8 at slot lane&7, which holds
-    // source chunk (lane&7) ^ swz(r); 32-bit byte offsets from the operand base.
-    uint32_t a_off[4], b_off[4];
+    // ---- load plan: A rows in 32 groups of 8, B rows in TN/8 groups; group q is
+    // loaded by wave q % 8 with one direct-to-LDS instruction.  Lane -> staged
+    // row r = 8*q + lane/8 at slot lane&7, which holds source chunk
+    // (lane&7) ^ swz(r); 32-bit byte offsets from the operand base.
+    constexpr int NB = (TN / 8 + 7) / 8;            // B groups per wave (upper bound)
+    uint32_t a_off[4], b_off[NB];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wave * 32 + 8 * i + (lane >> 3);
+        const int r = (wave + 8 * i) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(r);
         int64_t ar = m0 + r; ar = ar < g.M ? ar : g.M - 1;
-        int64_t br = n0 + r; br = br < g.N ? br : g.N - 1;
         a_off[i] = (uint32_t)(ar * g.lda) + chunk * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int r = (wave + 8 * i) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(r);
+        int64_t br = n0 + r; br = br < g.N ? br : g.N - 1;
         b_off[i] = (uint32_t)(br * g.ldb) + chunk * 16;
     }
-    // Scales.  Waves 0..3 stage SA, permuted so that a lane can fetch the scales
-    // of its row in all eight 16-row pieces with two 16-byte reads: float p of
-    // the SA area holds row 128*h + 16*i + q, p = 128*h + 64*(i>>2) + 4*q + (i&3).
-    // Waves 4..7 stage SB: the 256 column scales (Wgrad) or, in the first two
-    // floats, the block's two weight-tile scales (Fprop/Dgrad).
+    // Scales.  Waves 0..3 stage SA, permuted so that a lane fetches the scales of
+    // its row in all MI row pieces with MI/4 16-byte reads: float p of the SA
+    // area holds row WTM*h + 16*i + q for p = WTM*h + 64*(i>>2) + 4*q + (i&3).
+    // Waves 4..7 stage SB: the column scales (Wgrad), or (Fprop/Dgrad) in floats
+    // 0..3 the scales of the weight tiles floor(n0/128) + 0..3 that the block's
+    // columns can touch.
     const float* s_base;
     int64_t s_kb;
     uint32_t s_off;
     {
         const int sidx = (wave & 3) * 64 + lane;
         if (wave < 4) {
-            const int h = sidx >> 7, q7 = sidx & 127;
+            const int h = sidx / WTM, q7 = sidx % WTM;
             const int i = ((q7 >> 6) << 2) | (q7 & 3), q = (q7 >> 2) & 15;
-            int64_t r = m0 + h * 128 + 16 * i + q; r = r < g.M ? r : g.M - 1;
+            int64_t r = m0 + h * WTM + 16 * i + q; r = r < g.M ? r : g.M - 1;
             s_base = g.sa; s_kb = g.sa_ld; s_off = (uint32_t)r;
         } else if (OUTER) {
             int64_t c = n0 + sidx; c = c < g.N ? c : g.N - 1;
             s_base = g.sb; s_kb = g.sb_kb; s_off = (uint32_t)c;
         } else {
-            int64_t t = n0 / kTile + (lane & 1);
+            int64_t t = n0 / kTile + (lane & 3);
             const int64_t tmax = (g.N + kTile - 1) / kTile - 1;
             t = t < tmax ? t : tmax;
             s_base = g.sb; s_kb = g.sb_kb; s_off = (uint32_t)(t * g.sb_n);
@@ -309,77 +331,107 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
         const uint8_t* A = g.A + kb * kTile;
         const uint8_t* B = g.B + kb * kTile;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dma16(A + a_off[i], sbase + (wave * 32 + 8 * i) * kTile);
-            dma16(B + b_off[i], sbase + kStageA + (wave * 32 + 8 * i) * kTile);
-        }
+        for (int i = 0; i < 4; ++i) dma16(A + a_off[i], sbase + (wave + 8 * i) * 8 * kTile);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if ((wave + 8 * i) * 8 < TN) dma16(B + b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
         dma4(s_base + kb * s_kb + s_off, sbase + kStageA + kStageB + wave * 256);
     };
 
-    v4f acc[8][4];
+    v4f acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int frow = lane & 15, fg = lane >> 4;
+    const int tile0 = (int)(n0 / kTile);
 
-    // One 128-block: 32 MFMAs (8 row pieces x 4 column pieces) in a flat
-    // schedule where step t issues MFMA t and folds the partial of MFMA t-2 (a
-    // ring of four partials), so no fold waits on a result still in the matrix
-    // pipeline.  The operands of the first MFMA are requested first, A fragments
-    // run two row pieces ahead.
+    // One 128-block: MI*NJ MFMAs in a flat schedule where step t issues MFMA t
+    // and folds the partial of MFMA t-2 (a ring of four partials), so no fold
+    // waits on a result still in the matrix pipeline.  The operands of the first
+    // MFMA are requested first.  The shorter side's fragments (B for TN = 256,
+    // A for TN = 224) stay in registers for the whole block; the other side's
+    // stream two pieces ahead through a ring of three.
+    constexpr bool ROW_MAJOR = MI >= NJ;           // steps walk columns inside a row piece
+    constexpr int NH = ROW_MAJOR ? NJ : MI;        // held fragments
+    constexpr int NS = ROW_MAJOR ? MI : NJ;        // streamed fragments
     auto compute = [&](const uint8_t* sA) {
         const uint8_t* sB = sA + kStageA;
         const float* sSA = reinterpret_cast<const float*>(sB + kStageB);
         const float* sSB = sSA + 4 * 64;           // region of wave 4 onwards
+        auto afrag = [&](int i) { return frag_swz(sA, wm * WTM + i * 16 + frow, fg); };
+        auto bfrag = [&](int j) { return frag_swz(sB, wn * WTN + j * 16 + frow, fg); };
+        auto held = [&](int h) { return ROW_MAJOR ? bfrag(h) : afrag(h); };
+        auto streamed = [&](int q) { return ROW_MAJOR ? afrag(q) : bfrag(q); };
 
-        v8i bfr[4];
-        v8i af[3];
-        af[0] = frag_swz(sA, wm * 128 + frow, fg);
-        bfr[0] = frag_swz(sB, wn * 64 + frow, fg);
+        v8i hf[NH];
+        v8i sf[3];
+        sf[0] = streamed(0);
+        hf[0] = held(0);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) bfr[j] = frag_swz(sB, wn * 64 + j * 16 + frow, fg);
-        af[1] = frag_swz(sA, wm * 128 + 16 + frow, fg);
-        // row scales of this lane's row in the eight pieces
-        const float4 sa_lo = *reinterpret_cast<const float4*>(sSA + wm * 128 + frow * 4);
-        const float4 sa_hi = *reinterpret_cast<const float4*>(sSA + wm * 128 + 64 + frow * 4);
-        const float sa[8] = {sa_lo.x, sa_lo.y, sa_lo.z, sa_lo.w, sa_hi.x, sa_hi.y, sa_hi.z, sa_hi.w};
-        float sbv[4][4];
-        if constexpr (OUTER) {
+        for (int h = 1; h < NH; ++h) hf[h] = held(h);
+        if (NS > 1) sf[1] = streamed(1);
+        float sa[MI];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 t = *reinterpret_cast<const float4*>(sSB + wn * 64 + j * 16 + fg * 4);
-                sbv[j][0] = t.x; sbv[j][1] = t.y; sbv[j][2] = t.z; sbv[j][3] = t.w;
-            }
+        for (int h = 0; h < MI / 4; ++h) {
+            const float4 t = *reinterpret_cast<const float4*>(sSA + wm * WTM + 64 * h + frow * 4);
+            sa[4 * h] = t.x; sa[4 * h + 1] = t.y; sa[4 * h + 2] = t.z; sa[4 * h + 3] = t.w;
         }
-        const float s1 = OUTER ? 0.0f : sSB[wn >> 1];
+        // column scales of piece j: 4 per lane (Wgrad) or the piece's weight tile
+        auto col_scales = [&](int j, float (&c)[4]) {
+            if constexpr (OUTER) {
+                const float4 t = *reinterpret_cast<const float4*>(sSB + wn * WTN + j * 16 + fg * 4);
+                c[0] = t.x; c[1] = t.y; c[2] = t.z; c[3] = t.w;
+            } else {
+                // weight tile of this 16-column piece (pieces never straddle 128)
+                c[0] = sSB[(int)((n0 + wn * WTN + j * 16) / kTile) - tile0];
+            }
+        };
+        float cs[ROW_MAJOR ? NJ : 1][4];
+        if constexpr (ROW_MAJOR) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) col_scales(j, cs[j]);
+        }
+        // column-major walk: the scales of column piece p live in cbuf[p & 1]
+        float cbuf[2][4];
+        if constexpr (!ROW_MAJOR) col_scales(0, cbuf[0]);
 
         v4f P[4];
-        auto fold = [&](int t) {
-            const int i = t >> 2, j = t & 3;
+        auto fold = [&](int t, const float (&c)[4]) {
+            const int i = ROW_MAJOR ? t / NJ : t % MI;
+            const int j = ROW_MAJOR ? t % NJ : t / MI;
             if constexpr (OUTER) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i] * sbv[j][r], acc[i][j][r]);
+                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i] * c[r], acc[i][j][r]);
             } else {
-                const float c = sa[i] * s1;
+                const float f = sa[i] * c[0];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[t & 3][r], c, acc[i][j][r]);
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[t & 3][r], f, acc[i][j][r]);
             }
         };
+        auto scales_of_step = [&](int t) -> const float (&)[4] {
+            if constexpr (ROW_MAJOR) return cs[t % NJ];
+            else return cbuf[(t / MI) & 1];
+        };
+        constexpr int T = MI * NJ;
+        constexpr int PER = ROW_MAJOR ? NJ : MI;       // steps per streamed fragment
+        static_assert(ROW_MAJOR || MI >= 3, "column-major walk needs >= 3 row pieces");
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-            const int i = t >> 2, j = t & 3;
-            if (j == 0 && i + 2 < 8) af[(i + 2) % 3] = frag_swz(sA, wm * 128 + (i + 2) * 16 + frow, fg);
-            P[t & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], af[i % 3], zero, 0, 0, 0, 0, 0, 0);
-            if (t >= 2) fold(t - 2);
-            // keep the order: this MFMA, then the fold of MFMA t-2 (and the
-            // fragment reads of step t), instead of letting the scheduler pull
-            // each fold next to its own MFMA
+        for (int t = 0; t < T; ++t) {
+            const int q = t / PER, h = t % PER;        // streamed piece, held piece
+            if (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
+            // piece q-1's last fold runs at step q*PER + 1, so its scale slot is
+            // free from step q*PER + 2 on: load piece q+1's scales there
+            if (!ROW_MAJOR && h == 2 && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
+            P[t & 3] = ROW_MAJOR
+                ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], zero, 0, 0, 0, 0, 0, 0)
+                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], zero, 0, 0, 0, 0, 0, 0);
+            if (t >= 2) fold(t - 2, scales_of_step(t - 2));
         }
-        fold(30);
-        fold(31);
+        fold(T - 2, scales_of_step(T - 2));
+        fold(T - 1, scales_of_step(T - 1));
     };
 
     // K loop, one barrier per block: wait for this wave's loads of block kb, then
@@ -396,14 +448,14 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
         compute(smem + st * kStageBytes);
     }
 
-    // epilogue: row m0 + wm*128 + 16*i + frow, columns n0 + wn*64 + 16*j + 4*fg .. +3
+    // epilogue: row m0 + wm*WTM + 16*i + frow, columns n0 + wn*WTN + 16*j + 4*fg .. +3
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t row = m0 + wm * 128 + i * 16 + frow;
+    for (int i = 0; i < MI; ++i) {
+        const int64_t row = m0 + wm * WTM + i * 16 + frow;
         if (row >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 16 + fg * 4;
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t col = n0 + wn * WTN + j * 16 + fg * 4;
             if (col >= g.N) continue;
             if constexpr (BF16_OUT) {
                 const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
@@ -422,14 +474,48 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
     }
 }
 
+// Number of compute units of the current device (cached per device).
+static int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Pick the tile width: each block takes about TN units of time, and the blocks
+// run in rounds of (number of CUs) -- one block per CU.
+static int pick_tn(int64_t M, int64_t N)
+{
+    const int64_t cus = device_cus();
+    const int64_t tm = (M + kTM - 1) / kTM;
+    auto cost = [&](int64_t tn_w) { return ((tm * ((N + tn_w - 1) / tn_w) + cus - 1) / cus) * tn_w; };
+    if (N % 224 == 0 && cost(224) < cost(256)) return 224;
+    return 256;
+}
+
+template <int TN>
+static void launch_dense(GemmKind kind, const GemmArgs& a, hipStream_t stream)
+{
+    const int tiles = (int)(((a.M + kTM - 1) / kTM) * ((a.N + TN - 1) / TN));
+    if (kind == kWgrad)
+        hipLaunchKernelGGL((k_gemm_v1<TN, true, false>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_v1<TN, false, true>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+}
+
 hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
 {
     if (!grouped) {
-        const int tiles = (int)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
-        if (kind == kWgrad)
-            hipLaunchKernelGGL((k_gemm_v1<true, false>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+        if (pick_tn(a.M, a.N) == 224)
+            launch_dense<224>(kind, a, stream);
         else
-            hipLaunchKernelGGL((k_gemm_v1<false, true>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+            launch_dense<256>(kind, a, stream);
         return hipGetLastError();
     }
     const dim3 block(256);

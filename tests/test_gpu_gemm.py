@@ -35,7 +35,7 @@ def rand_scales(g, shape):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 384, 640), (1, 128, 128), (129, 256, 256),
-                                   (64, 128, 0), (513, 640, 1152)])
+                                   (64, 128, 0), (513, 640, 1152), (300, 896, 256), (700, 1792, 384)])
 def test_fprop_small(orc, M, N, K):
     g = np.random.default_rng(M * 31 + N * 7 + K)
     qx, qwT = rand_codes(g, (M, K)), rand_codes(g, (N, K))
@@ -45,7 +45,7 @@ def test_fprop_small(orc, M, N, K):
     check_gemm(bf16_host_f64(y), r, aabs, True, f"fprop {M}x{N}x{K}", hw_bound_fprop(qx, sx, qwT, sw), K // T)
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 384, 640), (1, 128, 128), (200, 256, 1152)])
+@pytest.mark.parametrize("M,K,N", [(300, 384, 640), (1, 128, 128), (200, 256, 1152), (333, 896, 384)])
 def test_dgrad_small(orc, M, K, N):
     g = np.random.default_rng(M * 13 + N * 5 + K)
     qdy, qw = rand_codes(g, (M, N)), rand_codes(g, (K, N))
@@ -55,7 +55,8 @@ def test_dgrad_small(orc, M, K, N):
     check_gemm(bf16_host_f64(dx), r, aabs, True, f"dgrad {M}x{K}x{N}", hw_bound_dgrad(qdy, sdy, qw, sw), N // T)
 
 
-@pytest.mark.parametrize("K,N,M", [(256, 384, 300), (128, 128, 1), (384, 256, 1024), (128, 256, 129)])
+@pytest.mark.parametrize("K,N,M", [(256, 384, 300), (128, 128, 1), (384, 256, 1024), (128, 256, 129),
+                                   (256, 896, 300), (896, 896, 200)])
 def test_wgrad_small(orc, K, N, M):
     g = np.random.default_rng(K * 3 + N * 11 + M)
     Mp = -(-M // T) * T
@@ -79,7 +80,7 @@ SMALL_INT_CODES = np.array([0x00, 0x80, 0x38, 0xB8, 0x40, 0xC0, 0x44, 0xC4, 0x48
                            np.uint8)   # 0, -0, +-1, +-2, +-3, +-4, +-6, +-8
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 384, 640), (129, 256, 2048)])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 640), (129, 256, 2048), (300, 896, 512)])
 def test_exact_mma_all_kinds(orc, M, N, K):
     """Operands whose products stay inside the matrix core's exact window (every
     product is a small integer, so no in-block truncation): Fprop and Wgrad must
