@@ -41,21 +41,29 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fgb_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# the mutation tests load a deliberately broken build of the same source from here
+_LIB_OVERRIDE = os.environ.get("FGB_ORACLE_LIB")
 TILE = 128
 
 _lib = None
 
 
+def compile_oracle(src: str, out: str) -> str:
+    """gcc with IEEE arithmetic: no fast-math, no FMA contraction."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", "-fexcess-precision=standard",
+           "-Wall", "-Wextra", "-Wno-unused-parameter",
+           src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no FMA contraction)."""
+    """Compile the oracle in place (oracle/liboracle.so)."""
     if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-               "-fno-fast-math", "-ffp-contract=off", "-fexcess-precision=standard",
-               "-Wall", "-Wextra", "-Wno-unused-parameter",
-               _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
+        compile_oracle(_SRC, _LIB_PATH)
     return _LIB_PATH
 
 
@@ -63,9 +71,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     F = ctypes.c_float

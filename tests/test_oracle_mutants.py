@@ -1,0 +1,88 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case below plants one plausible mistake in a copy of the oracle's C source
+(a dropped term, a wrong sign, index or constant, a transposed operand, another
+reading of a rounding rule), builds that copy, and runs the oracle's pin tests
+against it.  The pins are only worth something if every such mistake fails at
+least one of them, so each case asserts that the pin run fails.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PIN_FILES = ["tests/test_oracle_codec.py", "tests/test_oracle_quant.py", "tests/test_oracle_gemm.py"]
+
+# name -> (text in oracle/fgb_oracle.c, replacement); the text must occur exactly once
+MUTANTS = {
+    "ties_away_from_zero": ("return (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "return lo + 1.0;"),
+    "ties_toward_zero": ("return (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;", "return lo;"),
+    "decode_bias_8": ("mag = (1.0 + (double)m / 8.0) * ldexp(1.0, e - 7);",
+                      "mag = (1.0 + (double)m / 8.0) * ldexp(1.0, e - 8);"),
+    "decode_subnormal_scale": ("mag = (double)m * ldexp(1.0, -9);", "mag = (double)m * ldexp(1.0, -10);"),
+    "negative_zero_dropped": ("uint8_t sign = signbit(f) ? 0x80 : 0x00;", "uint8_t sign = (f < 0.0f) ? 0x80 : 0x00;"),
+    "overflow_to_nan": ("if (a > 448.0) return sign | 0x7E;", "if (a > 448.0) return sign | 0x7F;"),
+    "subnormal_encode_scale": ("double m = rne_integer(a * 512.0);", "double m = rne_integer(a * 256.0);"),
+    "binade_carry_lost": ("        m = 0.0;\n        ex += 1;", "        m = 7.0;"),
+    "bf16_ulp_off_by_one": ("double ulp = ldexp(1.0, ex - 7);", "double ulp = ldexp(1.0, ex - 8);"),
+    "absmax_signed": ("float av = fabsf(v[i]);", "float av = v[i];"),
+    "amax_floor_ignored": ("if (amax_floor > a) a = amax_floor;", ""),
+    "scale_denominator_447": ("float s = a / 448.0f;", "float s = a / 447.0f;"),
+    "cast_divides_by_scale": ("float t = v[i] * inv;", "float t = v[i] / s;"),
+    "zero_tile_nan_scale": ("        inv = 0.0f;\n", "        inv = 448.0f / a;\n"),
+    "transpose_pad_negative_zero": ("(k < n) ? code[k] : 0x00;", "(k < n) ? code[k] : 0x80;"),
+    "weight_transpose_not_transposed": ("if (qT) qT[(n0 + b) * ldqT + k0 + a] = code[a * nn + b];",
+                                        "if (qT) qT[(n0 + a) * ldqT + k0 + b] = code[a * nn + b];"),
+    "requant_first_block_scale": ("float sc = s[(c / ORC_TILE) * lds + r];", "float sc = s[r];"),
+    "requant_scale_unapplied": ("v[r * C + c] = (float)(d * (double)sc);", "v[r * C + c] = (float)d;"),
+    "gemm_partial_block_dropped": ("int64_t nblk = ceil_div(K, ORC_TILE);", "int64_t nblk = K / ORC_TILE;"),
+    "gemm_b_scale_block_ignored": ("(double)sb[b * sb_sb + (j / sb_group) * sb_sj];",
+                                   "(double)sb[(j / sb_group) * sb_sj];"),
+    "gemm_a_scale_wrong_row": ("(double)sa[b * sa_sb + (i / sa_group) * sa_si]",
+                               "(double)sa[b * sa_sb + (j / sa_group) * sa_si]"),
+    "gemm_operand_transposed": ("double p = dec[A[i * lda + t]] * dec[B[j * ldb + t]];",
+                                "double p = dec[A[i * lda + t]] * dec[B[t * ldb + j]];"),
+    "gemm_scale_unapplied": ("r += scale * sblk;", "r += sblk;"),
+    "gemm_block_sum_fp32": ("sblk += p;", "sblk = (float)(sblk + p);"),
+    "gemm_aabs_signed": ("sabs += fabs(p);", "sabs += p;"),
+}
+
+
+def _mutant_source(src, old, new):
+    assert src.count(old) == 1, f"mutation site not unique or missing: {old!r}"
+    return src.replace(old, new)
+
+
+def _run_pins(name, old, new, tmpdir):
+    import oracle
+    with open(os.path.join(ROOT, "oracle", "fgb_oracle.c")) as f:
+        src = _mutant_source(f.read(), old, new)
+    c_path = os.path.join(tmpdir, f"{name}.c")
+    with open(c_path, "w") as f:
+        f.write(src)
+    so = oracle.compile_oracle(c_path, os.path.join(tmpdir, f"lib{name}.so"))
+    env = dict(os.environ, FGB_ORACLE_LIB=so, OMP_NUM_THREADS="2")
+    cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+           "-k", "not exhaustive", *PIN_FILES]
+    p = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, p.returncode, p.stdout[-2000:]
+
+
+def test_every_planted_mistake_fails_a_pin(tmp_path):
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        results = list(pool.map(lambda kv: _run_pins(kv[0], *kv[1], str(tmp_path)), MUTANTS.items()))
+    survivors = [(n, out) for n, rc, out in results if rc == 0]
+    crashed = [(n, rc) for n, rc, _ in results if rc not in (0, 1)]
+    for n, rc, out in results:
+        print(f"{n}: pytest exit {rc}")
+    assert not crashed, f"pin runs that crashed instead of failing: {crashed}"
+    assert not survivors, "planted mistakes that no pin catches:\n" + "\n".join(
+        f"--- {n}\n{out}" for n, out in survivors)
+
+
+def test_unmutated_copy_passes_the_pins(tmp_path):
+    """Control: the same build route with no mutation passes, so a failing
+    mutant run fails because of its mutation."""
+    name, rc, out = _run_pins("control", "#define ORC_TILE 128", "#define ORC_TILE 128", str(tmp_path))
+    assert rc == 0, out
