@@ -31,6 +31,40 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 FP8_PEAK = 5.0e15          # FLOP/s, MI355X dense FP8 MFMA
 T = 128
+COPY_BYTES = 1 << 30       # the calibration copy reads and writes this many bytes
+CSRC = os.path.join(ROOT, "fine_grained_block_amd", "csrc")
+
+
+def kernel_source_hash():
+    """First 16 hex digits of sha256 over the kernel sources (csrc/*.hip, *.hpp, by
+    name): a traffic record is valid only for the sources it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 summary
+    (profiles/*_traffic.md, line 'traffic-record: kernel=... bytes=... source=...'),
+    or None when there is none or the kernel sources changed since."""
+    d = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(d):
+        return None
+    want = kernel_source_hash()
+    for f in sorted(os.listdir(d)):
+        if not f.endswith("_traffic.md"):
+            continue
+        for line in open(os.path.join(d, f)):
+            if line.strip().startswith("traffic-record:"):
+                kv = dict(t.split("=", 1) for t in line.split(":", 1)[1].split())
+                if kv.get("kernel") == kernel and kv.get("source") == want:
+                    return int(kv["bytes"])
+    return None
 
 
 def parse():
@@ -39,8 +73,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed region, run a plain streaming kernel (1 GiB read, 1 GiB "
+                        "written) three times: it scales rocprofv3's FETCH_SIZE/WRITE_SIZE to bytes")
     p.add_argument("--cpu-rows", type=int, default=0,
-                   help="output rows per GEMM in the CPU-baseline sample (0 = auto, ~10-30 s)")
+                   help="Fprop/Dgrad output rows in the CPU-baseline sample (0 = auto, ~15 s of GEMM work)")
     return p.parse_args()
 
 
@@ -149,7 +186,7 @@ def main():
     dom_rate = gemm_flop / (gemms[dom] * 1e-3)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_rate / 1e12, 1),
                 "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(dom_rate / FP8_PEAK, 4),
-                "traffic": None}
+                "traffic": traffic_record(dom)}
     quant_ms = sum(v for k, v in per_kernel_ms.items() if not k.startswith("gemm"))
     quant_bytes = sum(abytes.values())
 
@@ -175,6 +212,14 @@ def main():
         "kernels": kinfo,
     }
 
+    if args.copy_calibration:
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        c = torch.empty_like(a)
+        for _ in range(3):          # elementwise: each launch reads 1 GiB and writes 1 GiB
+            torch.neg(a, out=c)
+        torch.cuda.synchronize()
+        del a, c
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_rows)
     print(json.dumps(out), flush=True)
@@ -197,26 +242,31 @@ def cpu_baseline(d, rows_arg):
     qxT, sxT = oracle.requant_128x1(qx, sx)
     tq = time.perf_counter() - t0
     qbytes = sum(algorithmic_bytes(M, K, N).values())
-    # size the GEMM sample so the oracle works ~10-30 s: probe one row first
-    rows_n = rows_arg
-    if rows_n <= 0:
-        t1 = time.perf_counter()
-        oracle.gemm_fprop(qx, sx, qT, sw, rows=np.array([0]))
-        per_row = max(time.perf_counter() - t1, 1e-4)
-        rows_n = int(max(8, min(512, 5.0 / per_row)))
-    g = np.random.default_rng(0)
-    rows = np.sort(g.choice(M, size=rows_n, replace=False))
-    rowsK = np.sort(g.choice(K, size=rows_n, replace=False))
-    t2 = time.perf_counter()
-    oracle.gemm_fprop(qx, sx, qT, sw, rows=rows)
-    oracle.gemm_dgrad(qdy, sdy, q, sw, rows=rows)
-    oracle.gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows=rowsK)
-    tg = time.perf_counter() - t2
-    flop = 2.0 * rows_n * N * K + 2.0 * rows_n * K * N + 2.0 * rows_n * N * M
+    # size the GEMM sample so the oracle works ~15 s: time a 1/128 slice of each
+    # GEMM's output rows first, then take the fraction f of the rows (f <= 1: the
+    # whole step) that the target allows
+    def run(frac, seed):
+        g = np.random.default_rng(seed)
+        nr, nk = max(1, int(round(frac * M))), max(1, int(round(frac * K)))
+        rows = np.sort(g.choice(M, size=nr, replace=False))
+        rowsK = np.sort(g.choice(K, size=nk, replace=False))
+        t = time.perf_counter()
+        oracle.gemm_fprop(qx, sx, qT, sw, rows=rows)
+        oracle.gemm_dgrad(qdy, sdy, q, sw, rows=rows)
+        oracle.gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows=rowsK)
+        return time.perf_counter() - t, nr, nk
+
+    frac = min(1.0, rows_arg / M) if rows_arg > 0 else None
+    if frac is None:
+        tp, _, _ = run(1.0 / 128, 1)
+        frac = min(1.0, (1.0 / 128) * 15.0 / max(tp, 1e-6))
+    tg, nr, nk = run(frac, 0)
+    flop = 2.0 * nr * N * K + 2.0 * nr * K * N + 2.0 * nk * N * M
+    what = "the whole step" if nr == M and nk == K else f"{nr}/{M} Fprop and Dgrad rows, {nk}/{K} Wgrad rows"
     return {"value": round(flop / tg / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": f"Fprop/Dgrad/Wgrad on {rows_n} output rows each (all columns, full contraction) "
-                      f"of the same step; {tg:.1f} s",
+            "sample": f"quantizers on the full tensors ({tq:.1f} s), then GEMMs over {what} "
+                      f"(all columns, full contraction; {tg:.1f} s); value = GEMM FLOP / GEMM time",
             "quant_GBps": round(qbytes / tq / 1e9, 3), "quant_s": round(tq, 2)}
 
 
