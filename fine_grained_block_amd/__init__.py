@@ -212,6 +212,11 @@ def _offsets(offsets: torch.Tensor):
     return offsets.numel() - 1
 
 
+def _contiguous(t):
+    if not t.is_contiguous():
+        raise ValueError("grouped GEMM operands must be contiguous tensors")
+
+
 def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, y=None):
     E = _offsets(offsets)
     R_pad, K = qx.shape
@@ -219,7 +224,7 @@ def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, y=None):
     if y is None:
         y = torch.empty((R_pad, N), dtype=torch.bfloat16, device=qx.device)
     for t in (qx, sx, qwT, sw, y):
-        assert t.is_contiguous()
+        _contiguous(t)
     _check(lib().fgb_gemm_fprop_grouped(E, _ptr(offsets), R_pad, N, K, _ptr(qx), _ptr(sx), _ptr(qwT),
                                         _ptr(sw), _ptr(y), _stream(qx)), "gemm_fprop_grouped")
     return y
@@ -232,7 +237,7 @@ def gemm_dgrad_grouped(offsets, qdy, sdy, qw, sw, dx=None):
     if dx is None:
         dx = torch.empty((R_pad, K), dtype=torch.bfloat16, device=qdy.device)
     for t in (qdy, sdy, qw, sw, dx):
-        assert t.is_contiguous()
+        _contiguous(t)
     _check(lib().fgb_gemm_dgrad_grouped(E, _ptr(offsets), R_pad, K, N, _ptr(qdy), _ptr(sdy), _ptr(qw),
                                         _ptr(sw), _ptr(dx), _stream(qdy)), "gemm_dgrad_grouped")
     return dx
@@ -245,7 +250,7 @@ def gemm_wgrad_grouped(offsets, qxT, sxT, qdyT, sdyT, dw=None, accumulate: bool 
     if dw is None:
         dw = torch.empty((E, K, N), dtype=torch.float32, device=qxT.device)
     for t in (qxT, sxT, qdyT, sdyT, dw):
-        assert t.is_contiguous()
+        _contiguous(t)
     _check(lib().fgb_gemm_wgrad_grouped(E, _ptr(offsets), R_pad, K, N, _ptr(qxT), _ptr(sxT), _ptr(qdyT),
                                         _ptr(sdyT), _ptr(dw), 1 if accumulate else 0, _stream(qxT)),
            "gemm_wgrad_grouped")

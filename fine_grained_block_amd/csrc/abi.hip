@@ -147,6 +147,7 @@ int fgb_gemm_fprop(int64_t M, int64_t N, int64_t K,
     a.A = qx; a.lda = ldqx; a.sa = sx; a.sa_ld = ldsx;
     a.B = qwT; a.ldb = ldqwT; a.sb = sw; a.sb_kb = N / T; a.sb_n = 1;
     a.out = y; a.ldo = ldy;
+    if (!fgb::gemm_supported(a, false)) return FGB_E_UNSUPPORTED;
     return hip_status(fgb::launch_gemm(fgb::kFprop, false, a, as_stream(stream)));
 }
 
@@ -170,6 +171,7 @@ int fgb_gemm_dgrad(int64_t M, int64_t K, int64_t N,
     // output column k uses weight tile row k/128: SB(k, b) = sw[(k/128)*(N/128) + b]
     a.B = qw; a.ldb = ldqw; a.sb = sw; a.sb_kb = 1; a.sb_n = N / T;
     a.out = dx; a.ldo = lddx;
+    if (!fgb::gemm_supported(a, false)) return FGB_E_UNSUPPORTED;
     return hip_status(fgb::launch_gemm(fgb::kDgrad, false, a, as_stream(stream)));
 }
 
@@ -194,6 +196,7 @@ int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M,
     a.A = qxT; a.lda = ldqxT; a.sa = sxT; a.sa_ld = ldsxT;
     a.B = qdyT; a.ldb = ldqdyT; a.sb = sdyT; a.sb_kb = ldsdyT;
     a.out = dw; a.ldo = lddw; a.accumulate = accumulate ? 1 : 0;
+    if (!fgb::gemm_supported(a, false)) return FGB_E_UNSUPPORTED;
     return hip_status(fgb::launch_gemm(fgb::kWgrad, false, a, as_stream(stream)));
 }
 
@@ -219,6 +222,7 @@ int fgb_gemm_fprop_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     a.out = y; a.ldo = N;
     a.offsets = offsets; a.E = E;
     a.b_expert_stride = N * K; a.sb_expert_stride = (K / T) * (N / T);
+    if (!fgb::gemm_supported(a, true)) return FGB_E_UNSUPPORTED;
     return hip_status(fgb::launch_gemm(fgb::kFprop, true, a, as_stream(stream)));
 }
 
@@ -244,6 +248,7 @@ int fgb_gemm_dgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     a.out = dx; a.ldo = K;
     a.offsets = offsets; a.E = E;
     a.b_expert_stride = K * N; a.sb_expert_stride = (K / T) * (N / T);
+    if (!fgb::gemm_supported(a, true)) return FGB_E_UNSUPPORTED;
     return hip_status(fgb::launch_gemm(fgb::kDgrad, true, a, as_stream(stream)));
 }
 
@@ -268,6 +273,7 @@ int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     a.B = qdyT; a.ldb = R_pad; a.sb = sdyT; a.sb_kb = N;
     a.out = dw; a.ldo = N; a.accumulate = accumulate ? 1 : 0;
     a.offsets = offsets; a.E = E; a.out_expert_stride = K * N;
+    if (!fgb::gemm_supported(a, true)) return FGB_E_UNSUPPORTED;
     return hip_status(fgb::launch_gemm(fgb::kWgrad, true, a, as_stream(stream)));
 }
 

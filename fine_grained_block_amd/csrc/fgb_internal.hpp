@@ -48,6 +48,12 @@ struct GemmArgs {
     int64_t out_expert_stride = 0;     // elements of out per expert (K-grouped)
 };
 
+// Whether launch_gemm can address the operands: the kernel uses 32-bit byte
+// offsets inside each operand.  Dense GEMMs are cut into pieces that fit (so
+// only a leading dimension above ~16M bytes is refused); grouped operands must
+// each stay within 4 GiB.
+bool gemm_supported(const GemmArgs& args, bool grouped);
+
 hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& args, hipStream_t stream);
 
 }  // namespace fgb

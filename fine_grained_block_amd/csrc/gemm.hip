@@ -10,169 +10,18 @@
 // partial-sum-drift notes (section 3 row (b), section 5): the matrix core's
 // chain never spans more than one 128-block, and dequantization plus the
 // running sum happen in FP32 on the vector ALUs.
-//
-// Tile: 128x128 per block of 4 waves (2x2), 64x64 per wave; the 128-byte K
-// slices of A and B are staged through LDS.
 
 #include "device_common.hpp"
 #include "fgb_internal.hpp"
 
 namespace fgb {
 
-constexpr int kBM = 128, kBN = 128;
-constexpr int kLdsStride = 128 + 16;   // bytes per staged row
-
-__device__ __forceinline__ v8i lds_frag(const uint8_t* base) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(base);
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + 16);
-    v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-    return r;
-}
-
-// OUTER: SB(n,b) per output column (Wgrad); otherwise one weight-tile scale per
-// 128 output columns.  BF16_OUT: Fprop/Dgrad epilogue; else FP32 (+accumulate).
-// GROUP_M: rows grouped per expert (B and its scales chosen per 128-row tile).
-// GROUP_K: contraction grouped per expert (blockIdx.z = expert).
-template <bool OUTER, bool BF16_OUT, bool GROUP_M, bool GROUP_K>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t As[kBM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[kBN * kLdsStride];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
-
-    const uint8_t* B = g.B;
-    const float* sb = g.sb;
-    int64_t kb0 = 0, kb1 = g.nkb;
-    int64_t mend = g.M;
-    uint8_t* outp = static_cast<uint8_t*>(g.out);
-
-    if constexpr (GROUP_M) {
-        // segments are 128-aligned, so the whole 128-row tile is in one expert
-        int64_t total = g.offsets[g.E];
-        total = total < g.M ? total : g.M;       // never past R_pad
-        if (m0 >= total) return;
-        int64_t lo = 0, hi = g.E - 1;             // first e with offsets[e+1] > m0
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (g.offsets[mid + 1] > m0) hi = mid; else lo = mid + 1;
-        }
-        B += lo * g.b_expert_stride;
-        sb += lo * g.sb_expert_stride;
-        mend = total;
-    }
-    if constexpr (GROUP_K) {
-        // contraction blocks of expert e, clamped to the R_pad/128 blocks that exist
-        const int64_t e = blockIdx.z;
-        kb0 = g.offsets[e] / kTile;
-        kb1 = g.offsets[e + 1] / kTile;
-        kb0 = kb0 < 0 ? 0 : (kb0 > g.nkb ? g.nkb : kb0);
-        kb1 = kb1 < kb0 ? kb0 : (kb1 > g.nkb ? g.nkb : kb1);
-        outp += e * g.out_expert_stride * (int64_t)sizeof(float);
-    }
-
-    v4f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    const int frow = lane & 15;          // fragment row within a 16-row piece
-    const int fk = (lane >> 4) * 32;     // this lane's 32-byte K slice
-    const int orow = (lane >> 4) * 4;    // output rows orow..orow+3 of a 16x16 piece
-
-    for (int64_t kb = kb0; kb < kb1; ++kb) {
-        uint4 ga[4], gb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i;
-            const int row = id >> 3, seg = id & 7;
-            int64_t ar = m0 + row;
-            ar = ar < g.M ? ar : g.M - 1;
-            ga[i] = ld16(g.A + ar * g.lda + kb * kTile + seg * 16);
-            gb[i] = ld16(B + (n0 + row) * g.ldb + kb * kTile + seg * 16);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i;
-            const int row = id >> 3, seg = id & 7;
-            *reinterpret_cast<uint4*>(&As[row * kLdsStride + seg * 16]) = ga[i];
-            *reinterpret_cast<uint4*>(&Bs[row * kLdsStride + seg * 16]) = gb[i];
-        }
-        __syncthreads();
-
-        v8i af[4], bf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            af[i] = lds_frag(&As[(wm * 64 + i * 16 + frow) * kLdsStride + fk]);
-            bf[i] = lds_frag(&Bs[(wn * 64 + i * 16 + frow) * kLdsStride + fk]);
-        }
-
-        // scales of this block: SA for the lane's 16 rows, SB per column or per tile
-        float sa[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                int64_t row = m0 + wm * 64 + i * 16 + orow + r;
-                row = row < g.M ? row : g.M - 1;
-                sa[i][r] = g.sa[kb * g.sa_ld + row];
-            }
-        float sbv[4];
-        if constexpr (OUTER) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sbv[j] = sb[kb * g.sb_kb + n0 + wn * 64 + j * 16 + frow];
-        } else {
-            const float s1 = sb[kb * g.sb_kb + (n0 / kTile) * g.sb_n];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sbv[j] = s1;
-        }
-
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], bf[j], zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sa[i][r] * sbv[j], acc[i][j][r]);
-            }
-    }
-
-    // epilogue
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 16 + orow + r;
-                const int64_t col = n0 + wn * 64 + j * 16 + frow;
-                if (row >= mend) continue;
-                if constexpr (BF16_OUT) {
-                    reinterpret_cast<uint16_t*>(outp)[row * g.ldo + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-                } else {
-                    float* o = reinterpret_cast<float*>(outp) + row * g.ldo + col;
-                    *o = g.accumulate ? *o + acc[i][j][r] : acc[i][j][r];
-                }
-            }
-}
-
 // ===========================================================================
-// Dense kernel: 256x256 output tile per block of 8 waves (2 along M x 4 along N,
-// 128x64 per wave, two waves per SIMD so the 128 accumulator VGPRs of a wave fit
-// beside its fragments).  Per 128-block the A and B slices (32 KB each) and the
-// block's scales are brought into LDS by direct-to-LDS 16-byte loads, double
-// buffered: the loads of block kb+1 are in flight while block kb is computed.
-// The 16-byte chunk c of staged row r sits at slot c ^ (r & 7), which makes the
-// fragment reads (8 rows x 16 B per access group) bank-conflict free.
+// 256 x TN output tile per block of 8 waves (two waves per SIMD, so the 112-128
+// accumulator VGPRs of a wave fit beside its fragments).  Per 128-block the A
+// and B slices (32 KB each) and the block's scales are brought into LDS by
+// direct-to-LDS 16-byte loads, double buffered: the loads of block kb+1 are in
+// flight while block kb is computed.
 // ===========================================================================
 constexpr int kTM = 256;                           // output rows per block tile
 constexpr int kStageA = kTM * kTile;               // 32 KB
@@ -221,15 +70,18 @@ __device__ __forceinline__ v8i frag_swz(const uint8_t* stage_rows, int row, int 
     return r;
 }
 
-// Map the linear block id to an output tile: consecutive ids go round-robin over
-// the 8 XCDs, so give each XCD a contiguous range of the tile order, and order
-// tiles in groups of 8 M-tiles (column-major inside a group) so that the tiles
-// an XCD runs together share A rows and B columns in its L2.
-__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
+// Consecutive block ids go round-robin over the 8 XCDs: give each XCD a
+// contiguous range of the tile order instead (bijective on [0, total)).
+__device__ __forceinline__ int xcd_order(int bid, int total) {
     const int per = total / 8, rem = total % 8;
     const int xcd = bid % 8, local = bid / 8;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
+    return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+// Tile t of a tiles_m x tiles_n grid, in groups of 8 M-tiles (column-major
+// inside a group), so that the tiles an XCD runs together share A rows and B
+// columns in its L2.
+__device__ __forceinline__ void group_order(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
     constexpr int G = 8;
     const int in_group = G * tiles_n;
     const int first_m = (t / in_group) * G;
@@ -237,6 +89,68 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     const int r = t % in_group;
     tm = first_m + r % gsize;
     tn = r / gsize;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+// Row-grouped (MoE) tiles: expert e owns rows [o(e), o(e+1)) of the output,
+// o(e) = offsets[e] clamped to [0, min(offsets[E], M)], and is cut into
+// ceil(len/256) row tiles of its own (the last one may hold 128 rows).  Every
+// wave of the block finds, for row-tile tm, the expert and its row range;
+// ntm is the number of row tiles over all experts.
+struct RowTile { int e; int64_t m0, mend; };
+
+__device__ __forceinline__ int clamp_off(int v, int total) { return v < 0 ? 0 : (v > total ? total : v); }
+
+__device__ int row_tiles_total(const GemmArgs& g, int total) {
+    const int lane = threadIdx.x & 63;
+    int ntm = 0;
+    for (int base = 0; base < g.E; base += 64) {
+        const int e = base + lane;
+        int te = 0;
+        if (e < g.E) {
+            const int lo = clamp_off(g.offsets[e], total), hi = clamp_off(g.offsets[e + 1], total);
+            te = hi > lo ? (hi - lo + kTM - 1) / kTM : 0;
+        }
+        ntm += __builtin_amdgcn_readlane(wave_scan(te), 63);
+    }
+    return ntm;
+}
+
+__device__ RowTile row_tile_of(const GemmArgs& g, int total, int tm) {
+    const int lane = threadIdx.x & 63;
+    RowTile rt{0, 0, 0};
+    int before = 0;                                 // row tiles of the experts before this chunk
+    for (int base = 0; base < g.E; base += 64) {
+        const int e = base + lane;
+        int lo = 0, hi = 0, te = 0;
+        if (e < g.E) {
+            lo = clamp_off(g.offsets[e], total); hi = clamp_off(g.offsets[e + 1], total);
+            te = hi > lo ? (hi - lo + kTM - 1) / kTM : 0;
+        }
+        const int incl = wave_scan(te), excl = incl - te;
+        const bool mine = te > 0 && before + excl <= tm && tm < before + incl;
+        const uint64_t hit = __ballot(mine);
+        if (hit) {
+            const int j = __builtin_ctzll(hit);
+            rt.e = base + j;
+            rt.m0 = (int64_t)__builtin_amdgcn_readlane(lo, j) +
+                    (int64_t)kTM * (tm - before - __builtin_amdgcn_readlane(excl, j));
+            rt.mend = __builtin_amdgcn_readlane(hi, j);
+            return rt;
+        }
+        before += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return rt;
 }
 
 // Barrier between the waves of a block for LDS traffic: waits only for this
@@ -265,8 +179,15 @@ template <int TN> struct TileShape {
 // up holding ONE output row (lane & 15) and FOUR consecutive output columns
 // (4 * (lane >> 4) .. +3) of every 16x16 piece: one row scale per piece, and
 // 8- or 16-byte vector stores in the epilogue.
-template <int TN, bool OUTER, bool BF16_OUT>
-__global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
+//
+// GROUP = kDense: one GEMM.  kGroupRows: the output rows are cut into expert
+// segments (row tiles never straddle two experts) and each segment uses its
+// expert's B and weight scales.  kGroupK: the contraction blocks are cut into
+// expert segments and expert e writes its own output g.out + e*out_expert_stride.
+enum { kDense = 0, kGroupRows = 1, kGroupK = 2 };
+
+template <int TN, bool OUTER, bool BF16_OUT, int GROUP>
+__global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
 {
     using S = TileShape<TN>;
     constexpr int MI = S::MI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
@@ -275,10 +196,41 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave % S::WAVES_M, wn = wave / S::WAVES_M;
 
-    const int tiles_m = (int)((g.M + kTM - 1) / kTM), tiles_n = (int)((g.N + TN - 1) / TN);
+    const int tiles_n = (int)((g.N + TN - 1) / TN);
     int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * TN;
+    int64_t m0, mend = g.M, kb0 = 0, kb1 = g.nkb;
+    const uint8_t* Bp = g.B;
+    const float* sbp = g.sb;
+    void* outp = g.out;
+    if constexpr (GROUP == kDense) {
+        const int tiles_m = (int)((g.M + kTM - 1) / kTM);
+        group_order(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+        m0 = (int64_t)tm * kTM;
+    } else if constexpr (GROUP == kGroupRows) {
+        int total = g.offsets[g.E];
+        total = total < 0 ? 0 : (total > g.M ? (int)g.M : total);     // never past the rows that exist
+        const int ntm = row_tiles_total(g, total);
+        if ((int)blockIdx.x >= ntm * tiles_n) return;                  // the grid is an upper bound
+        group_order(xcd_order(blockIdx.x, ntm * tiles_n), ntm, tiles_n, tm, tn);
+        const RowTile rt = row_tile_of(g, total, tm);
+        if (rt.mend <= rt.m0) return;                                  // tm < ntm always finds one
+        m0 = rt.m0; mend = rt.mend;
+        Bp += rt.e * g.b_expert_stride;
+        sbp += rt.e * g.sb_expert_stride;
+    } else {
+        const int tiles_m = (int)((g.M + kTM - 1) / kTM), per_e = tiles_m * tiles_n;
+        const int t = xcd_order(blockIdx.x, per_e * (int)g.E);
+        const int e = t / per_e;
+        group_order(t - e * per_e, tiles_m, tiles_n, tm, tn);
+        m0 = (int64_t)tm * kTM;
+        // contraction blocks of expert e, clamped to the nkb blocks that exist
+        int64_t b0 = g.offsets[e] / kTile, b1 = g.offsets[e + 1] / kTile;
+        b0 = b0 < 0 ? 0 : (b0 > g.nkb ? g.nkb : b0);
+        b1 = b1 < b0 ? b0 : (b1 > g.nkb ? g.nkb : b1);
+        kb0 = b0; kb1 = b1;
+        outp = reinterpret_cast<uint8_t*>(g.out) + e * g.out_expert_stride * (int64_t)sizeof(float);
+    }
+    const int64_t n0 = (int64_t)tn * TN;
 
     // ---- load plan: A rows in 32 groups of 8, B rows in TN/8 groups; group q is
     // loaded by wave q % 8 with one direct-to-LDS instruction.  Lane -> staged
@@ -290,7 +242,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
     for (int i = 0; i < 4; ++i) {
         const int r = (wave + 8 * i) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(r);
-        int64_t ar = m0 + r; ar = ar < g.M ? ar : g.M - 1;
+        int64_t ar = m0 + r; ar = ar < mend ? ar : mend - 1;
         a_off[i] = (uint32_t)(ar * g.lda) + chunk * 16;
     }
 #pragma unroll
@@ -314,22 +266,22 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
         if (wave < 4) {
             const int h = sidx / WTM, q7 = sidx % WTM;
             const int i = ((q7 >> 6) << 2) | (q7 & 3), q = (q7 >> 2) & 15;
-            int64_t r = m0 + h * WTM + 16 * i + q; r = r < g.M ? r : g.M - 1;
+            int64_t r = m0 + h * WTM + 16 * i + q; r = r < mend ? r : mend - 1;
             s_base = g.sa; s_kb = g.sa_ld; s_off = (uint32_t)r;
         } else if (OUTER) {
             int64_t c = n0 + sidx; c = c < g.N ? c : g.N - 1;
-            s_base = g.sb; s_kb = g.sb_kb; s_off = (uint32_t)c;
+            s_base = sbp; s_kb = g.sb_kb; s_off = (uint32_t)c;
         } else {
             int64_t t = n0 / kTile + (lane & 3);
             const int64_t tmax = (g.N + kTile - 1) / kTile - 1;
             t = t < tmax ? t : tmax;
-            s_base = g.sb; s_kb = g.sb_kb; s_off = (uint32_t)(t * g.sb_n);
+            s_base = sbp; s_kb = g.sb_kb; s_off = (uint32_t)(t * g.sb_n);
         }
     }
 
     auto issue = [&](int64_t kb, uint8_t* sbase) {
         const uint8_t* A = g.A + kb * kTile;
-        const uint8_t* B = g.B + kb * kTile;
+        const uint8_t* B = Bp + kb * kTile;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(A + a_off[i], sbase + (wave + 8 * i) * 8 * kTile);
 #pragma unroll
@@ -438,13 +390,12 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
     // the barrier (all waves' loads of kb have landed, and all waves are done
     // with block kb-1, so its stage can be refilled), then start the loads of
     // kb+1 into that stage and compute kb while they fly.
-    const int64_t nkb = g.nkb;
-    if (nkb > 0) issue(0, smem);
-    for (int64_t kb = 0; kb < nkb; ++kb) {
-        const int st = (int)(kb & 1);
+    if (kb1 > kb0) issue(kb0, smem);
+    for (int64_t kb = kb0; kb < kb1; ++kb) {
+        const int st = (int)((kb - kb0) & 1);
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of block kb
         lds_barrier();
-        if (kb + 1 < nkb) issue(kb + 1, smem + (st ^ 1) * kStageBytes);
+        if (kb + 1 < kb1) issue(kb + 1, smem + (st ^ 1) * kStageBytes);
         compute(smem + st * kStageBytes);
     }
 
@@ -452,7 +403,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const int64_t row = m0 + wm * WTM + i * 16 + frow;
-        if (row >= g.M) continue;
+        if (row >= mend) continue;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int64_t col = n0 + wn * WTN + j * 16 + fg * 4;
@@ -460,9 +411,9 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_v1(GemmArgs g)
             if constexpr (BF16_OUT) {
                 const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
                 const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-                st8(reinterpret_cast<uint16_t*>(g.out) + row * g.ldo + col, make_uint2(lo, hi));
+                st8(reinterpret_cast<uint16_t*>(outp) + row * g.ldo + col, make_uint2(lo, hi));
             } else {
-                float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(g.out) + row * g.ldo + col);
+                float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(outp) + row * g.ldo + col);
                 float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
                 if (g.accumulate) {
                     const float4 pv = *o;
@@ -500,33 +451,86 @@ static int pick_tn(int64_t M, int64_t N)
 }
 
 template <int TN>
-static void launch_dense(GemmKind kind, const GemmArgs& a, hipStream_t stream)
+static void launch_v1(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
 {
-    const int tiles = (int)(((a.M + kTM - 1) / kTM) * ((a.N + TN - 1) / TN));
-    if (kind == kWgrad)
-        hipLaunchKernelGGL((k_gemm_v1<TN, true, false>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+    const int64_t tiles_m = (a.M + kTM - 1) / kTM, tiles_n = (a.N + TN - 1) / TN;
+    const dim3 block(kV1Threads);
+    if (!grouped) {
+        const dim3 grid((unsigned)(tiles_m * tiles_n));
+        if (kind == kWgrad)
+            hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kDense>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense>), grid, block, 0, stream, a);
+    } else if (kind == kWgrad) {
+        const dim3 grid((unsigned)(tiles_m * tiles_n * a.E));
+        hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kGroupK>), grid, block, 0, stream, a);
+    } else {
+        // upper bound on the row tiles: sum over experts of ceil(len/256) <= ceil(M/256) + E
+        const dim3 grid((unsigned)((tiles_m + a.E) * tiles_n));
+        hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kGroupRows>), grid, block, 0, stream, a);
+    }
+}
+
+// The kernel addresses each operand through 32-bit byte offsets from its base:
+// row r of A is at r*lda, so (rows-1)*ld + 128 must stay within 2^32.
+static bool fits_32bit(int64_t rows, int64_t ld) { return rows <= 0 || (rows - 1) * ld + kTile <= (1ll << 32); }
+
+static bool gemm_offsets_fit(const GemmArgs& a)
+{
+    return fits_32bit(a.M, a.lda) && fits_32bit(a.N, a.ldb);
+}
+
+// Dense pieces: rows in steps of whole 256-row tiles, columns in steps of 1792
+// (a multiple of both tile widths and of the 128-wide weight tiles).
+static int64_t dense_row_step(const GemmArgs& a)
+{
+    const int64_t max_rows = a.lda > 0 ? ((1ll << 32) - kTile) / a.lda + 1 : a.M;
+    return a.M <= max_rows ? a.M : (max_rows / kTM) * kTM;
+}
+static int64_t dense_col_step(const GemmArgs& a)
+{
+    const int64_t max_cols = a.ldb > 0 ? ((1ll << 32) - kTile) / a.ldb + 1 : a.N;
+    return a.N <= max_cols ? a.N : (max_cols / 1792) * 1792;
+}
+
+bool gemm_supported(const GemmArgs& a, bool grouped)
+{
+    if (grouped) return gemm_offsets_fit(a) && a.M < (1ll << 31) && a.E < (1ll << 16);
+    return dense_row_step(a) > 0 && dense_col_step(a) > 0;
+}
+
+static hipError_t launch_one(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
+{
+    const int64_t units = grouped && kind == kWgrad ? a.M * a.E : a.M;
+    if (pick_tn(units, a.N) == 224)
+        launch_v1<224>(kind, grouped, a, stream);
     else
-        hipLaunchKernelGGL((k_gemm_v1<TN, false, true>), dim3(tiles), dim3(kV1Threads), 0, stream, a);
+        launch_v1<256>(kind, grouped, a, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
 {
-    if (!grouped) {
-        if (pick_tn(a.M, a.N) == 224)
-            launch_dense<224>(kind, a, stream);
-        else
-            launch_dense<256>(kind, a, stream);
-        return hipGetLastError();
-    }
-    const dim3 block(256);
-    if (kind == kWgrad) {
-        dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM), (unsigned)a.E);
-        hipLaunchKernelGGL((k_gemm<true, false, false, true>), grid, block, 0, stream, a);
-    } else {
-        dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM));
-        hipLaunchKernelGGL((k_gemm<false, true, true, false>), grid, block, 0, stream, a);
-    }
-    return hipGetLastError();
+    if (!gemm_supported(a, grouped)) return hipErrorInvalidValue;
+    if (grouped) return launch_one(kind, true, a, stream);
+    // Dense operands beyond 4 GiB: cut the output into row and column ranges
+    // whose operand slices fit the kernel's 32-bit offsets.
+    const int64_t rstep = dense_row_step(a), cstep = dense_col_step(a);
+    const int64_t osz = kind == kWgrad ? (int64_t)sizeof(float) : (int64_t)sizeof(uint16_t);
+    for (int64_t r0 = 0; r0 < a.M; r0 += rstep)
+        for (int64_t c0 = 0; c0 < a.N; c0 += cstep) {
+            GemmArgs p = a;
+            p.M = a.M - r0 < rstep ? a.M - r0 : rstep;
+            p.N = a.N - c0 < cstep ? a.N - c0 : cstep;
+            p.A = a.A + r0 * a.lda;
+            p.sa = a.sa + r0;
+            p.B = a.B + c0 * a.ldb;
+            p.sb = kind == kWgrad ? a.sb + c0 : a.sb + (c0 / kTile) * a.sb_n;
+            p.out = reinterpret_cast<uint8_t*>(a.out) + (r0 * a.ldo + c0) * osz;
+            const hipError_t e = launch_one(kind, false, p, stream);
+            if (e != hipSuccess) return e;
+        }
+    return hipSuccess;
 }
 
 }  // namespace fgb

@@ -215,3 +215,81 @@ def test_moe_down_sampled(orc, moe):
     hw = wgrad_hw_grouped(offsets, oqhT, oshT, oqdyT, osdyT, wrows, wcols)
     dwh = np.stack([host(dw[e])[np.ix_(wrows, wcols)] for e in range(E)])
     check_gemm(dwh, r, aabs, False, "moe down wgrad (all experts)", hw, int(np.diff(offsets).max()) // T)
+
+
+@pytest.mark.parametrize("E,N", [(100, 256), (70, 896)])
+def test_grouped_many_experts_tail_rows_untouched(orc, E, N):
+    """More experts than one wave has lanes (the tile search walks them in
+    chunks of 64), half-height row tiles, a 224-wide tile (N = 896), and rows
+    past offsets[E] that no expert owns: those output rows keep what they held."""
+    K = 256
+    g = np.random.default_rng(E)
+    loads = g.integers(1, 300, E)
+    loads[g.random(E) < 0.3] = 0
+    offsets, x, dy, ws = grouped_inputs(loads, K, N, E + 1)
+    R_used = int(offsets[-1])
+    R_pad = R_used + 384
+    x = np.concatenate([x, np.zeros((R_pad - R_used, K), np.uint16)])
+    dy = np.concatenate([dy, np.zeros((R_pad - R_used, N), np.uint16)])
+    od = offsets_dev(offsets)
+    qx, sx = fgb.quantize_1x128(bf16_dev(x))
+    qdy, sdy = fgb.quantize_1x128(bf16_dev(dy))
+    qw, qwT, sw = quant_weights_gpu(ws)
+    sentinel = torch.full((R_pad, max(N, K)), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = sentinel[:, :N].clone()
+    dx = sentinel[:, :K].clone()
+    fgb.gemm_fprop_grouped(od, qx, sx, qwT, sw, y=y)
+    fgb.gemm_dgrad_grouped(od, qdy, sdy, qw, sw, dx=dx)
+    qxT, sxT = fgb.requant_128x1(qx, sx)
+    qdyT, sdyT = fgb.quantize_128x1(bf16_dev(dy))
+    dw = fgb.gemm_wgrad_grouped(od, qxT, sxT, qdyT, sdyT)
+    torch.cuda.synchronize()
+    assert torch.all(y[R_used:] == 7.0) and torch.all(dx[R_used:] == 7.0)
+
+    oqx, osx = orc.quantize_1x128(x)
+    oqdy, osdy = orc.quantize_1x128(dy)
+    oqw, oqwT, osw = quant_weights_orc(orc, ws)
+    oqxT, osxT = orc.requant_128x1(oqx, osx)
+    oqdyT, osdyT = orc.quantize_128x1(dy)
+    # every expert, a few rows each (its first and last rows, the 128/256 boundaries)
+    rows = np.concatenate([int(offsets[e]) + sample_idx(int(offsets[e + 1] - offsets[e]), 6, e)
+                           for e in range(E) if offsets[e + 1] > offsets[e]])
+    cols, colsK = sample_idx(N, 40, 1), sample_idx(K, 40, 2)
+    hwf, hwd = np.zeros((rows.size, cols.size)), np.zeros((rows.size, colsK.size))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        pick = np.nonzero((rows >= a) & (rows < b))[0]
+        if pick.size:
+            hwf[pick] = hw_bound_fprop(oqx[a:b], osx[:, a:b], oqwT[e], osw[e], rows[pick] - a, cols)
+            hwd[pick] = hw_bound_dgrad(oqdy[a:b], osdy[:, a:b], oqw[e], osw[e], rows[pick] - a, colsK)
+    r, aabs = orc.gemm_fprop_grouped(offsets, oqx, osx, oqwT, osw, rows=rows, cols=cols)
+    check_gemm(bf16_host_f64(y)[np.ix_(rows, cols)], r, aabs, True, f"fprop grouped E={E}", hwf, K // T)
+    r, aabs = orc.gemm_dgrad_grouped(offsets, oqdy, osdy, oqw, osw, rows=rows, cols=colsK)
+    check_gemm(bf16_host_f64(dx)[np.ix_(rows, colsK)], r, aabs, True, f"dgrad grouped E={E}", hwd, N // T)
+    wr, wc = sample_idx(K, 24, 3), sample_idx(N, 24, 4)
+    r, aabs = orc.gemm_wgrad_grouped(offsets, oqxT, osxT, oqdyT, osdyT, rows=wr, cols=wc)
+    hw = wgrad_hw_grouped(offsets, oqxT, osxT, oqdyT, osdyT, wr, wc)
+    nbw = max(1, int(np.diff(offsets).max()) // T)
+    check_gemm(host(dw)[:, wr][:, :, wc], r, aabs, False, f"wgrad grouped E={E}", hw, nbw)
+
+
+def test_grouped_all_experts_empty():
+    """offsets all zero: no row tile exists; outputs keep their contents and
+    every expert's dW is zero."""
+    E, R_pad, K, N = 5, 256, 256, 256
+    od = offsets_dev([0] * (E + 1))
+    qx = torch.zeros((R_pad, K), dtype=torch.uint8, device="cuda")
+    sx = torch.ones((K // T, R_pad), dtype=torch.float32, device="cuda")
+    qwT = torch.ones((E, N, K), dtype=torch.uint8, device="cuda")
+    sw = torch.ones((E, K // T, N // T), dtype=torch.float32, device="cuda")
+    y = torch.full((R_pad, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    fgb.gemm_fprop_grouped(od, qx, sx, qwT, sw, y=y)
+    qxT = torch.ones((K, R_pad), dtype=torch.uint8, device="cuda")
+    sxT = torch.ones((R_pad // T, K), dtype=torch.float32, device="cuda")
+    qdyT = torch.ones((N, R_pad), dtype=torch.uint8, device="cuda")
+    sdyT = torch.ones((R_pad // T, N), dtype=torch.float32, device="cuda")
+    dw = torch.full((E, K, N), 9.0, dtype=torch.float32, device="cuda")
+    fgb.gemm_wgrad_grouped(od, qxT, sxT, qdyT, sdyT, dw=dw)
+    torch.cuda.synchronize()
+    assert torch.all(y == 5.0)
+    assert torch.all(dw == 0.0)
