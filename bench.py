@@ -15,7 +15,11 @@ against MI355X's dense FP8 MFMA peak, and `kernels` lists every kernel's rate
 against its own roofline (HBM for the quantizers).  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same step.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+`--workload moe_grouped` times the grouped expert GEMMs of one GPU's MoE share
+instead (32 experts, 8192 tokens routed top-8, gate/up and down projections,
+forward and backward); `value` then counts the routed rows' GEMM FLOP.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -72,6 +76,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=["linear_dsv3_attn", "moe_grouped"], default="linear_dsv3_attn",
+                   help="linear_dsv3_attn (default): the DeepSeek-V3 attention projection's linear; "
+                        "moe_grouped: the grouped expert GEMMs of one GPU's MoE share (no CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, run a plain streaming kernel (1 GiB read, 1 GiB "
@@ -94,6 +101,104 @@ def algorithmic_bytes(M, K, N):
     }
 
 
+def linear_step(fgb, torch, dev, d):
+    """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work)
+    per kernel, work = {"flop": ...} or {"bytes": ...} (algorithmic)."""
+    import numpy as np
+    M, K, N = d["M"], d["K"], d["N"]
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w, dy = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    Mp = -(-M // T) * T
+    b = {
+        "qx": torch.empty((M, K), **u8), "sx": torch.empty((K // T, M), **f32),
+        "qw": torch.empty((K, N), **u8), "qwT": torch.empty((N, K), **u8), "sw": torch.empty((K // T, N // T), **f32),
+        "y": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        "qdy": torch.empty((M, N), **u8), "sdy": torch.empty((N // T, M), **f32),
+        "dx": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+        "qdyT": torch.empty((N, Mp), **u8), "sdyT": torch.empty((Mp // T, N), **f32),
+        "qxT": torch.empty((K, Mp), **u8), "sxT": torch.empty((Mp // T, K), **f32),
+        "dw": torch.empty((K, N), **f32),
+    }
+    ab = algorithmic_bytes(M, K, N)
+    flop = {"flop": 2.0 * M * N * K}
+    return [
+        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]), {"bytes": ab["quantize_1x128_x"]}),
+        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"]),
+         {"bytes": ab["quantize_128x128_w"]}),
+        ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"]), flop),
+        ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"]), {"bytes": ab["quantize_1x128_dy"]}),
+        ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"]), flop),
+        ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"]),
+         {"bytes": ab["quantize_128x1_dy"]}),
+        ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
+         {"bytes": ab["requant_128x1_x"]}),
+        ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"]), flop),
+    ]
+
+
+def moe_step(fgb, torch, dev, d):
+    """The grouped expert GEMMs of one GPU's MoE share, both projections (gate/up
+    d_model -> 2*d_ff, down d_ff -> d_model), forward and backward.  GEMM work
+    counts the routed rows only (padding rows are computed but not counted);
+    weight quantization is one launch per expert."""
+    import numpy as np
+    E, R = d["E"], d["R_pad"]
+    rows = int(np.sum(d["loads"]))
+    od = torch.from_numpy(np.asarray(d["offsets"], np.int32)).to(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = []
+    for tag, xin, wts, dyin, K, N in [("up", "x", "w_up", "dy_up", d["d_model"], d["d_ff2"]),
+                                       ("down", "h", "w_down", "dy_down", d["d_ff"], d["d_model"])]:
+        x, dy = to_dev(d[xin]), to_dev(d[dyin])
+        w = to_dev(d[wts])                                   # [E, K, N]
+        b = {
+            "qx": torch.empty((R, K), **u8), "sx": torch.empty((K // T, R), **f32),
+            "qw": torch.empty((E, K, N), **u8), "qwT": torch.empty((E, N, K), **u8),
+            "sw": torch.empty((E, K // T, N // T), **f32),
+            "y": torch.empty((R, N), dtype=torch.bfloat16, device=dev),
+            "qdy": torch.empty((R, N), **u8), "sdy": torch.empty((N // T, R), **f32),
+            "dx": torch.empty((R, K), dtype=torch.bfloat16, device=dev),
+            "qdyT": torch.empty((N, R), **u8), "sdyT": torch.empty((R // T, N), **f32),
+            "qxT": torch.empty((K, R), **u8), "sxT": torch.empty((R // T, K), **f32),
+            "dw": torch.empty((E, K, N), **f32),
+        }
+        ab = algorithmic_bytes(R, K, N)
+
+        def quant_w(w=w, b=b):
+            for e in range(E):
+                fgb.quantize_128x128(w[e], q=b["qw"][e], qT=b["qwT"][e], s=b["sw"][e])
+
+        flop = {"flop": 2.0 * rows * K * N}
+        out += [
+            (f"{tag}.quantize_1x128_x", lambda x=x, b=b: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]),
+             {"bytes": ab["quantize_1x128_x"]}),
+            (f"{tag}.quantize_128x128_w", quant_w, {"bytes": E * ab["quantize_128x128_w"]}),
+            (f"{tag}.gemm_fprop_grouped",
+             lambda b=b: fgb.gemm_fprop_grouped(od, b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"]), flop),
+            (f"{tag}.quantize_1x128_dy", lambda dy=dy, b=b: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"]),
+             {"bytes": ab["quantize_1x128_dy"]}),
+            (f"{tag}.gemm_dgrad_grouped",
+             lambda b=b: fgb.gemm_dgrad_grouped(od, b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"]), flop),
+            (f"{tag}.quantize_128x1_dy", lambda dy=dy, b=b: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"]),
+             {"bytes": ab["quantize_128x1_dy"]}),
+            (f"{tag}.requant_128x1_x", lambda b=b: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
+             {"bytes": ab["requant_128x1_x"]}),
+            (f"{tag}.gemm_wgrad_grouped",
+             lambda b=b: fgb.gemm_wgrad_grouped(od, b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], dw=b["dw"]), flop),
+        ]
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -108,40 +213,24 @@ def main():
     from fine_grained_block_amd import workloads as wl
 
     dev = torch.device("cuda:0")
-    d = wl.linear_dsv3_attn()
-    M, K, N = d["M"], d["K"], d["N"]
-
-    def to_dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    x, w, dy = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
-    u8 = dict(dtype=torch.uint8, device=dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    Mp = -(-M // T) * T
-    buf = {
-        "qx": torch.empty((M, K), **u8), "sx": torch.empty((K // T, M), **f32),
-        "qw": torch.empty((K, N), **u8), "qwT": torch.empty((N, K), **u8), "sw": torch.empty((K // T, N // T), **f32),
-        "y": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
-        "qdy": torch.empty((M, N), **u8), "sdy": torch.empty((N // T, M), **f32),
-        "dx": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
-        "qdyT": torch.empty((N, Mp), **u8), "sdyT": torch.empty((Mp // T, N), **f32),
-        "qxT": torch.empty((K, Mp), **u8), "sxT": torch.empty((Mp // T, K), **f32),
-        "dw": torch.empty((K, N), **f32),
-    }
-    b = buf
-    kernels = [
-        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"])),
-        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"])),
-        ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"])),
-        ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"])),
-        ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"])),
-        ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"])),
-        ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"])),
-        ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"])),
-    ]
+    if args.workload == "linear_dsv3_attn":
+        d = wl.linear_dsv3_attn()
+        kernels = linear_step(fgb, torch, dev, d)
+        config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]",
+                  "M": d["M"], "K": d["K"], "N": d["N"]}
+        data = "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)"
+    else:
+        d = wl.moe_grouped()
+        kernels = moe_step(fgb, torch, dev, d)
+        config = {"workload": "moe_grouped fwd+bwd, one GPU's expert share: 32 experts, 8192 tokens top-8 "
+                              "(Zipf 1.1 loads, 3 empty), W_up [7168,4096], W_down [2048,7168] per expert",
+                  "experts": d["E"], "routed_rows": int(np.sum(d["loads"])), "R_pad": d["R_pad"]}
+        data = "synthetic (seeded N(0,1) X and H, N(0,0.02) W, N(0,1e-3) dY; bf16)"
+        del d
+        args.no_cpu_baseline = True
 
     def step(events=None):
-        for i, (_, fn) in enumerate(kernels):
+        for i, (_, fn, _) in enumerate(kernels):
             if events is not None:
                 events[i][0].record()
             fn()
@@ -165,30 +254,30 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
     per_kernel_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
-                     for i, (name, _) in enumerate(kernels)}
+                     for i, (name, _, _) in enumerate(kernels)}
+    work = {name: w for name, _, w in kernels}
 
-    gemm_flop = 2.0 * M * N * K
-    step_flop = 3 * gemm_flop
+    step_flop = sum(w.get("flop", 0.0) for w in work.values())
+    quant_bytes = sum(w.get("bytes", 0) for w in work.values())
     value = step_flop / (ms_per_step * 1e-3) / 1e12
-    abytes = algorithmic_bytes(M, K, N)
     kinfo = {}
     for name, ms in per_kernel_ms.items():
-        if name.startswith("gemm"):
-            rate = gemm_flop / (ms * 1e-3)
+        if "flop" in work[name]:
+            rate = work[name]["flop"] / (ms * 1e-3)
             kinfo[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(rate / 1e12, 1),
                            "frac_fp8_peak": round(rate / FP8_PEAK, 4)}
         else:
-            rate = abytes[name] / (ms * 1e-3)
+            rate = work[name]["bytes"] / (ms * 1e-3)
             kinfo[name] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
-                           "frac_hbm_peak": round(rate / HBM_PEAK, 4), "bytes": abytes[name]}
-    gemms = {k: v for k, v in per_kernel_ms.items() if k.startswith("gemm")}
+                           "frac_hbm_peak": round(rate / HBM_PEAK, 4), "bytes": work[name]["bytes"]}
+    gemms = {k: v for k, v in per_kernel_ms.items() if "flop" in work[k]}
     dom = max(gemms, key=gemms.get)
-    dom_rate = gemm_flop / (gemms[dom] * 1e-3)
+    dom_rate = work[dom]["flop"] / (gemms[dom] * 1e-3)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_rate / 1e12, 1),
                 "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(dom_rate / FP8_PEAK, 4),
                 "traffic": traffic_record(dom)}
-    quant_ms = sum(v for k, v in per_kernel_ms.items() if not k.startswith("gemm"))
-    quant_bytes = sum(abytes.values())
+    quant_ms = sum(v for k, v in per_kernel_ms.items() if "bytes" in work[k])
+    config.update({"gemm_flop_per_step": step_flop, "quant_bytes_per_step": quant_bytes})
 
     out = {
         "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak) + quant GB/s (% HBM) at 1 GPU",
@@ -202,10 +291,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "e4m3 x e4m3 -> fp32 accumulate (bf16 in/out, fp32 dW)",
-        "data": "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)",
-        "config": {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]",
-                   "M": M, "K": K, "N": N, "gemm_flop_per_step": step_flop,
-                   "quant_bytes_per_step": quant_bytes},
+        "data": data,
+        "config": config,
         "quant_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quant_frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / HBM_PEAK, 4),
         "roofline": roofline,
@@ -221,7 +308,7 @@ def main():
         del a, c
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(d, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(wl.linear_dsv3_attn(), args.cpu_rows)
     print(json.dumps(out), flush=True)
 
 

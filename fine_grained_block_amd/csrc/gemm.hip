@@ -218,10 +218,12 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         Bp += rt.e * g.b_expert_stride;
         sbp += rt.e * g.sb_expert_stride;
     } else {
+        // experts in order, each expert's tiles spread over all 8 XCDs (experts
+        // differ in contraction length, so whole experts per XCD would leave
+        // the XCDs unevenly loaded)
         const int tiles_m = (int)((g.M + kTM - 1) / kTM), per_e = tiles_m * tiles_n;
-        const int t = xcd_order(blockIdx.x, per_e * (int)g.E);
-        const int e = t / per_e;
-        group_order(t - e * per_e, tiles_m, tiles_n, tm, tn);
+        const int e = (int)blockIdx.x / per_e;
+        group_order(xcd_order((int)blockIdx.x - e * per_e, per_e), tiles_m, tiles_n, tm, tn);
         m0 = (int64_t)tm * kTM;
         // contraction blocks of expert e, clamped to the nkb blocks that exist
         int64_t b0 = g.offsets[e] / kTile, b1 = g.offsets[e + 1] / kTile;
