@@ -4,8 +4,8 @@ at the DeepSeek-V3 attention-projection shape X [4096, 7168], W [7168, 7168],
 dY [4096, 7168] (synthetic, seeded; inputs resident in HBM):
 
   quantize X 1x128 -> quantize W 128x128 (both layouts) -> Fprop Y = X W (bf16)
-  -> quantize dY 1x128 -> Dgrad dX = dY W^T (bf16)
-  -> quantize dY 128x1 -> requant X 128x1 -> Wgrad dW = X^T dY (fp32)
+  -> quantize dY 1x128 and 128x1 (one fused read) -> Dgrad dX = dY W^T (bf16)
+  -> requant X 128x1 -> Wgrad dW = X^T dY (fp32)
 
 Prints one JSON line.  `value` is the step's GEMM throughput (3 x 2*M*N*K
 FLOP over the whole step time, quantization included) in TFLOP/s.  Per-kernel
@@ -80,6 +80,8 @@ def parse():
                    help="linear_dsv3_attn (default): the DeepSeek-V3 attention projection's linear; "
                         "moe_grouped: the grouped expert GEMMs of one GPU's MoE share (no CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--separate-dy-casts", action="store_true",
+                   help="quantize dY with two kernels (1x128, then 128x1) instead of the fused one")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, run a plain streaming kernel (1 GiB read, 1 GiB "
                         "written) three times: it scales rocprofv3's FETCH_SIZE/WRITE_SIZE to bytes")
@@ -98,10 +100,11 @@ def algorithmic_bytes(M, K, N):
         "quantize_1x128_dy": M * N * 2 + M * N + nbN * M * 4,
         "quantize_128x1_dy": M * N * 2 + N * Mp + nbM * N * 4,
         "requant_128x1_x": M * K + nbK * M * 4 + K * Mp + nbM * K * 4,
+        "quantize_dual_dy": M * N * 2 + M * N + nbN * M * 4 + N * Mp + nbM * N * 4,
     }
 
 
-def linear_step(fgb, torch, dev, d):
+def linear_step(fgb, torch, dev, d, separate_dy=False):
     """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work)
     per kernel, work = {"flop": ...} or {"bytes": ...} (algorithmic)."""
     import numpy as np
@@ -126,15 +129,25 @@ def linear_step(fgb, torch, dev, d):
     }
     ab = algorithmic_bytes(M, K, N)
     flop = {"flop": 2.0 * M * N * K}
+    if separate_dy:
+        dy_casts = [
+            ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"]),
+             {"bytes": ab["quantize_1x128_dy"]}),
+            ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"]),
+             {"bytes": ab["quantize_128x1_dy"]}),
+        ]
+    else:
+        dy_casts = [
+            ("quantize_dual_dy", lambda: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
+             {"bytes": ab["quantize_dual_dy"]}),
+        ]
     return [
         ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]), {"bytes": ab["quantize_1x128_x"]}),
         ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"]),
          {"bytes": ab["quantize_128x128_w"]}),
         ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"]), flop),
-        ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"]), {"bytes": ab["quantize_1x128_dy"]}),
+    ] + dy_casts + [
         ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"]), flop),
-        ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"]),
-         {"bytes": ab["quantize_128x1_dy"]}),
         ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
          {"bytes": ab["requant_128x1_x"]}),
         ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"]), flop),
@@ -185,12 +198,11 @@ def moe_step(fgb, torch, dev, d):
             (f"{tag}.quantize_128x128_w", quant_w, {"bytes": E * ab["quantize_128x128_w"]}),
             (f"{tag}.gemm_fprop_grouped",
              lambda b=b: fgb.gemm_fprop_grouped(od, b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"]), flop),
-            (f"{tag}.quantize_1x128_dy", lambda dy=dy, b=b: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"]),
-             {"bytes": ab["quantize_1x128_dy"]}),
+            (f"{tag}.quantize_dual_dy",
+             lambda dy=dy, b=b: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
+             {"bytes": ab["quantize_dual_dy"]}),
             (f"{tag}.gemm_dgrad_grouped",
              lambda b=b: fgb.gemm_dgrad_grouped(od, b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"]), flop),
-            (f"{tag}.quantize_128x1_dy", lambda dy=dy, b=b: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"]),
-             {"bytes": ab["quantize_128x1_dy"]}),
             (f"{tag}.requant_128x1_x", lambda b=b: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
              {"bytes": ab["requant_128x1_x"]}),
             (f"{tag}.gemm_wgrad_grouped",
@@ -215,7 +227,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "linear_dsv3_attn":
         d = wl.linear_dsv3_attn()
-        kernels = linear_step(fgb, torch, dev, d)
+        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts)
         config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]",
                   "M": d["M"], "K": d["K"], "N": d["N"]}
         data = "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)"

@@ -37,6 +37,7 @@ _P, _I, _F, _N = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
 SIGNATURES = {
     "fgb_quantize_1x128": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
     "fgb_quantize_128x1": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
+    "fgb_quantize_dual": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _P],
     "fgb_quantize_128x128": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _P],
     "fgb_requant_128x1": [_P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P],
     "fgb_gemm_fprop": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
@@ -132,6 +133,25 @@ def quantize_128x1(x: torch.Tensor, amax_floor: float = 0.0, qT=None, sT=None):
     _check(lib().fgb_quantize_128x1(_ptr(x), R, C, ldx, amax_floor, _ptr(qT), _rows(qT, torch.uint8, "qT"),
                                     _ptr(sT), _rows(sT, torch.float32, "sT"), _stream(x)), "quantize_128x1")
     return qT, sT
+
+
+def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=None, sT=None):
+    """Both orientations from one read: (q, s) as quantize_1x128, (qT, sT) as quantize_128x1."""
+    R, C = x.shape
+    ldx = _rows(x, torch.bfloat16, "x")
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device)
+    if qT is None:
+        qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=x.device)
+    if sT is None:
+        sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=x.device)
+    _check(lib().fgb_quantize_dual(_ptr(x), R, C, ldx, amax_floor,
+                                   _ptr(q), _rows(q, torch.uint8, "q"), _ptr(s), _rows(s, torch.float32, "s"),
+                                   _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT), _rows(sT, torch.float32, "sT"),
+                                   _stream(x)), "quantize_dual")
+    return q, s, qT, sT
 
 
 def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = True, want_qT: bool = True,

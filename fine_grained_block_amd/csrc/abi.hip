@@ -100,6 +100,22 @@ int fgb_quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, flo
                                           nullptr, 0, qT, ldqT, sT, ldsT, as_stream(stream)));
 }
 
+int fgb_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                      uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+{
+    if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
+    if (bad_floor(amax_floor)) return FGB_E_ARG;
+    if (R == 0 || C == 0) return FGB_OK;
+    FGB_TRY(check_bf16(x, ldx, C));
+    FGB_TRY(check_codes(q, ldq, C, 8));
+    FGB_TRY(check_scales(s, lds, R));
+    FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
+    FGB_TRY(check_scales(sT, ldsT, C));
+    return hip_status(fgb::launch_tile128(fgb::kTileDual, x, R, C, ldx, nullptr, 0, amax_floor,
+                                          q, ldq, qT, ldqT, sT, ldsT, as_stream(stream), s, lds));
+}
+
 int fgb_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
                          uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, void* stream)
 {

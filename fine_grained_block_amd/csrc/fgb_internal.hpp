@@ -12,16 +12,19 @@ hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_
                                  float amax_floor, uint8_t* q, int64_t ldq,
                                  float* s, int64_t lds, hipStream_t stream);
 
-enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2 };
+enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 3 };
 
 // 128x128 tile kernels over a [R][C] input:
 //   kTile128x1:   bf16 in, per-column 128-row scales, transposed codes out (qT, sT)
 //   kTile128x128: bf16 in, one scale per tile, q and/or qT out, s [R/128][C/128]
 //   kTileRequant: E4M3 + 1x128 scales in, then as kTile128x1
+//   kTileDual:    bf16 in, both the 1x128 codes and scales (q, s_row) and the
+//                 128x1 transposed codes and scales (qT, sT) from one read
 hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
-                          float* s_out, int64_t lds_out, hipStream_t stream);
+                          float* s_out, int64_t lds_out, hipStream_t stream,
+                          float* s_row = nullptr, int64_t lds_row = 0);
 
 // ------------------------------- GEMMs -------------------------------------
 // out[m][n] = sum_b SA(m,b) * SB(n,b) * sum_{t in block b} dec(A[m][t]) dec(B[n][t])

@@ -76,7 +76,8 @@ hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_
 }
 
 // ---------------------------------------------------------------------------
-// 128x128-element tile kernels (128x1 columns, 128x128 weight tiles, requant).
+// 128x128-element tile kernels (128x1 columns, 128x128 weight tiles, requant,
+// and the dual 1x128 + 128x1 quantization of one tensor).
 // Block = 256 threads over rows [r0, r0+128) x columns [c0, c0+128).  Thread t
 // holds an 8x8 patch: columns c0 + 8*(t%16) .. +8, rows r0 + 8*(t/16) .. +8.
 // Column maxima combine the 4 patches of a wave with lane swizzles and the 4
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void k_tile128(
     const void* __restrict__ in, int64_t R, int64_t C, int64_t ldin,
     const float* __restrict__ s_in, int64_t lds_in, float amax_floor,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
-    float* __restrict__ s_out, int64_t lds_out)
+    float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row)
 {
     __shared__ uint32_t red[4][kTile];
     __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kTrStride];
@@ -174,6 +175,30 @@ __global__ __launch_bounds__(256) void k_tile128(
         }
     }
 
+    // Dual mode, 1x128 part: row r's tile is the block's 128 columns of row r,
+    // held by the 16 lanes that share rg; their absmax is one DPP reduction.
+    if constexpr (MODE == kTileDual) {
+        float sr_own = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
+            m = max16(m);
+            const float a = fmaxf(__uint_as_float(m), amax_floor);
+            float sc, iv;
+            tile_scale(a, sc, iv);
+            if (cg == i) sr_own = sc;
+            const int64_t r = r0 + rg * 8 + i;
+            const uint32_t o0 = e4m3x4(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
+            const uint32_t o1 = e4m3x4(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
+            if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
+        }
+        // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
+        const int64_t rr = r0 + rg * 8 + cg;
+        if (cg < 8 && rr < R) s_row[(int64_t)blockIdx.y * lds_row + rr] = sr_own;
+    }
+
     // Row-major codes (128x128 weights, q != nullptr): 8 bytes per patch row.
     if constexpr (MODE == kTile128x128) {
         if (q != nullptr) {
@@ -211,21 +236,26 @@ __global__ __launch_bounds__(256) void k_tile128(
 hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
-                          float* s_out, int64_t lds_out, hipStream_t stream)
+                          float* s_out, int64_t lds_out, hipStream_t stream,
+                          float* s_row, int64_t lds_row)
 {
     dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
     switch (mode) {
     case kTile128x1:
         hipLaunchKernelGGL(k_tile128<kTile128x1>, grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     case kTile128x128:
         hipLaunchKernelGGL(k_tile128<kTile128x128>, grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     case kTileRequant:
         hipLaunchKernelGGL(k_tile128<kTileRequant>, grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
+        break;
+    case kTileDual:
+        hipLaunchKernelGGL(k_tile128<kTileDual>, grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     }
     return hipGetLastError();

@@ -103,6 +103,19 @@ int fgb_quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                        uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                        void* stream);
 
+/* Both orientations of one tensor from a single read of x [R][C] (bf16):
+ * the 1x128 codes and scales of fgb_quantize_1x128 (q [R][ldq], s
+ * [ceil(C/128)][lds]) and the 128x1 transposed codes and scales of
+ * fgb_quantize_128x1 (qT [C][ldqT] zero padded, sT [ceil(R/128)][ldsT]),
+ * bit for bit the same as the two separate calls ([scratch]: backward casts
+ * emit both tile orientations of dY, "+T").  Argument rules are those of
+ * the two calls; C % 8 == 0. */
+int fgb_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                      float amax_floor,
+                      uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                      void* stream);
+
 /* 128x128 tiles of a weight w [K][N] (bf16, ldw >= N), K and N multiples of
  * 128.  Writes q [K][N] (ldq >= N) and/or its transpose qT [N][K]
  * (ldqT >= K); either may be NULL but not both.  Scales s [K/128][N/128]

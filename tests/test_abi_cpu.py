@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = fgb.lib()
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fgb.SIGNATURES)
@@ -76,6 +76,26 @@ def test_quantize_128x1_validation():
     assert f(C=100) == E_SHAPE
     assert f(lds=127) == E_LD
     assert f(R=0) == OK
+
+
+def test_quantize_dual_validation():
+    L = fgb.lib()
+    E = P(0x50000)
+    f = lambda **k: L.fgb_quantize_dual(k.get("x", A), k.get("R", 200), k.get("C", 128), k.get("ldx", 128),
+                                        k.get("fl", 0.0), k.get("q", B), k.get("ldq", 128), k.get("s", C_),
+                                        k.get("lds", 200), k.get("qT", D), k.get("ldqT", 256), k.get("sT", E),
+                                        k.get("ldsT", 128), None)
+    assert f(C=100) == E_SHAPE
+    assert f(fl=-1.0) == E_ARG
+    assert f(x=None) == E_NULL
+    assert f(q=None) == E_NULL
+    assert f(sT=None) == E_NULL
+    assert f(ldq=120) == E_LD
+    assert f(lds=199) == E_LD
+    assert f(ldqT=200) == E_LD         # must cover roundup(200, 128) = 256
+    assert f(ldsT=127) == E_LD
+    assert f(qT=P(0x40008), ldqT=264) == E_ALIGN
+    assert f(R=0) == OK and f(C=0) == OK
 
 
 def test_quantize_128x128_validation():

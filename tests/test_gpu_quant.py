@@ -51,6 +51,19 @@ def test_128x1_small(orc, R, C):
     assert_scales_equal(sT, osT, f"sT[{R}x{C}]")
 
 
+@pytest.mark.parametrize("R,C", SMALL)
+def test_dual_small(orc, R, C):
+    """One read, both orientations: each output equals the oracle's 1x128 or 128x1 result."""
+    x = stress(R, C, 2500 + R * 7 + C)
+    q, s, qT, sT = fgb.quantize_dual(bf16_dev(x))
+    oq, os_ = orc.quantize_1x128(x)
+    oqT, osT = orc.quantize_128x1(x)
+    assert_codes_equal(q, oq, f"dual q[{R}x{C}]")
+    assert_scales_equal(s, os_, f"dual s[{R}x{C}]")
+    assert_codes_equal(qT, oqT, f"dual qT[{R}x{C}]")
+    assert_scales_equal(sT, osT, f"dual sT[{R}x{C}]")
+
+
 @pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (384, 128)])
 def test_128x128_small(orc, K, N):
     w = stress(K, N, 3000 + K + N)
@@ -90,6 +103,11 @@ def test_amax_floor(orc):
         oqT, osT = orc.quantize_128x1(x, amax_floor=fl)
         assert_codes_equal(qT, oqT, f"qT floor {fl}")
         assert_scales_equal(sT, osT, f"sT floor {fl}")
+        q, s, qT, sT = fgb.quantize_dual(bf16_dev(x), amax_floor=fl)
+        assert_codes_equal(q, oq, f"dual q floor {fl}")
+        assert_scales_equal(s, os_, f"dual s floor {fl}")
+        assert_codes_equal(qT, oqT, f"dual qT floor {fl}")
+        assert_scales_equal(sT, osT, f"dual sT floor {fl}")
     w = stress(256, 256, 6)
     q, qT, s = fgb.quantize_128x128(bf16_dev(w), amax_floor=2.0)
     oq, oqT, os_ = orc.quantize_128x128(w, amax_floor=2.0)
@@ -115,6 +133,19 @@ def test_strided_operands(orc):
     oqT, _ = orc.quantize_128x1(x)
     assert_codes_equal(qTbuf[:, :256], oqT, "qT strided")
     assert np.all(host(qTbuf[:, 256:]) == 0xCD)
+    # dual: all four outputs as views of wider buffers
+    qbuf.fill_(0xAB)
+    qTbuf.fill_(0xCD)
+    sbuf.zero_()
+    sTbuf = torch.zeros((2, C + 8), dtype=torch.float32, device="cuda")
+    fgb.quantize_dual(wide[:, :C], q=qbuf[:, :C], s=sbuf[:, :R], qT=qTbuf[:, :256], sT=sTbuf[:, :C])
+    _, osT = orc.quantize_128x1(x)
+    assert_codes_equal(qbuf[:, :C], oq, "dual q strided")
+    assert_scales_equal(sbuf[:, :R], os_, "dual s strided")
+    assert_codes_equal(qTbuf[:, :256], oqT, "dual qT strided")
+    assert_scales_equal(sTbuf[:, :C], osT, "dual sT strided")
+    assert np.all(host(qbuf[:, C:]) == 0xAB) and np.all(host(qTbuf[:, 256:]) == 0xCD)
+    assert np.all(host(sbuf[:, R:]) == 0) and np.all(host(sTbuf[:, C:]) == 0)
 
 
 def test_deterministic_repeat():
@@ -143,7 +174,12 @@ def test_quant_stress_full(orc):
     oqT, osT = orc.quantize_128x1(x)
     assert_codes_equal(qT, oqT, "stress 128x1 qT")
     assert_scales_equal(sT, osT, "stress 128x1 sT")
-    del qT, sT, oqT, osT
+    dq, ds, dqT, dsT = fgb.quantize_dual(xd)
+    assert_codes_equal(dq, oq, "stress dual q")
+    assert_scales_equal(ds, os_, "stress dual s")
+    assert_codes_equal(dqT, oqT, "stress dual qT")
+    assert_scales_equal(dsT, osT, "stress dual sT")
+    del qT, sT, oqT, osT, dq, ds, dqT, dsT
     qw, qwT, sw = fgb.quantize_128x128(xd)
     oqw, oqwT, osw = orc.quantize_128x128(x)
     assert_codes_equal(qw, oqw, "stress 128x128 q")
@@ -173,6 +209,12 @@ def test_linear_workload_quantizers_full(orc):
     oqT, osT = orc.quantize_128x1(d["dy"])
     assert_codes_equal(qT, oqT, "dy 128x1")
     assert_scales_equal(sT, osT, "dy 128x1 s")
+    q, s, qT, sT = fgb.quantize_dual(bf16_dev(d["dy"]))
+    oq, os_ = orc.quantize_1x128(d["dy"])
+    assert_codes_equal(q, oq, "dy dual 1x128")
+    assert_scales_equal(s, os_, "dy dual 1x128 s")
+    assert_codes_equal(qT, oqT, "dy dual 128x1")
+    assert_scales_equal(sT, osT, "dy dual 128x1 s")
     q, qT, s = fgb.quantize_128x128(bf16_dev(d["w"]))
     oq, oqT, os_ = orc.quantize_128x128(d["w"])
     assert_codes_equal(q, oq, "w q")
