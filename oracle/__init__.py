@@ -25,6 +25,9 @@ function computes, with the passage it follows:
   output dtypes from the "scratch" page (Fprop/Dgrad BF16, Wgrad FP32).
 * ``*_grouped`` -- the same per expert over 128-aligned row segments (grouped
   expert GEMMs with empty experts, prime-rl PR #4073 "Validation completed").
+* ``*_ue8m0`` quantizers -- power-of-two scales stored as E8M0 bytes (prime-rl
+  PR #4073 "Results": the power-of-two scale format); the GEMMs take them as
+  fp32 scales through ``e8m0_decode``.
 
 The GEMM functions return the exact-to-fp64 value ``r`` and the absolute sum
 ``aabs`` (sum of |terms|), not a rounded output; callers compare the GPU's
@@ -90,6 +93,12 @@ def _load():
     lib.orc_quantize_128x1.argtypes = [P, I64, I64, I64, F, P, I64, P, I64]
     lib.orc_quantize_128x128.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, P]
     lib.orc_requant_128x1.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64]
+    lib.orc_e8m0_decode.restype = ctypes.c_double
+    lib.orc_e8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_quantize_1x128_ue8m0.argtypes = [P, I64, I64, I64, F, P, I64, P, I64]
+    lib.orc_quantize_128x1_ue8m0.argtypes = [P, I64, I64, I64, F, P, I64, P, I64]
+    lib.orc_quantize_128x128_ue8m0.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, P]
+    lib.orc_requant_128x1_ue8m0.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64]
     lib.orc_gemm_block_scaled.argtypes = [I64, P, I64, P, I64, I64, I64,
                                           P, I64, P, I64, I64, I64,
                                           P, I64, P, I64, P, P]
@@ -207,6 +216,65 @@ def requant_128x1(q, s):
     sT = np.empty((_cdiv(R, TILE), C), np.float32)
     _load().orc_requant_128x1(_ptr(q), R, C, C, _ptr(s), R, _ptr(qT), Rp, _ptr(sT), C)
     return qT, sT
+
+
+# --------------------------------------------------------------------------
+# Power-of-two (UE8M0) scales: the same tilings, each scale 2^e stored as the
+# E8M0 byte e + 127, e the smallest integer with 448 * 2^e >= absmax
+# (prime-rl PR #4073 "Results": power-of-two scales; rounding up is a reading).
+# --------------------------------------------------------------------------
+
+def e8m0_decode(e) -> np.ndarray:
+    """E8M0 bytes -> float64 scales 2^(byte - 127) (0xFF -> NaN)."""
+    e = np.asarray(e, np.uint8)
+    lib = _load()
+    table = np.array([lib.orc_e8m0_decode(u) for u in range(256)])
+    return table[e]
+
+
+def quantize_1x128_ue8m0(x_bits, amax_floor: float = 0.0):
+    """bf16 bits [R, C] -> (q [R, C] uint8, e [ceil(C/128), R] uint8)."""
+    x = _c(x_bits, np.uint16)
+    R, C = x.shape
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((_cdiv(C, TILE), R), np.uint8)
+    _load().orc_quantize_1x128_ue8m0(_ptr(x), R, C, C, amax_floor, _ptr(q), C, _ptr(e), R)
+    return q, e
+
+
+def quantize_128x1_ue8m0(x_bits, amax_floor: float = 0.0):
+    """bf16 bits [R, C] -> (qT [C, roundup(R,128)] zero padded, eT [ceil(R/128), C])."""
+    x = _c(x_bits, np.uint16)
+    R, C = x.shape
+    Rp = _cdiv(R, TILE) * TILE
+    qT = np.empty((C, Rp), np.uint8)
+    eT = np.empty((_cdiv(R, TILE), C), np.uint8)
+    _load().orc_quantize_128x1_ue8m0(_ptr(x), R, C, C, amax_floor, _ptr(qT), Rp, _ptr(eT), C)
+    return qT, eT
+
+
+def quantize_128x128_ue8m0(w_bits, amax_floor: float = 0.0):
+    """bf16 bits [K, N] -> (q [K, N], qT [N, K], e [ceil(K/128), ceil(N/128)])."""
+    w = _c(w_bits, np.uint16)
+    K, N = w.shape
+    q = np.empty((K, N), np.uint8)
+    qT = np.empty((N, K), np.uint8)
+    e = np.empty((_cdiv(K, TILE), _cdiv(N, TILE)), np.uint8)
+    _load().orc_quantize_128x128_ue8m0(_ptr(w), K, N, N, amax_floor, _ptr(q), N, _ptr(qT), K, _ptr(e))
+    return q, qT, e
+
+
+def requant_128x1_ue8m0(q, e):
+    """UE8M0 1x128 codes q [R, C] with bytes e [ceil(C/128), R] -> (qT, eT) as quantize_128x1_ue8m0."""
+    q = _c(q, np.uint8)
+    e = _c(e, np.uint8)
+    R, C = q.shape
+    assert e.shape == (_cdiv(C, TILE), R)
+    Rp = _cdiv(R, TILE) * TILE
+    qT = np.empty((C, Rp), np.uint8)
+    eT = np.empty((_cdiv(R, TILE), C), np.uint8)
+    _load().orc_requant_128x1_ue8m0(_ptr(q), R, C, C, _ptr(e), R, _ptr(qT), Rp, _ptr(eT), C)
+    return qT, eT
 
 
 # --------------------------------------------------------------------------

@@ -277,6 +277,146 @@ void orc_requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
 }
 
 /* ------------------------------------------------------------------ */
+/* Power-of-two (UE8M0) scale variant                                  */
+/* ------------------------------------------------------------------ */
+
+/* One tile with a power-of-two scale (prime-rl PR #4073, "Results": the
+ * power-of-two / UE8M0 scale format and its two-stage requant; the pages fix
+ * no rounding direction, read here as rounding the scale up):
+ *   a   = max |v|, a' = max(a, amax_floor)
+ *   e   = the smallest integer with 448 * 2^e >= a', clamped to [-127, 127]
+ *         (an all-zero tile gets -127); stored as the byte e + 127, the E8M0
+ *         encoding of 2^e
+ *   q_i = enc(fl32(v_i * 2^-e))
+ * The scaled values never exceed 448 in magnitude, so no code saturates
+ * unless e was clamped.  A NaN in the tile stores the E8M0 NaN byte 0xFF. */
+static void quantize_tile_ue8m0(const float* v, int64_t n, float amax_floor,
+                                uint8_t* e_out, uint8_t* q_out)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float av = fabsf(v[i]);
+        if (isnan(av) || av > a) a = av;
+        if (isnan(a)) break;
+    }
+    if (amax_floor > a) a = amax_floor;
+    if (isnan(a)) {
+        *e_out = 0xFF;
+        for (int64_t i = 0; i < n; ++i) q_out[i] = orc_e4m3_encode(NAN);
+        return;
+    }
+    int e = -127;
+    while (e < 127 && ldexp(448.0, e) < (double)a) ++e;
+    *e_out = (uint8_t)(e + 127);
+    const double m = ldexp(1.0, -e);
+    for (int64_t i = 0; i < n; ++i) q_out[i] = orc_e4m3_encode((float)((double)v[i] * m));
+}
+
+/* E8M0 byte -> the scale 2^(byte - 127); 0xFF is NaN. */
+double orc_e8m0_decode(uint8_t b)
+{
+    return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+/* As orc_quantize_1x128, with the UE8M0 rule; e[j*lde + r] is the byte of tile (r, j). */
+void orc_quantize_1x128_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                              float amax_floor, uint8_t* q, int64_t ldq,
+                              uint8_t* e, int64_t lde)
+{
+    int64_t nb = ceil_div(C, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        float v[ORC_TILE];
+        uint8_t code[ORC_TILE];
+        for (int64_t j = 0; j < nb; ++j) {
+            int64_t c0 = j * ORC_TILE;
+            int64_t n = (C - c0 < ORC_TILE) ? C - c0 : ORC_TILE;
+            for (int64_t i = 0; i < n; ++i) v[i] = orc_bf16_to_float(x[r * ldx + c0 + i]);
+            quantize_tile_ue8m0(v, n, amax_floor, &e[j * lde + r], code);
+            for (int64_t i = 0; i < n; ++i) q[r * ldq + c0 + i] = code[i];
+        }
+    }
+}
+
+/* As quantize_128x1_f32, with the UE8M0 rule. */
+static void quantize_128x1_f32_ue8m0(const float* xf, int64_t R, int64_t C, int64_t ldxf,
+                                     float amax_floor, uint8_t* qT, int64_t ldqT,
+                                     uint8_t* eT, int64_t ldeT)
+{
+    int64_t nb = ceil_div(R, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        float v[ORC_TILE];
+        uint8_t code[ORC_TILE];
+        for (int64_t i = 0; i < nb; ++i) {
+            int64_t r0 = i * ORC_TILE;
+            int64_t n = (R - r0 < ORC_TILE) ? R - r0 : ORC_TILE;
+            for (int64_t k = 0; k < n; ++k) v[k] = xf[(r0 + k) * ldxf + c];
+            quantize_tile_ue8m0(v, n, amax_floor, &eT[i * ldeT + c], code);
+            for (int64_t k = 0; k < ORC_TILE; ++k)
+                qT[c * ldqT + r0 + k] = (k < n) ? code[k] : 0x00;
+        }
+    }
+}
+
+void orc_quantize_128x1_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                              float amax_floor, uint8_t* qT, int64_t ldqT,
+                              uint8_t* eT, int64_t ldeT)
+{
+    float* xf = (float*)malloc((size_t)(R * C > 0 ? R * C : 1) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) xf[r * C + c] = orc_bf16_to_float(x[r * ldx + c]);
+    quantize_128x1_f32_ue8m0(xf, R, C, C, amax_floor, qT, ldqT, eT, ldeT);
+    free(xf);
+}
+
+/* As orc_quantize_128x128, with the UE8M0 rule; e[i*ceil(N/128) + j]. */
+void orc_quantize_128x128_ue8m0(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
+                                float amax_floor, uint8_t* q, int64_t ldq,
+                                uint8_t* qT, int64_t ldqT, uint8_t* e)
+{
+    int64_t kb = ceil_div(K, ORC_TILE), nb = ceil_div(N, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < kb * nb; ++t) {
+        int64_t i = t / nb, j = t % nb;
+        int64_t k0 = i * ORC_TILE, n0 = j * ORC_TILE;
+        int64_t kn = (K - k0 < ORC_TILE) ? K - k0 : ORC_TILE;
+        int64_t nn = (N - n0 < ORC_TILE) ? N - n0 : ORC_TILE;
+        float v[ORC_TILE * ORC_TILE];
+        uint8_t code[ORC_TILE * ORC_TILE];
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b)
+                v[a * nn + b] = orc_bf16_to_float(w[(k0 + a) * ldw + n0 + b]);
+        quantize_tile_ue8m0(v, kn * nn, amax_floor, &e[i * nb + j], code);
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b) {
+                if (q) q[(k0 + a) * ldq + n0 + b] = code[a * nn + b];
+                if (qT) qT[(n0 + b) * ldqT + k0 + a] = code[a * nn + b];
+            }
+    }
+}
+
+/* Re-tile a UE8M0 1x128 tensor (codes q [R][C], bytes e [ceil(C/128)][R]) to
+ * 128x1: v = fl32(dec(q) * 2^(e-127)) (exact: a 4-bit significand times a
+ * power of two), then the UE8M0 128x1 rule on v. */
+void orc_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
+                             const uint8_t* e, int64_t lde,
+                             uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT)
+{
+    float* v = (float*)malloc((size_t)(R * C > 0 ? R * C : 1) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            double d = orc_e4m3_decode(q[r * ldq + c]);
+            double sc = orc_e8m0_decode(e[(c / ORC_TILE) * lde + r]);
+            v[r * C + c] = (float)(d * sc);
+        }
+    quantize_128x1_f32_ue8m0(v, R, C, C, 0.0f, qT, ldqT, eT, ldeT);
+    free(v);
+}
+
+/* ------------------------------------------------------------------ */
 /* Block-scaled GEMM                                                   */
 /* ------------------------------------------------------------------ */
 
