@@ -17,6 +17,11 @@ scales = ``torch.float32``):
 * ``gemm_dgrad(qdy, sdy, qw, sw)`` -> ``dx[M, K]`` bf16 (dX = dY W^T)
 * ``gemm_wgrad(qxT, sxT, qdyT, sdyT, M)`` -> ``dw[K, N]`` fp32 (dW = X^T dY)
 * ``gemm_*_grouped(offsets, ...)`` -- the same per expert segment.
+* ``quantize_dual(x[R, C])`` -> both ``quantize_1x128`` and ``quantize_128x1`` outputs from one read.
+
+Every quantizer and GEMM takes ``ue8m0=True`` for the power-of-two-scale twin
+(``..._ue8m0`` entry points): scales are exact powers of two in fp32 and the
+GEMMs let the matrix core apply them.
 """
 from __future__ import annotations
 
@@ -46,6 +51,17 @@ SIGNATURES = {
     "fgb_gemm_fprop_grouped": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
     "fgb_gemm_dgrad_grouped": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
     "fgb_gemm_wgrad_grouped": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _N, _P],
+    "fgb_quantize_1x128_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
+    "fgb_quantize_128x1_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
+    "fgb_quantize_dual_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _P],
+    "fgb_quantize_128x128_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _P],
+    "fgb_requant_128x1_ue8m0": [_P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P],
+    "fgb_gemm_fprop_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
+    "fgb_gemm_dgrad_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
+    "fgb_gemm_wgrad_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _N, _P],
+    "fgb_gemm_fprop_grouped_ue8m0": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
+    "fgb_gemm_dgrad_grouped_ue8m0": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
+    "fgb_gemm_wgrad_grouped_ue8m0": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _N, _P],
     "fgb_status_string": [_N],
     "fgb_version": [],
 }
@@ -103,6 +119,11 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
+def _fn(name: str, ue8m0: bool):
+    """The entry point `name`, or its power-of-two-scale twin `name`_ue8m0."""
+    return getattr(lib(), name + "_ue8m0" if ue8m0 else name)
+
+
 def version() -> int:
     return lib().fgb_version()
 
@@ -111,31 +132,31 @@ def version() -> int:
 # Quantizers
 # ---------------------------------------------------------------------------
 
-def quantize_1x128(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None):
+def quantize_1x128(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, ue8m0: bool = False):
     R, C = x.shape
     ldx = _rows(x, torch.bfloat16, "x")
     if q is None:
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device)
-    _check(lib().fgb_quantize_1x128(_ptr(x), R, C, ldx, amax_floor, _ptr(q), _rows(q, torch.uint8, "q"),
+    _check(_fn("fgb_quantize_1x128", ue8m0)(_ptr(x), R, C, ldx, amax_floor, _ptr(q), _rows(q, torch.uint8, "q"),
                                     _ptr(s), _rows(s, torch.float32, "s"), _stream(x)), "quantize_1x128")
     return q, s
 
 
-def quantize_128x1(x: torch.Tensor, amax_floor: float = 0.0, qT=None, sT=None):
+def quantize_128x1(x: torch.Tensor, amax_floor: float = 0.0, qT=None, sT=None, ue8m0: bool = False):
     R, C = x.shape
     ldx = _rows(x, torch.bfloat16, "x")
     if qT is None:
         qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=x.device)
     if sT is None:
         sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=x.device)
-    _check(lib().fgb_quantize_128x1(_ptr(x), R, C, ldx, amax_floor, _ptr(qT), _rows(qT, torch.uint8, "qT"),
+    _check(_fn("fgb_quantize_128x1", ue8m0)(_ptr(x), R, C, ldx, amax_floor, _ptr(qT), _rows(qT, torch.uint8, "qT"),
                                     _ptr(sT), _rows(sT, torch.float32, "sT"), _stream(x)), "quantize_128x1")
     return qT, sT
 
 
-def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=None, sT=None):
+def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=None, sT=None, ue8m0: bool = False):
     """Both orientations from one read: (q, s) as quantize_1x128, (qT, sT) as quantize_128x1."""
     R, C = x.shape
     ldx = _rows(x, torch.bfloat16, "x")
@@ -147,7 +168,7 @@ def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=N
         qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=x.device)
     if sT is None:
         sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=x.device)
-    _check(lib().fgb_quantize_dual(_ptr(x), R, C, ldx, amax_floor,
+    _check(_fn("fgb_quantize_dual", ue8m0)(_ptr(x), R, C, ldx, amax_floor,
                                    _ptr(q), _rows(q, torch.uint8, "q"), _ptr(s), _rows(s, torch.float32, "s"),
                                    _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT), _rows(sT, torch.float32, "sT"),
                                    _stream(x)), "quantize_dual")
@@ -155,7 +176,7 @@ def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=N
 
 
 def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = True, want_qT: bool = True,
-                     q=None, qT=None, s=None):
+                     q=None, qT=None, s=None, ue8m0: bool = False):
     K, N = w.shape
     ldw = _rows(w, torch.bfloat16, "w")
     if want_q and q is None:
@@ -166,19 +187,19 @@ def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = Tr
         s = torch.empty((_cdiv(K, TILE), _cdiv(N, TILE)), dtype=torch.float32, device=w.device)
     ldq = _rows(q, torch.uint8, "q") if q is not None else 0
     ldqT = _rows(qT, torch.uint8, "qT") if qT is not None else 0
-    _check(lib().fgb_quantize_128x128(_ptr(w), K, N, ldw, amax_floor, _ptr(q), ldq, _ptr(qT), ldqT,
+    _check(_fn("fgb_quantize_128x128", ue8m0)(_ptr(w), K, N, ldw, amax_floor, _ptr(q), ldq, _ptr(qT), ldqT,
                                       _ptr(s), _stream(w)), "quantize_128x128")
     return q, qT, s
 
 
-def requant_128x1(q: torch.Tensor, s: torch.Tensor, qT=None, sT=None):
+def requant_128x1(q: torch.Tensor, s: torch.Tensor, qT=None, sT=None, ue8m0: bool = False):
     R, C = q.shape
     ldq = _rows(q, torch.uint8, "q")
     if qT is None:
         qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=q.device)
     if sT is None:
         sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=q.device)
-    _check(lib().fgb_requant_128x1(_ptr(q), R, C, ldq, _ptr(s), _rows(s, torch.float32, "s"),
+    _check(_fn("fgb_requant_128x1", ue8m0)(_ptr(q), R, C, ldq, _ptr(s), _rows(s, torch.float32, "s"),
                                    _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT),
                                    _rows(sT, torch.float32, "sT"), _stream(q)), "requant_128x1")
     return qT, sT
@@ -188,36 +209,36 @@ def requant_128x1(q: torch.Tensor, s: torch.Tensor, qT=None, sT=None):
 # GEMMs
 # ---------------------------------------------------------------------------
 
-def gemm_fprop(qx, sx, qwT, sw, y=None):
+def gemm_fprop(qx, sx, qwT, sw, y=None, ue8m0: bool = False):
     M, K = qx.shape
     N = qwT.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
-    _check(lib().fgb_gemm_fprop(M, N, K, _ptr(qx), _rows(qx, torch.uint8, "qx"), _ptr(sx),
+    _check(_fn("fgb_gemm_fprop", ue8m0)(M, N, K, _ptr(qx), _rows(qx, torch.uint8, "qx"), _ptr(sx),
                                 _rows(sx, torch.float32, "sx") if K else M, _ptr(qwT),
                                 _rows(qwT, torch.uint8, "qwT"), _ptr(sw), _ptr(y),
                                 _rows(y, torch.bfloat16, "y"), _stream(qx)), "gemm_fprop")
     return y
 
 
-def gemm_dgrad(qdy, sdy, qw, sw, dx=None):
+def gemm_dgrad(qdy, sdy, qw, sw, dx=None, ue8m0: bool = False):
     M, N = qdy.shape
     K = qw.shape[0]
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=qdy.device)
-    _check(lib().fgb_gemm_dgrad(M, K, N, _ptr(qdy), _rows(qdy, torch.uint8, "qdy"), _ptr(sdy),
+    _check(_fn("fgb_gemm_dgrad", ue8m0)(M, K, N, _ptr(qdy), _rows(qdy, torch.uint8, "qdy"), _ptr(sdy),
                                 _rows(sdy, torch.float32, "sdy") if N else M, _ptr(qw),
                                 _rows(qw, torch.uint8, "qw"), _ptr(sw), _ptr(dx),
                                 _rows(dx, torch.bfloat16, "dx"), _stream(qdy)), "gemm_dgrad")
     return dx
 
 
-def gemm_wgrad(qxT, sxT, qdyT, sdyT, M: int, dw=None, accumulate: bool = False):
+def gemm_wgrad(qxT, sxT, qdyT, sdyT, M: int, dw=None, accumulate: bool = False, ue8m0: bool = False):
     K = qxT.shape[0]
     N = qdyT.shape[0]
     if dw is None:
         dw = torch.empty((K, N), dtype=torch.float32, device=qxT.device)
-    _check(lib().fgb_gemm_wgrad(K, N, M, _ptr(qxT), _rows(qxT, torch.uint8, "qxT"), _ptr(sxT),
+    _check(_fn("fgb_gemm_wgrad", ue8m0)(K, N, M, _ptr(qxT), _rows(qxT, torch.uint8, "qxT"), _ptr(sxT),
                                 _rows(sxT, torch.float32, "sxT") if M else K, _ptr(qdyT),
                                 _rows(qdyT, torch.uint8, "qdyT"), _ptr(sdyT),
                                 _rows(sdyT, torch.float32, "sdyT") if M else N, _ptr(dw),
@@ -237,7 +258,7 @@ def _contiguous(t):
         raise ValueError("grouped GEMM operands must be contiguous tensors")
 
 
-def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, y=None):
+def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, y=None, ue8m0: bool = False):
     E = _offsets(offsets)
     R_pad, K = qx.shape
     N = qwT.shape[1]
@@ -245,12 +266,12 @@ def gemm_fprop_grouped(offsets, qx, sx, qwT, sw, y=None):
         y = torch.empty((R_pad, N), dtype=torch.bfloat16, device=qx.device)
     for t in (qx, sx, qwT, sw, y):
         _contiguous(t)
-    _check(lib().fgb_gemm_fprop_grouped(E, _ptr(offsets), R_pad, N, K, _ptr(qx), _ptr(sx), _ptr(qwT),
+    _check(_fn("fgb_gemm_fprop_grouped", ue8m0)(E, _ptr(offsets), R_pad, N, K, _ptr(qx), _ptr(sx), _ptr(qwT),
                                         _ptr(sw), _ptr(y), _stream(qx)), "gemm_fprop_grouped")
     return y
 
 
-def gemm_dgrad_grouped(offsets, qdy, sdy, qw, sw, dx=None):
+def gemm_dgrad_grouped(offsets, qdy, sdy, qw, sw, dx=None, ue8m0: bool = False):
     E = _offsets(offsets)
     R_pad, N = qdy.shape
     K = qw.shape[1]
@@ -258,12 +279,12 @@ def gemm_dgrad_grouped(offsets, qdy, sdy, qw, sw, dx=None):
         dx = torch.empty((R_pad, K), dtype=torch.bfloat16, device=qdy.device)
     for t in (qdy, sdy, qw, sw, dx):
         _contiguous(t)
-    _check(lib().fgb_gemm_dgrad_grouped(E, _ptr(offsets), R_pad, K, N, _ptr(qdy), _ptr(sdy), _ptr(qw),
+    _check(_fn("fgb_gemm_dgrad_grouped", ue8m0)(E, _ptr(offsets), R_pad, K, N, _ptr(qdy), _ptr(sdy), _ptr(qw),
                                         _ptr(sw), _ptr(dx), _stream(qdy)), "gemm_dgrad_grouped")
     return dx
 
 
-def gemm_wgrad_grouped(offsets, qxT, sxT, qdyT, sdyT, dw=None, accumulate: bool = False):
+def gemm_wgrad_grouped(offsets, qxT, sxT, qdyT, sdyT, dw=None, accumulate: bool = False, ue8m0: bool = False):
     E = _offsets(offsets)
     K, R_pad = qxT.shape
     N = qdyT.shape[0]
@@ -271,7 +292,7 @@ def gemm_wgrad_grouped(offsets, qxT, sxT, qdyT, sdyT, dw=None, accumulate: bool 
         dw = torch.empty((E, K, N), dtype=torch.float32, device=qxT.device)
     for t in (qxT, sxT, qdyT, sdyT, dw):
         _contiguous(t)
-    _check(lib().fgb_gemm_wgrad_grouped(E, _ptr(offsets), R_pad, K, N, _ptr(qxT), _ptr(sxT), _ptr(qdyT),
+    _check(_fn("fgb_gemm_wgrad_grouped", ue8m0)(E, _ptr(offsets), R_pad, K, N, _ptr(qxT), _ptr(sxT), _ptr(qdyT),
                                         _ptr(sdyT), _ptr(dw), 1 if accumulate else 0, _stream(qxT)),
            "gemm_wgrad_grouped")
     return dw

@@ -75,49 +75,54 @@ const char* fgb_status_string(int status)
     }
 }
 
-int fgb_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
-                       uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+// ------------------------------ quantizers --------------------------------
+// Each quantizer exists for scales absmax/448 and for power-of-two scales (po2,
+// the UE8M0 value set); both are fp32 arrays with the same layout and rules.
+static int check_sc(const float* p, int64_t ld, int64_t need, bool) { return check_scales(p, ld, need); }
+
+static int quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds, bool po2, void* stream)
 {
     if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
     if (R == 0 || C == 0) return FGB_OK;
     FGB_TRY(check_bf16(x, ldx, C));
     FGB_TRY(check_codes(q, ldq, C, 8));
-    FGB_TRY(check_scales(s, lds, R));
-    return hip_status(fgb::launch_quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, as_stream(stream)));
+    FGB_TRY(check_sc(s, lds, R, po2));
+    return hip_status(fgb::launch_quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, po2, as_stream(stream)));
 }
 
-int fgb_quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
-                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+static int quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream)
 {
     if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
     if (R == 0 || C == 0) return FGB_OK;
     FGB_TRY(check_bf16(x, ldx, C));
     FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
-    FGB_TRY(check_scales(sT, ldsT, C));
+    FGB_TRY(check_sc(sT, ldsT, C, po2));
     return hip_status(fgb::launch_tile128(fgb::kTile128x1, x, R, C, ldx, nullptr, 0, amax_floor,
-                                          nullptr, 0, qT, ldqT, sT, ldsT, as_stream(stream)));
+                                          nullptr, 0, qT, ldqT, sT, ldsT, po2, as_stream(stream)));
 }
 
-int fgb_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
-                      uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+static int quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream)
 {
     if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
     if (R == 0 || C == 0) return FGB_OK;
     FGB_TRY(check_bf16(x, ldx, C));
     FGB_TRY(check_codes(q, ldq, C, 8));
-    FGB_TRY(check_scales(s, lds, R));
+    FGB_TRY(check_sc(s, lds, R, po2));
     FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
-    FGB_TRY(check_scales(sT, ldsT, C));
+    FGB_TRY(check_sc(sT, ldsT, C, po2));
     return hip_status(fgb::launch_tile128(fgb::kTileDual, x, R, C, ldx, nullptr, 0, amax_floor,
-                                          q, ldq, qT, ldqT, sT, ldsT, as_stream(stream), s, lds));
+                                          q, ldq, qT, ldqT, sT, ldsT, po2, as_stream(stream), s, lds));
 }
 
-int fgb_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
-                         uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, void* stream)
+static int quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
+                            uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, bool po2, void* stream)
 {
     if (K < 0 || N < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
@@ -126,28 +131,90 @@ int fgb_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, f
     if (!q && !qT) return FGB_E_NULL;
     if (q) FGB_TRY(check_codes(q, ldq, N, 8));
     if (qT) FGB_TRY(check_codes(qT, ldqT, K, 16));
-    FGB_TRY(check_scales(s, N / T, N / T));
+    FGB_TRY(check_sc(s, N / T, N / T, po2));
     return hip_status(fgb::launch_tile128(fgb::kTile128x128, w, K, N, ldw, nullptr, 0, amax_floor,
-                                          q, ldq, qT, ldqT, s, N / T, as_stream(stream)));
+                                          q, ldq, qT, ldqT, s, N / T, po2, as_stream(stream)));
+}
+
+static int requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq, const float* s, int64_t lds,
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream)
+{
+    if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
+    if (R == 0 || C == 0) return FGB_OK;
+    FGB_TRY(check_codes(q, ldq, C, 8));
+    FGB_TRY(check_sc(s, lds, R, po2));
+    FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
+    FGB_TRY(check_sc(sT, ldsT, C, po2));
+    return hip_status(fgb::launch_tile128(fgb::kTileRequant, q, R, C, ldq, s, lds, 0.0f,
+                                          nullptr, 0, qT, ldqT, sT, ldsT, po2, as_stream(stream)));
+}
+
+int fgb_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+{
+    return quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, false, stream);
+}
+
+int fgb_quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+{
+    return quantize_128x1(x, R, C, ldx, amax_floor, qT, ldqT, sT, ldsT, false, stream);
+}
+
+int fgb_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                      uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+{
+    return quantize_dual(x, R, C, ldx, amax_floor, q, ldq, s, lds, qT, ldqT, sT, ldsT, false, stream);
+}
+
+int fgb_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
+                         uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, void* stream)
+{
+    return quantize_128x128(w, K, N, ldw, amax_floor, q, ldq, qT, ldqT, s, false, stream);
 }
 
 int fgb_requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq, const float* s, int64_t lds,
                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
 {
-    if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
-    if (R == 0 || C == 0) return FGB_OK;
-    FGB_TRY(check_codes(q, ldq, C, 8));
-    FGB_TRY(check_scales(s, lds, R));
-    FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
-    FGB_TRY(check_scales(sT, ldsT, C));
-    return hip_status(fgb::launch_tile128(fgb::kTileRequant, q, R, C, ldq, s, lds, 0.0f,
-                                          nullptr, 0, qT, ldqT, sT, ldsT, as_stream(stream)));
+    return requant_128x1(q, R, C, ldq, s, lds, qT, ldqT, sT, ldsT, false, stream);
 }
 
-int fgb_gemm_fprop(int64_t M, int64_t N, int64_t K,
+int fgb_quantize_1x128_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+{
+    return quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, true, stream);
+}
+
+int fgb_quantize_128x1_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+{
+    return quantize_128x1(x, R, C, ldx, amax_floor, qT, ldqT, sT, ldsT, true, stream);
+}
+
+int fgb_quantize_dual_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                            uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                            uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+{
+    return quantize_dual(x, R, C, ldx, amax_floor, q, ldq, s, lds, qT, ldqT, sT, ldsT, true, stream);
+}
+
+int fgb_quantize_128x128_ue8m0(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
+                               uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, void* stream)
+{
+    return quantize_128x128(w, K, N, ldw, amax_floor, q, ldq, qT, ldqT, s, true, stream);
+}
+
+int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq, const float* s, int64_t lds,
+                            uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
+{
+    return requant_128x1(q, R, C, ldq, s, lds, qT, ldqT, sT, ldsT, true, stream);
+}
+
+static int gemm_fprop_impl(int64_t M, int64_t N, int64_t K,
                    const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx,
                    const uint8_t* qwT, int64_t ldqwT, const float* sw,
-                   uint16_t* y, int64_t ldy, void* stream)
+                   uint16_t* y, int64_t ldy, void* stream, bool po2)
 {
     if (M < 0 || N < 0 || K < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (M == 0 || N == 0) return FGB_OK;
@@ -164,13 +231,13 @@ int fgb_gemm_fprop(int64_t M, int64_t N, int64_t K,
     a.B = qwT; a.ldb = ldqwT; a.sb = sw; a.sb_kb = N / T; a.sb_n = 1;
     a.out = y; a.ldo = ldy;
     if (!fgb::gemm_supported(a, false)) return FGB_E_UNSUPPORTED;
-    return hip_status(fgb::launch_gemm(fgb::kFprop, false, a, as_stream(stream)));
+    return hip_status(fgb::launch_gemm(fgb::kFprop, false, a, as_stream(stream), po2));
 }
 
-int fgb_gemm_dgrad(int64_t M, int64_t K, int64_t N,
+static int gemm_dgrad_impl(int64_t M, int64_t K, int64_t N,
                    const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy,
                    const uint8_t* qw, int64_t ldqw, const float* sw,
-                   uint16_t* dx, int64_t lddx, void* stream)
+                   uint16_t* dx, int64_t lddx, void* stream, bool po2)
 {
     if (M < 0 || N < 0 || K < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (M == 0 || K == 0) return FGB_OK;
@@ -188,13 +255,13 @@ int fgb_gemm_dgrad(int64_t M, int64_t K, int64_t N,
     a.B = qw; a.ldb = ldqw; a.sb = sw; a.sb_kb = 1; a.sb_n = N / T;
     a.out = dx; a.ldo = lddx;
     if (!fgb::gemm_supported(a, false)) return FGB_E_UNSUPPORTED;
-    return hip_status(fgb::launch_gemm(fgb::kDgrad, false, a, as_stream(stream)));
+    return hip_status(fgb::launch_gemm(fgb::kDgrad, false, a, as_stream(stream), po2));
 }
 
-int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M,
+static int gemm_wgrad_impl(int64_t K, int64_t N, int64_t M,
                    const uint8_t* qxT, int64_t ldqxT, const float* sxT, int64_t ldsxT,
                    const uint8_t* qdyT, int64_t ldqdyT, const float* sdyT, int64_t ldsdyT,
-                   float* dw, int64_t lddw, int accumulate, void* stream)
+                   float* dw, int64_t lddw, int accumulate, void* stream, bool po2)
 {
     if (M < 0 || N < 0 || K < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (K == 0 || N == 0) return FGB_OK;
@@ -213,12 +280,12 @@ int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M,
     a.B = qdyT; a.ldb = ldqdyT; a.sb = sdyT; a.sb_kb = ldsdyT;
     a.out = dw; a.ldo = lddw; a.accumulate = accumulate ? 1 : 0;
     if (!fgb::gemm_supported(a, false)) return FGB_E_UNSUPPORTED;
-    return hip_status(fgb::launch_gemm(fgb::kWgrad, false, a, as_stream(stream)));
+    return hip_status(fgb::launch_gemm(fgb::kWgrad, false, a, as_stream(stream), po2));
 }
 
-int fgb_gemm_fprop_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t N, int64_t K,
+static int gemm_fprop_grouped_impl(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t N, int64_t K,
                            const uint8_t* qx, const float* sx, const uint8_t* qwT, const float* sw,
-                           uint16_t* y, void* stream)
+                           uint16_t* y, void* stream, bool po2)
 {
     if (E < 0 || R_pad < 0 || N < 0 || K < 0) return FGB_E_SHAPE;
     if (R_pad % T != 0 || N % T != 0 || K % T != 0 || E > 65535) return FGB_E_SHAPE;
@@ -239,12 +306,12 @@ int fgb_gemm_fprop_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     a.offsets = offsets; a.E = E;
     a.b_expert_stride = N * K; a.sb_expert_stride = (K / T) * (N / T);
     if (!fgb::gemm_supported(a, true)) return FGB_E_UNSUPPORTED;
-    return hip_status(fgb::launch_gemm(fgb::kFprop, true, a, as_stream(stream)));
+    return hip_status(fgb::launch_gemm(fgb::kFprop, true, a, as_stream(stream), po2));
 }
 
-int fgb_gemm_dgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
+static int gemm_dgrad_grouped_impl(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
                            const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw,
-                           uint16_t* dx, void* stream)
+                           uint16_t* dx, void* stream, bool po2)
 {
     if (E < 0 || R_pad < 0 || N < 0 || K < 0) return FGB_E_SHAPE;
     if (R_pad % T != 0 || N % T != 0 || K % T != 0 || E > 65535) return FGB_E_SHAPE;
@@ -265,12 +332,12 @@ int fgb_gemm_dgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     a.offsets = offsets; a.E = E;
     a.b_expert_stride = K * N; a.sb_expert_stride = (K / T) * (N / T);
     if (!fgb::gemm_supported(a, true)) return FGB_E_UNSUPPORTED;
-    return hip_status(fgb::launch_gemm(fgb::kDgrad, true, a, as_stream(stream)));
+    return hip_status(fgb::launch_gemm(fgb::kDgrad, true, a, as_stream(stream), po2));
 }
 
-int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
+static int gemm_wgrad_grouped_impl(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
                            const uint8_t* qxT, const float* sxT, const uint8_t* qdyT, const float* sdyT,
-                           float* dw, int accumulate, void* stream)
+                           float* dw, int accumulate, void* stream, bool po2)
 {
     if (E < 0 || R_pad < 0 || N < 0 || K < 0) return FGB_E_SHAPE;
     if (R_pad % T != 0 || N % T != 0 || K % T != 0 || E > 65535) return FGB_E_SHAPE;
@@ -290,7 +357,54 @@ int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int
     a.out = dw; a.ldo = N; a.accumulate = accumulate ? 1 : 0;
     a.offsets = offsets; a.E = E; a.out_expert_stride = K * N;
     if (!fgb::gemm_supported(a, true)) return FGB_E_UNSUPPORTED;
-    return hip_status(fgb::launch_gemm(fgb::kWgrad, true, a, as_stream(stream)));
+    return hip_status(fgb::launch_gemm(fgb::kWgrad, true, a, as_stream(stream), po2));
 }
+
+// Public GEMMs: scales absmax/448 (any fp32), or powers of two (_ue8m0).
+int fgb_gemm_fprop(int64_t M, int64_t N, int64_t K, const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx,
+                   const uint8_t* qwT, int64_t ldqwT, const float* sw, uint16_t* y, int64_t ldy, void* stream)
+{ return gemm_fprop_impl(M, N, K, qx, ldqx, sx, ldsx, qwT, ldqwT, sw, y, ldy, stream, false); }
+int fgb_gemm_dgrad(int64_t M, int64_t K, int64_t N, const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy,
+                   const uint8_t* qw, int64_t ldqw, const float* sw, uint16_t* dx, int64_t lddx, void* stream)
+{ return gemm_dgrad_impl(M, K, N, qdy, ldqdy, sdy, ldsdy, qw, ldqw, sw, dx, lddx, stream, false); }
+int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M, const uint8_t* qxT, int64_t ldqxT, const float* sxT, int64_t ldsxT,
+                   const uint8_t* qdyT, int64_t ldqdyT, const float* sdyT, int64_t ldsdyT,
+                   float* dw, int64_t lddw, int accumulate, void* stream)
+{ return gemm_wgrad_impl(K, N, M, qxT, ldqxT, sxT, ldsxT, qdyT, ldqdyT, sdyT, ldsdyT, dw, lddw, accumulate, stream, false); }
+int fgb_gemm_fprop_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t N, int64_t K,
+                           const uint8_t* qx, const float* sx, const uint8_t* qwT, const float* sw,
+                           uint16_t* y, void* stream)
+{ return gemm_fprop_grouped_impl(E, offsets, R_pad, N, K, qx, sx, qwT, sw, y, stream, false); }
+int fgb_gemm_dgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
+                           const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw,
+                           uint16_t* dx, void* stream)
+{ return gemm_dgrad_grouped_impl(E, offsets, R_pad, K, N, qdy, sdy, qw, sw, dx, stream, false); }
+int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
+                           const uint8_t* qxT, const float* sxT, const uint8_t* qdyT, const float* sdyT,
+                           float* dw, int accumulate, void* stream)
+{ return gemm_wgrad_grouped_impl(E, offsets, R_pad, K, N, qxT, sxT, qdyT, sdyT, dw, accumulate, stream, false); }
+
+int fgb_gemm_fprop_ue8m0(int64_t M, int64_t N, int64_t K, const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx,
+                         const uint8_t* qwT, int64_t ldqwT, const float* sw, uint16_t* y, int64_t ldy, void* stream)
+{ return gemm_fprop_impl(M, N, K, qx, ldqx, sx, ldsx, qwT, ldqwT, sw, y, ldy, stream, true); }
+int fgb_gemm_dgrad_ue8m0(int64_t M, int64_t K, int64_t N, const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy,
+                         const uint8_t* qw, int64_t ldqw, const float* sw, uint16_t* dx, int64_t lddx, void* stream)
+{ return gemm_dgrad_impl(M, K, N, qdy, ldqdy, sdy, ldsdy, qw, ldqw, sw, dx, lddx, stream, true); }
+int fgb_gemm_wgrad_ue8m0(int64_t K, int64_t N, int64_t M, const uint8_t* qxT, int64_t ldqxT, const float* sxT, int64_t ldsxT,
+                         const uint8_t* qdyT, int64_t ldqdyT, const float* sdyT, int64_t ldsdyT,
+                         float* dw, int64_t lddw, int accumulate, void* stream)
+{ return gemm_wgrad_impl(K, N, M, qxT, ldqxT, sxT, ldsxT, qdyT, ldqdyT, sdyT, ldsdyT, dw, lddw, accumulate, stream, true); }
+int fgb_gemm_fprop_grouped_ue8m0(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t N, int64_t K,
+                                 const uint8_t* qx, const float* sx, const uint8_t* qwT, const float* sw,
+                                 uint16_t* y, void* stream)
+{ return gemm_fprop_grouped_impl(E, offsets, R_pad, N, K, qx, sx, qwT, sw, y, stream, true); }
+int fgb_gemm_dgrad_grouped_ue8m0(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
+                                 const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw,
+                                 uint16_t* dx, void* stream)
+{ return gemm_dgrad_grouped_impl(E, offsets, R_pad, K, N, qdy, sdy, qw, sw, dx, stream, true); }
+int fgb_gemm_wgrad_grouped_ue8m0(int64_t E, const int32_t* offsets, int64_t R_pad, int64_t K, int64_t N,
+                                 const uint8_t* qxT, const float* sxT, const uint8_t* qdyT, const float* sdyT,
+                                 float* dw, int accumulate, void* stream)
+{ return gemm_wgrad_grouped_impl(E, offsets, R_pad, K, N, qxT, sxT, qdyT, sdyT, dw, accumulate, stream, true); }
 
 }  // extern "C"

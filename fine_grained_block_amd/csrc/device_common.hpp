@@ -57,6 +57,35 @@ __device__ __forceinline__ void tile_scale(float a, float& s, float& inv) {
 }
 
 // ---------------------------------------------------------------------------
+// Power-of-two (UE8M0) tile scale from the absmax a (>= 0): e is the smallest
+// integer with 448 * 2^e >= a, clamped to [-127, 127] (zero and fp32-subnormal
+// absmaxes give -127, +inf gives 127); byte = e + 127 is its E8M0 encoding and
+// mul = 2^-e (exact).  NaN gives the E8M0 NaN byte 0xFF and mul = NaN.
+// With a = (1 + m/2^23) 2^(E-127) and 448 = 1.75 * 2^8: e = E - 135 when the
+// significand is at most 1.75 (m <= 0x600000), else E - 134.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tile_scale_ue8m0(float a, uint32_t& byte, float& mul) {
+    const uint32_t u = __float_as_uint(a);
+    const int E = (int)(u >> 23);
+    const uint32_t m = u & 0x7FFFFFu;
+    if (E == 255 && m != 0) {
+        byte = 0xFFu;
+        mul = __uint_as_float(0x7FC00000u);
+        return;
+    }
+    int e = (E == 0) ? -127 : (E == 255 ? 127 : (m <= 0x600000u ? E - 135 : E - 134));
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    byte = (uint32_t)(e + 127);
+    mul = e <= 126 ? __uint_as_float((uint32_t)(127 - e) << 23) : __uint_as_float(0x00400000u);
+}
+
+// E8M0 byte -> 2^(byte - 127) as fp32 (byte 0 is the subnormal 2^-127; 0xFF is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
+    return byte == 0xFFu ? __uint_as_float(0x7FC00000u)
+         : (byte == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(byte << 23));
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane unsigned max.  DPP within a row of 16 lanes, then swizzles.
 // ---------------------------------------------------------------------------
 template <int CTRL>

@@ -8,9 +8,10 @@
 namespace fgb {
 
 // ----------------------------- quantizers ---------------------------------
+// po2: power-of-two scales (the UE8M0 value set, in fp32); otherwise absmax/448.
 hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                                  float amax_floor, uint8_t* q, int64_t ldq,
-                                 float* s, int64_t lds, hipStream_t stream);
+                                 float* s, int64_t lds, bool po2, hipStream_t stream);
 
 enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 3 };
 
@@ -20,10 +21,11 @@ enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 
 //   kTileRequant: E4M3 + 1x128 scales in, then as kTile128x1
 //   kTileDual:    bf16 in, both the 1x128 codes and scales (q, s_row) and the
 //                 128x1 transposed codes and scales (qT, sT) from one read
+// po2 as above for every scale written (scales read by the requant are fp32 either way).
 hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
-                          float* s_out, int64_t lds_out, hipStream_t stream,
+                          float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
                           float* s_row = nullptr, int64_t lds_row = 0);
 
 // ------------------------------- GEMMs -------------------------------------
@@ -57,6 +59,7 @@ struct GemmArgs {
 // each stay within 4 GiB.
 bool gemm_supported(const GemmArgs& args, bool grouped);
 
-hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& args, hipStream_t stream);
+// po2: every scale is a power of two (the matrix core applies them; no rescale).
+hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& args, hipStream_t stream, bool po2 = false);
 
 }  // namespace fgb

@@ -186,7 +186,14 @@ template <int TN> struct TileShape {
 // expert segments and expert e writes its own output g.out + e*out_expert_stride.
 enum { kDense = 0, kGroupRows = 1, kGroupK = 2 };
 
-template <int TN, bool OUTER, bool BF16_OUT, int GROUP>
+//
+// PO2: every scale is a power of two (the UE8M0 value set, held in fp32).  The
+// matrix core then applies SA*SB itself (its E8M0 block-scale operands are the
+// fp32 exponent fields) and adds each block's partial sums to the accumulator
+// it is given as C: that addition is an fp32 round-to-nearest-even add, so
+// chaining the accumulator through C promotes every 128-block into fp32 with
+// no vector-ALU rescale at all.
+template <int TN, bool OUTER, bool BF16_OUT, int GROUP, bool PO2>
 __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
 {
     using S = TileShape<TN>;
@@ -388,6 +395,51 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         fold(T - 1, scales_of_step(T - 1));
     };
 
+    // Power-of-two scales: one MFMA per 16x16 piece and block, accumulating
+    // through C; the scale operand of a lane is the exponent field (the E8M0
+    // byte) of its fragment row's scale: B rows are output columns 16j + frow,
+    // A rows are output rows 16i + frow.
+    auto compute_po2 = [&](const uint8_t* sA) {
+        const uint8_t* sB = sA + kStageA;
+        const float* sSA = reinterpret_cast<const float*>(sB + kStageB);
+        const float* sSB = sSA + 4 * 64;
+        auto afrag = [&](int i) { return frag_swz(sA, wm * WTM + i * 16 + frow, fg); };
+        auto bfrag = [&](int j) { return frag_swz(sB, wn * WTN + j * 16 + frow, fg); };
+        auto held = [&](int h) { return ROW_MAJOR ? bfrag(h) : afrag(h); };
+        auto streamed = [&](int q) { return ROW_MAJOR ? afrag(q) : bfrag(q); };
+        v8i hf[NH];
+        v8i sf[3];
+        sf[0] = streamed(0);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) hf[h] = held(h);
+        if (NS > 1) sf[1] = streamed(1);
+        int ea[MI], eb[NJ];
+#pragma unroll
+        for (int h = 0; h < MI / 4; ++h) {
+            const float4 t = *reinterpret_cast<const float4*>(sSA + wm * WTM + 64 * h + frow * 4);
+            ea[4 * h] = (int)(__float_as_uint(t.x) >> 23); ea[4 * h + 1] = (int)(__float_as_uint(t.y) >> 23);
+            ea[4 * h + 2] = (int)(__float_as_uint(t.z) >> 23); ea[4 * h + 3] = (int)(__float_as_uint(t.w) >> 23);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if constexpr (OUTER)
+                eb[j] = (int)(__float_as_uint(sSB[wn * WTN + j * 16 + frow]) >> 23);
+            else
+                eb[j] = (int)(__float_as_uint(sSB[(int)((n0 + wn * WTN + j * 16) / kTile) - tile0]) >> 23);
+        }
+        constexpr int T = MI * NJ;
+        constexpr int PER = ROW_MAJOR ? NJ : MI;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int q = t / PER, h = t % PER;
+            if (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
+            const int i = ROW_MAJOR ? q : h, j = ROW_MAJOR ? h : q;
+            acc[i][j] = ROW_MAJOR
+                ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], acc[i][j], 0, 0, 0, eb[j], 0, ea[i])
+                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], acc[i][j], 0, 0, 0, eb[j], 0, ea[i]);
+        }
+    };
+
     // K loop, one barrier per block: wait for this wave's loads of block kb, then
     // the barrier (all waves' loads of kb have landed, and all waves are done
     // with block kb-1, so its stage can be refilled), then start the loads of
@@ -398,7 +450,8 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of block kb
         lds_barrier();
         if (kb + 1 < kb1) issue(kb + 1, smem + (st ^ 1) * kStageBytes);
-        compute(smem + st * kStageBytes);
+        if constexpr (PO2) compute_po2(smem + st * kStageBytes);
+        else compute(smem + st * kStageBytes);
     }
 
     // epilogue: row m0 + wm*WTM + 16*i + frow, columns n0 + wn*WTN + 16*j + 4*fg .. +3
@@ -452,7 +505,7 @@ static int pick_tn(int64_t M, int64_t N)
     return 256;
 }
 
-template <int TN>
+template <int TN, bool PO2>
 static void launch_v1(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
 {
     const int64_t tiles_m = (a.M + kTM - 1) / kTM, tiles_n = (a.N + TN - 1) / TN;
@@ -460,16 +513,16 @@ static void launch_v1(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_
     if (!grouped) {
         const dim3 grid((unsigned)(tiles_m * tiles_n));
         if (kind == kWgrad)
-            hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kDense>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kDense, PO2>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense, PO2>), grid, block, 0, stream, a);
     } else if (kind == kWgrad) {
         const dim3 grid((unsigned)(tiles_m * tiles_n * a.E));
-        hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kGroupK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kGroupK, PO2>), grid, block, 0, stream, a);
     } else {
         // upper bound on the row tiles: sum over experts of ceil(len/256) <= ceil(M/256) + E
         const dim3 grid((unsigned)((tiles_m + a.E) * tiles_n));
-        hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kGroupRows>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kGroupRows, PO2>), grid, block, 0, stream, a);
     }
 }
 
@@ -501,20 +554,24 @@ bool gemm_supported(const GemmArgs& a, bool grouped)
     return dense_row_step(a) > 0 && dense_col_step(a) > 0;
 }
 
-static hipError_t launch_one(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
+static hipError_t launch_one(GemmKind kind, bool grouped, bool po2, const GemmArgs& a, hipStream_t stream)
 {
     const int64_t units = grouped && kind == kWgrad ? a.M * a.E : a.M;
-    if (pick_tn(units, a.N) == 224)
-        launch_v1<224>(kind, grouped, a, stream);
-    else
-        launch_v1<256>(kind, grouped, a, stream);
+    const bool w224 = pick_tn(units, a.N) == 224;
+    if (po2) {
+        if (w224) launch_v1<224, true>(kind, grouped, a, stream);
+        else launch_v1<256, true>(kind, grouped, a, stream);
+    } else {
+        if (w224) launch_v1<224, false>(kind, grouped, a, stream);
+        else launch_v1<256, false>(kind, grouped, a, stream);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream)
+hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_t stream, bool po2)
 {
     if (!gemm_supported(a, grouped)) return hipErrorInvalidValue;
-    if (grouped) return launch_one(kind, true, a, stream);
+    if (grouped) return launch_one(kind, true, po2, a, stream);
     // Dense operands beyond 4 GiB: cut the output into row and column ranges
     // whose operand slices fit the kernel's 32-bit offsets.
     const int64_t rstep = dense_row_step(a), cstep = dense_col_step(a);
@@ -529,7 +586,7 @@ hipError_t launch_gemm(GemmKind kind, bool grouped, const GemmArgs& a, hipStream
             p.B = a.B + c0 * a.ldb;
             p.sb = kind == kWgrad ? a.sb + c0 : a.sb + (c0 / kTile) * a.sb_n;
             p.out = reinterpret_cast<uint8_t*>(a.out) + (r0 * a.ldo + c0) * osz;
-            const hipError_t e = launch_one(kind, false, p, stream);
+            const hipError_t e = launch_one(kind, false, po2, p, stream);
             if (e != hipSuccess) return e;
         }
     return hipSuccess;

@@ -24,6 +24,8 @@ namespace fgb {
 // ---------------------------------------------------------------------------
 constexpr int kQ1Rows = 64;
 
+// PO2: power-of-two scales (the UE8M0 values, held in fp32); otherwise absmax/448.
+template <bool PO2>
 __global__ __launch_bounds__(256) void k_quantize_1x128(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds)
@@ -53,25 +55,31 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
         m = max16(m);
         const float a = fmaxf(__uint_as_float(m << 16), amax_floor);
         float sc, inv;
-        tile_scale(a, sc, inv);
+        uint32_t eb = 0;
+        if constexpr (PO2) tile_scale_ue8m0(a, eb, inv);
+        else tile_scale(a, sc, inv);
         const uint32_t o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv,
                                    bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
         const uint32_t o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv,
                                    bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
         if (cok && r < R) {
             st8(q + r * ldq + c, make_uint2(o0, o1));
-            if (lane16 == 0) s[j * lds + r] = sc;
+            if (lane16 == 0) s[j * lds + r] = PO2 ? e8m0_to_f32(eb) : sc;
         }
     }
 }
 
 hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                                  float amax_floor, uint8_t* q, int64_t ldq,
-                                 float* s, int64_t lds, hipStream_t stream)
+                                 float* s, int64_t lds, bool po2, hipStream_t stream)
 {
     dim3 grid((unsigned)((R + kQ1Rows - 1) / kQ1Rows), (unsigned)((C + kTile - 1) / kTile));
-    hipLaunchKernelGGL(k_quantize_1x128, grid, dim3(256), 0, stream,
-                       x, R, C, ldx, amax_floor, q, ldq, s, lds);
+    if (po2)
+        hipLaunchKernelGGL(k_quantize_1x128<true>, grid, dim3(256), 0, stream,
+                           x, R, C, ldx, amax_floor, q, ldq, s, lds);
+    else
+        hipLaunchKernelGGL(k_quantize_1x128<false>, grid, dim3(256), 0, stream,
+                           x, R, C, ldx, amax_floor, q, ldq, s, lds);
     return hipGetLastError();
 }
 
@@ -88,13 +96,22 @@ constexpr int kTrStride = 136;   // bytes per staged qT row (128 + 8 to spread b
 
 __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
 
-template <int MODE>
+// PO2: the scales written are powers of two (the UE8M0 values, held in fp32).
+template <int MODE, bool PO2>
 __global__ __launch_bounds__(256) void k_tile128(
     const void* __restrict__ in, int64_t R, int64_t C, int64_t ldin,
     const float* __restrict__ s_in, int64_t lds_in, float amax_floor,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
     float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row)
 {
+    // scale of absmax a: fp32 (s = a/448, mul = 448/a) or power of two (E8M0 byte, mul = 2^-e)
+    auto scale_of = [&](float a, float& sc, uint32_t& eb, float& mul) {
+        if constexpr (PO2) tile_scale_ue8m0(a, eb, mul);
+        else tile_scale(a, sc, mul);
+    };
+    auto put_scale = [&](float* base, int64_t idx, float sc, uint32_t eb) {
+        base[idx] = PO2 ? e8m0_to_f32(eb) : sc;
+    };
     __shared__ uint32_t red[4][kTile];
     __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kTrStride];
 
@@ -140,11 +157,12 @@ __global__ __launch_bounds__(256) void k_tile128(
         __syncthreads();
         m = max(max(red[0][0], red[1][0]), max(red[2][0], red[3][0]));
         const float a = fmaxf(__uint_as_float(m), amax_floor);
-        float sc, iv;
-        tile_scale(a, sc, iv);
+        float sc = 0.0f, iv;
+        uint32_t eb = 0;
+        scale_of(a, sc, eb, iv);
 #pragma unroll
         for (int k = 0; k < 8; ++k) inv[k] = iv;
-        if (t == 0) s_out[(int64_t)blockIdx.x * lds_out + blockIdx.y] = sc;
+        if (t == 0) put_scale(s_out, (int64_t)blockIdx.x * lds_out + blockIdx.y, sc, eb);
     } else {
         uint32_t mc[8];
 #pragma unroll
@@ -162,16 +180,19 @@ __global__ __launch_bounds__(256) void k_tile128(
         }
         __syncthreads();
         float sc[8];
+        uint32_t eb[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int col = cg * 8 + k;
             const uint32_t m = max(max(red[0][col], red[1][col]), max(red[2][col], red[3][col]));
             const float a = fmaxf(__uint_as_float(m), amax_floor);
-            tile_scale(a, sc[k], inv[k]);
+            sc[k] = 0.0f;
+            eb[k] = 0;
+            scale_of(a, sc[k], eb[k], inv[k]);
         }
         if (rg == 0 && cok) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) s_out[(int64_t)blockIdx.x * lds_out + cc + k] = sc[k];
+            for (int k = 0; k < 8; ++k) put_scale(s_out, (int64_t)blockIdx.x * lds_out + cc + k, sc[k], eb[k]);
         }
     }
 
@@ -179,6 +200,7 @@ __global__ __launch_bounds__(256) void k_tile128(
     // held by the 16 lanes that share rg; their absmax is one DPP reduction.
     if constexpr (MODE == kTileDual) {
         float sr_own = 0.0f;
+        uint32_t er_own = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t m = 0;
@@ -186,9 +208,10 @@ __global__ __launch_bounds__(256) void k_tile128(
             for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
             m = max16(m);
             const float a = fmaxf(__uint_as_float(m), amax_floor);
-            float sc, iv;
-            tile_scale(a, sc, iv);
-            if (cg == i) sr_own = sc;
+            float sc = 0.0f, iv;
+            uint32_t eb = 0;
+            scale_of(a, sc, eb, iv);
+            if (cg == i) { sr_own = sc; er_own = eb; }
             const int64_t r = r0 + rg * 8 + i;
             const uint32_t o0 = e4m3x4(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
             const uint32_t o1 = e4m3x4(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
@@ -196,7 +219,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         }
         // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
         const int64_t rr = r0 + rg * 8 + cg;
-        if (cg < 8 && rr < R) s_row[(int64_t)blockIdx.y * lds_row + rr] = sr_own;
+        if (cg < 8 && rr < R) put_scale(s_row, (int64_t)blockIdx.y * lds_row + rr, sr_own, er_own);
     }
 
     // Row-major codes (128x128 weights, q != nullptr): 8 bytes per patch row.
@@ -233,31 +256,45 @@ __global__ __launch_bounds__(256) void k_tile128(
     }
 }
 
-hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
-                          const float* s_in, int64_t lds_in, float amax_floor,
-                          uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
-                          float* s_out, int64_t lds_out, hipStream_t stream,
-                          float* s_row, int64_t lds_row)
+template <bool PO2>
+static void launch_tile128_t(TileMode mode, dim3 grid, const void* in, int64_t R, int64_t C, int64_t ldin,
+                             const float* s_in, int64_t lds_in, float amax_floor,
+                             uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                             float* s_out, int64_t lds_out, hipStream_t stream, float* s_row, int64_t lds_row)
 {
-    dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
     switch (mode) {
     case kTile128x1:
-        hipLaunchKernelGGL(k_tile128<kTile128x1>, grid, dim3(256), 0, stream, in, R, C, ldin,
+        hipLaunchKernelGGL((k_tile128<kTile128x1, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
                            s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     case kTile128x128:
-        hipLaunchKernelGGL(k_tile128<kTile128x128>, grid, dim3(256), 0, stream, in, R, C, ldin,
+        hipLaunchKernelGGL((k_tile128<kTile128x128, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
                            s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     case kTileRequant:
-        hipLaunchKernelGGL(k_tile128<kTileRequant>, grid, dim3(256), 0, stream, in, R, C, ldin,
+        hipLaunchKernelGGL((k_tile128<kTileRequant, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
                            s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     case kTileDual:
-        hipLaunchKernelGGL(k_tile128<kTileDual>, grid, dim3(256), 0, stream, in, R, C, ldin,
+        hipLaunchKernelGGL((k_tile128<kTileDual, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
                            s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
         break;
     }
+}
+
+hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
+                          const float* s_in, int64_t lds_in, float amax_floor,
+                          uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                          float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
+                          float* s_row, int64_t lds_row)
+{
+    dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
+    if (po2)
+        launch_tile128_t<true>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
+                               s_out, lds_out, stream, s_row, lds_row);
+    else
+        launch_tile128_t<false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
+                                s_out, lds_out, stream, s_row, lds_row);
     return hipGetLastError();
 }
 

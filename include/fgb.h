@@ -20,6 +20,9 @@
  *   [grouped]  prime-rl PR #4073, "Validation completed" (grouped/empty
  *              experts) and TransformerEngine PR #3573 "Changes" (per-group
  *              GEMM paths).
+ *   [po2]      prime-rl PR #4073, conventions table rows "Two-stage
+ *              weights", "Activation floors" and "Compact formats" (UE8M0
+ *              power-of-two scales, held in FP32 containers on Hopper).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers on the current HIP device; the
@@ -42,9 +45,12 @@
  *   - Scale arrays are FP32, one per tile ([conv] "FP32 scale containers"),
  *     laid out block-major: the scales of consecutive rows (or columns) of
  *     one 128-block are contiguous.
- *   - Alignment: every pointer to bf16 or E4M3 data is 16-byte aligned and
- *     every such leading dimension is a multiple of 16 bytes (8 bf16 or 16
- *     codes); scale pointers are 4-byte aligned.
+ *   - Alignment: bf16 arrays are 16-byte aligned with leading dimensions a
+ *     multiple of 8 elements; row-major 1x128 / 128x128 code arrays written
+ *     by the quantizers are 8-byte aligned with ld % 8 == 0; transposed code
+ *     arrays and every GEMM operand are 16-byte aligned with ld % 16 == 0;
+ *     fp32 dW is 16-byte aligned with ld % 4 == 0; scale pointers are 4-byte
+ *     aligned.
  *   - Errors: argument errors return a negative fgb_status synchronously and
  *     launch nothing; a launch failure returns FGB_E_HIP.  Faults during
  *     execution surface at the caller's next synchronization (HIP semantics).
@@ -140,6 +146,38 @@ int fgb_requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * Power-of-two scales ([po2]).  Each quantizer above has a _ue8m0 twin with
+ * the same arguments and layouts whose scales are powers of two:
+ *     e = the smallest integer with 448 * 2^e >= a, clamped to [-127, 127]
+ *         (an all-zero tile gets -127); s = 2^e (an fp32 holding the UE8M0
+ *         value: its exponent field is the E8M0 byte e + 127)
+ *     q = e4m3(x * 2^-e)           (exact scaling; |x * 2^-e| <= 448)
+ * The requant twin dequantizes with the given power-of-two scales and
+ * re-tiles with this rule.
+ * ---------------------------------------------------------------------- */
+int fgb_quantize_1x128_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                             float amax_floor,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             void* stream);
+int fgb_quantize_128x1_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                             float amax_floor,
+                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                             void* stream);
+int fgb_quantize_dual_ue8m0(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                            float amax_floor,
+                            uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                            uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                            void* stream);
+int fgb_quantize_128x128_ue8m0(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
+                               float amax_floor,
+                               uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                               float* s, void* stream);
+int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
+                            const float* s, int64_t lds,
+                            uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * Block-scaled GEMMs ([drift] section 3 rows (a)/(b) and section 5: the
  * partial sum of every 128-long contraction segment is multiplied by
  * s_a * s_b and promoted into an FP32 accumulator; [scratch]: all three
@@ -221,6 +259,44 @@ int fgb_gemm_wgrad_grouped(int64_t E, const int32_t* offsets, int64_t R_pad,
                            const uint8_t* qxT, const float* sxT,
                            const uint8_t* qdyT, const float* sdyT,
                            float* dw, int accumulate, void* stream);
+
+/* ------------------------------------------------------------------------
+ * GEMMs on power-of-two scales ([po2]; [drift] section 5).  Same arguments,
+ * layouts and results as the GEMMs above, for operands quantized by the
+ * _ue8m0 quantizers: EVERY scale must be an exact power of two (2^-127 ..
+ * 2^127).  The matrix core applies the scales (its E8M0 block-scale operands
+ * are the fp32 exponent fields) and adds each 128-block's partial sums into
+ * the FP32 accumulator with round-to-nearest-even adds, so the per-block
+ * promotion happens inside the matrix core.  A scale that is not a power of
+ * two gives a wrong result (only its exponent field is used).
+ * ---------------------------------------------------------------------- */
+int fgb_gemm_fprop_ue8m0(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* qx, int64_t ldqx, const float* sx, int64_t ldsx,
+                         const uint8_t* qwT, int64_t ldqwT, const float* sw,
+                         uint16_t* y, int64_t ldy, void* stream);
+int fgb_gemm_dgrad_ue8m0(int64_t M, int64_t K, int64_t N,
+                         const uint8_t* qdy, int64_t ldqdy, const float* sdy, int64_t ldsdy,
+                         const uint8_t* qw, int64_t ldqw, const float* sw,
+                         uint16_t* dx, int64_t lddx, void* stream);
+int fgb_gemm_wgrad_ue8m0(int64_t K, int64_t N, int64_t M,
+                         const uint8_t* qxT, int64_t ldqxT, const float* sxT, int64_t ldsxT,
+                         const uint8_t* qdyT, int64_t ldqdyT, const float* sdyT, int64_t ldsdyT,
+                         float* dw, int64_t lddw, int accumulate, void* stream);
+int fgb_gemm_fprop_grouped_ue8m0(int64_t E, const int32_t* offsets, int64_t R_pad,
+                                 int64_t N, int64_t K,
+                                 const uint8_t* qx, const float* sx,
+                                 const uint8_t* qwT, const float* sw,
+                                 uint16_t* y, void* stream);
+int fgb_gemm_dgrad_grouped_ue8m0(int64_t E, const int32_t* offsets, int64_t R_pad,
+                                 int64_t K, int64_t N,
+                                 const uint8_t* qdy, const float* sdy,
+                                 const uint8_t* qw, const float* sw,
+                                 uint16_t* dx, void* stream);
+int fgb_gemm_wgrad_grouped_ue8m0(int64_t E, const int32_t* offsets, int64_t R_pad,
+                                 int64_t K, int64_t N,
+                                 const uint8_t* qxT, const float* sxT,
+                                 const uint8_t* qdyT, const float* sdyT,
+                                 float* dw, int accumulate, void* stream);
 
 #ifdef __cplusplus
 }
