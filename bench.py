@@ -15,6 +15,9 @@ against MI355X's dense FP8 MFMA peak, and `kernels` lists every kernel's rate
 against its own roofline (HBM for the quantizers).  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same step.
 
+`--recipe ue8m0` runs the same step with power-of-two (UE8M0) scales, which the
+matrix core applies itself (no vector-ALU rescale).
+
 `--workload moe_grouped` times the grouped expert GEMMs of one GPU's MoE share
 instead (32 experts, 8192 tokens routed top-8, gate/up and down projections,
 forward and backward); `value` then counts the routed rows' GEMM FLOP.
@@ -79,6 +82,8 @@ def parse():
     p.add_argument("--workload", choices=["linear_dsv3_attn", "moe_grouped"], default="linear_dsv3_attn",
                    help="linear_dsv3_attn (default): the DeepSeek-V3 attention projection's linear; "
                         "moe_grouped: the grouped expert GEMMs of one GPU's MoE share (no CPU baseline)")
+    p.add_argument("--recipe", choices=["fp32", "ue8m0"], default="fp32",
+                   help="fp32: scales absmax/448 (default); ue8m0: power-of-two scales, applied by the matrix core")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--separate-dy-casts", action="store_true",
                    help="quantize dY with two kernels (1x128, then 128x1) instead of the fused one")
@@ -104,7 +109,7 @@ def algorithmic_bytes(M, K, N):
     }
 
 
-def linear_step(fgb, torch, dev, d, separate_dy=False):
+def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False):
     """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work)
     per kernel, work = {"flop": ...} or {"bytes": ...} (algorithmic)."""
     import numpy as np
@@ -131,27 +136,33 @@ def linear_step(fgb, torch, dev, d, separate_dy=False):
     flop = {"flop": 2.0 * M * N * K}
     if separate_dy:
         dy_casts = [
-            ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"]),
+            ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"], ue8m0=ue8m0),
              {"bytes": ab["quantize_1x128_dy"]}),
-            ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"]),
+            ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"], ue8m0=ue8m0),
              {"bytes": ab["quantize_128x1_dy"]}),
         ]
     else:
         dy_casts = [
-            ("quantize_dual_dy", lambda: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
+            ("quantize_dual_dy", lambda: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"],
+                                                          ue8m0=ue8m0),
              {"bytes": ab["quantize_dual_dy"]}),
         ]
-    return [
-        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]), {"bytes": ab["quantize_1x128_x"]}),
-        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"]),
+    steps = [
+        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"], ue8m0=ue8m0),
+         {"bytes": ab["quantize_1x128_x"]}),
+        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"], ue8m0=ue8m0),
          {"bytes": ab["quantize_128x128_w"]}),
-        ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"]), flop),
+        ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"], ue8m0=ue8m0), flop),
     ] + dy_casts + [
-        ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"]), flop),
-        ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
+        ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"], ue8m0=ue8m0), flop),
+        ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"], ue8m0=ue8m0),
          {"bytes": ab["requant_128x1_x"]}),
-        ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"]), flop),
+        ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"], ue8m0=ue8m0),
+         flop),
     ]
+    if ue8m0:
+        steps = [(name + "_ue8m0", fn, work) for name, fn, work in steps]
+    return steps
 
 
 def moe_step(fgb, torch, dev, d):
@@ -227,9 +238,11 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "linear_dsv3_attn":
         d = wl.linear_dsv3_attn()
-        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts)
-        config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]",
-                  "M": d["M"], "K": d["K"], "N": d["N"]}
+        ue8m0 = args.recipe == "ue8m0"
+        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts, ue8m0=ue8m0)
+        config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]"
+                              + (", power-of-two (UE8M0) scales" if ue8m0 else ""),
+                  "M": d["M"], "K": d["K"], "N": d["N"], "scales": args.recipe}
         data = "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)"
     else:
         d = wl.moe_grouped()
@@ -320,11 +333,11 @@ def main():
         del a, c
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl.linear_dsv3_attn(), args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(wl.linear_dsv3_attn(), args.cpu_rows, args.recipe == "ue8m0")
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(d, rows_arg):
+def cpu_baseline(d, rows_arg, ue8m0=False):
     """The CPU oracle, as it stands, on a bounded sample of the same step: the
     three quantizers of X/dY and W on full tensors, then Fprop, Dgrad and Wgrad
     on a sample of output rows (all columns, full contraction).  Reported as the
@@ -334,11 +347,20 @@ def cpu_baseline(d, rows_arg):
     import oracle
     M, K, N = d["M"], d["K"], d["N"]
     t0 = time.perf_counter()
-    qx, sx = oracle.quantize_1x128(d["x"])
-    q, qT, sw = oracle.quantize_128x128(d["w"])
-    qdy, sdy = oracle.quantize_1x128(d["dy"])
-    qdyT, sdyT = oracle.quantize_128x1(d["dy"])
-    qxT, sxT = oracle.requant_128x1(qx, sx)
+    if ue8m0:
+        dec = lambda e: oracle.e8m0_decode(e).astype(np.float32)
+        qx, ex = oracle.quantize_1x128_ue8m0(d["x"])
+        q, qT, ew = oracle.quantize_128x128_ue8m0(d["w"])
+        qdy, edy = oracle.quantize_1x128_ue8m0(d["dy"])
+        qdyT, edyT = oracle.quantize_128x1_ue8m0(d["dy"])
+        qxT, exT = oracle.requant_128x1_ue8m0(qx, ex)
+        sx, sw, sdy, sdyT, sxT = dec(ex), dec(ew), dec(edy), dec(edyT), dec(exT)
+    else:
+        qx, sx = oracle.quantize_1x128(d["x"])
+        q, qT, sw = oracle.quantize_128x128(d["w"])
+        qdy, sdy = oracle.quantize_1x128(d["dy"])
+        qdyT, sdyT = oracle.quantize_128x1(d["dy"])
+        qxT, sxT = oracle.requant_128x1(qx, sx)
     tq = time.perf_counter() - t0
     qbytes = sum(algorithmic_bytes(M, K, N).values())
     # size the GEMM sample so the oracle works ~15 s: time a 1/128 slice of each
