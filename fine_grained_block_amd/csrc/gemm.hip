@@ -53,11 +53,16 @@ __device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
 }
 
 // Staged row r keeps its eight 16-byte chunks at slots c ^ swz(r), swz(r) =
-// (r >> 1) & 7.  A 16-byte LDS read serves 16 lanes per cycle across the 64
-// banks (256 B); the 16 rows of a fragment fall in the two 128-byte halves of
-// that window by parity and in eight distinct slots by (r >> 1) & 7, so the
-// fragment reads are free of bank conflicts.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// (r & 7) ^ ((r >> 3) & 1).  A fragment read has the 16 lanes of a lane group
+// read one 16-byte chunk from each of 16 consecutive rows (128 bytes apart).
+// The LDS counters (SQ_LDS_BANK_CONFLICT) show that such a read is free of bank
+// conflicts only when every 8 consecutive lanes hit 8 distinct 16-byte slots of
+// a 128-byte window AND all 16 lanes hit distinct slots of a 256-byte window:
+// r & 7 separates rows 0..7 (and 8..15), the ^ ((r >> 3) & 1) separates row r
+// from row r + 8, which shares its parity.  The swizzle depends on r mod 16
+// only, and fragments start at multiples of 16 rows, so one per-lane value
+// serves every fragment.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ v8i frag_swz(const uint8_t* stage_rows, int row, int g) {
     // 32 bytes = chunks 2g and 2g+1 of staged row `row`
@@ -193,7 +198,10 @@ enum { kDense = 0, kGroupRows = 1, kGroupK = 2 };
 // it is given as C: that addition is an fp32 round-to-nearest-even add, so
 // chaining the accumulator through C promotes every 128-block into fp32 with
 // no vector-ALU rescale at all.
-template <int TN, bool OUTER, bool BF16_OUT, int GROUP, bool PO2>
+//
+// SPLIT (dense only): blocks from g.split_from on compute one column half of a
+// tile each (the tiles that do not fill a whole round of CUs).
+template <int TN, bool OUTER, bool BF16_OUT, int GROUP, bool PO2, bool SPLIT = false>
 __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
 {
     using S = TileShape<TN>;
@@ -209,9 +217,23 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     const uint8_t* Bp = g.B;
     const float* sbp = g.sb;
     void* outp = g.out;
+    int half = -1;                                  // >= 0: this block computes column half `half`
     if constexpr (GROUP == kDense) {
         const int tiles_m = (int)((g.M + kTM - 1) / kTM);
-        group_order(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+        const int bid = (int)blockIdx.x;
+        if (!SPLIT) {
+            group_order(xcd_order(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
+        } else if (bid < g.split_from) {
+            group_order(xcd_order(bid, (int)g.split_from), tiles_m, tiles_n, tm, tn);
+        } else {
+            // the tail tiles split_from .. total-1, two blocks each; blocks h and
+            // h + 8 (same XCD) take the two halves of one tile, and an XCD's
+            // tail tiles are 8 apart in the grouped order (same row tile)
+            const int h = bid - (int)g.split_from;
+            const int t = (int)g.split_from + (h >> 4) * 8 + (h & 7);
+            half = (h >> 3) & 1;
+            group_order(t, tiles_m, tiles_n, tm, tn);
+        }
         m0 = (int64_t)tm * kTM;
     } else if constexpr (GROUP == kGroupRows) {
         int total = g.offsets[g.E];
@@ -239,7 +261,11 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         kb0 = b0; kb1 = b1;
         outp = reinterpret_cast<uint8_t*>(g.out) + e * g.out_expert_stride * (int64_t)sizeof(float);
     }
-    const int64_t n0 = (int64_t)tn * TN;
+    // A half block covers TN/2 columns from n0 with the waves of the first half
+    // of the wave columns; the other waves only share the loads and barriers.
+    const int64_t n0 = (int64_t)tn * TN + (half > 0 ? TN / 2 : 0);
+    const int b_rows = SPLIT && half >= 0 ? TN / 2 : TN;     // staged B rows this block needs
+    const bool active = !SPLIT || half < 0 || wn < S::WAVES_N / 2;
 
     // ---- load plan: A rows in 32 groups of 8, B rows in TN/8 groups; group q is
     // loaded by wave q % 8 with one direct-to-LDS instruction.  Lane -> staged
@@ -295,7 +321,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         for (int i = 0; i < 4; ++i) dma16(A + a_off[i], sbase + (wave + 8 * i) * 8 * kTile);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if ((wave + 8 * i) * 8 < TN) dma16(B + b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
+            if ((wave + 8 * i) * 8 < b_rows) dma16(B + b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
         dma4(s_base + kb * s_kb + s_off, sbase + kStageA + kStageB + wave * 256);
     };
 
@@ -450,9 +476,12 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of block kb
         lds_barrier();
         if (kb + 1 < kb1) issue(kb + 1, smem + (st ^ 1) * kStageBytes);
-        if constexpr (PO2) compute_po2(smem + st * kStageBytes);
-        else compute(smem + st * kStageBytes);
+        if (!SPLIT || active) {
+            if constexpr (PO2) compute_po2(smem + st * kStageBytes);
+            else compute(smem + st * kStageBytes);
+        }
     }
+    if (SPLIT && !active) return;
 
     // epilogue: row m0 + wm*WTM + 16*i + frow, columns n0 + wn*WTN + 16*j + 4*fg .. +3
 #pragma unroll
@@ -511,11 +540,29 @@ static void launch_v1(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_
     const int64_t tiles_m = (a.M + kTM - 1) / kTM, tiles_n = (a.N + TN - 1) / TN;
     const dim3 block(kV1Threads);
     if (!grouped) {
-        const dim3 grid((unsigned)(tiles_m * tiles_n));
-        if (kind == kWgrad)
-            hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kDense, PO2>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense, PO2>), grid, block, 0, stream, a);
+        // Tiles beyond the last whole round of CUs: when they fill at most half a
+        // round and come in multiples of 8, each is computed as two column halves
+        // by two blocks, so that round takes about half a tile's time.
+        const int64_t total = tiles_m * tiles_n, cus = device_cus();
+        const int64_t full = (total / cus) * cus, rem = total - full;
+        GemmArgs p = a;
+        p.split_from = -1;
+        int64_t nblocks = total;
+        if (full > 0 && rem > 0 && 2 * rem <= cus && rem % 8 == 0 && full % 8 == 0) {
+            p.split_from = full;
+            nblocks = full + 2 * rem;
+        }
+        const dim3 grid((unsigned)nblocks);
+        if (p.split_from >= 0) {
+            if (kind == kWgrad)
+                hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kDense, PO2, true>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense, PO2, true>), grid, block, 0, stream, p);
+        } else if (kind == kWgrad) {
+            hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kDense, PO2>), grid, block, 0, stream, p);
+        } else {
+            hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense, PO2>), grid, block, 0, stream, p);
+        }
     } else if (kind == kWgrad) {
         const dim3 grid((unsigned)(tiles_m * tiles_n * a.E));
         hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kGroupK, PO2>), grid, block, 0, stream, a);

@@ -161,10 +161,13 @@ def mfma_block_model(a_codes, b_codes):
 def gemm_bound(r, aabs, bf16_out, hw, nblk):
     """Acceptance bound per output: the in-block truncation bound `hw`, fp32
     rounding of sub-group sums, scale products and the cross-block FMA chain
-    ((nblk + 20) * 2^-24 * aabs), and half a bf16 ulp of r for BF16 outputs."""
+    ((nblk + 20) * 2^-24 * aabs), and, for BF16 outputs, half a bf16 ulp at the
+    largest magnitude the fp32 result can have (|r| + that fp32 bound): a result
+    pushed across a power of two rounds on the upper binade's coarser grid."""
     tol = hw + (nblk + 20) * 2.0 ** -24 * aabs
     if bf16_out:
-        tol = tol + np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 8)
+        top = np.maximum(np.abs(r) + tol, 2.0 ** -126)
+        tol = tol + np.exp2(np.floor(np.log2(top)) - 8)
     return tol
 
 

@@ -76,6 +76,29 @@ def test_wgrad_small(orc, K, N, M):
     check_gemm(host(dw2), r + prev, aabs + np.abs(prev), False, "wgrad accumulate", hw, nb + 1)
 
 
+@pytest.mark.parametrize("M,N", [(2048, 8448)])
+def test_tail_round_split(orc, M, N):
+    """A dense grid of 8 x 33 = 264 tiles of 256 x 256 on 256 CUs: the 8 tiles
+    beyond the first round are computed as column halves by 16 blocks.  Fprop
+    and Wgrad, every output compared."""
+    g = np.random.default_rng(M + N)
+    K = 128
+    qx, qwT = rand_codes(g, (M, K)), rand_codes(g, (N, K))
+    sx, sw = rand_scales(g, (K // T, M)), rand_scales(g, (K // T, N // T))
+    y = fgb.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qwT), f32_dev(sw))
+    r, aabs = orc.gemm_fprop(qx, sx, qwT, sw)
+    check_gemm(bf16_host_f64(y), r, aabs, True, f"fprop {M}x{N}x{K}", hw_bound_fprop(qx, sx, qwT, sw), K // T)
+    Mc = 200                                        # Wgrad contraction, ragged
+    Mp = T * 2
+    qxT, qdyT = rand_codes(g, (M, Mp)), rand_codes(g, (N, Mp))
+    qxT[:, Mc:] = 0
+    qdyT[:, Mc:] = 0
+    sxT, sdyT = rand_scales(g, (2, M)), rand_scales(g, (2, N))
+    dw = fgb.gemm_wgrad(u8_dev(qxT), f32_dev(sxT), u8_dev(qdyT), f32_dev(sdyT), Mc)
+    r, aabs = orc.gemm_wgrad(qxT, sxT, qdyT, sdyT, Mc)
+    check_gemm(host(dw), r, aabs, False, f"wgrad {M}x{N}x{Mc}", hw_bound_wgrad(qxT, sxT, qdyT, sdyT, Mc), 2)
+
+
 SMALL_INT_CODES = np.array([0x00, 0x80, 0x38, 0xB8, 0x40, 0xC0, 0x44, 0xC4, 0x48, 0xC8, 0x4C, 0xCC, 0x50, 0xD0],
                            np.uint8)   # 0, -0, +-1, +-2, +-3, +-4, +-6, +-8
 
