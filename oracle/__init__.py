@@ -28,6 +28,10 @@ function computes, with the passage it follows:
 * ``*_ue8m0`` quantizers -- power-of-two scales stored as E8M0 bytes (prime-rl
   PR #4073 "Results": the power-of-two scale format); the GEMMs take them as
   fp32 scales through ``e8m0_decode``.
+* ``*_sr`` quantizers, ``philox4x32_10``, ``e4m3_encode_sr`` -- stochastic
+  rounding of the cast (prime-rl PR #4073 conventions row "SR agreement":
+  stateless seed/salt/counter words from Philox, lower/upper-magnitude
+  neighbour); Philox4x32-10 as published by Salmon et al. (SC'11).
 
 The GEMM functions return the exact-to-fp64 value ``r`` and the absolute sum
 ``aabs`` (sum of |terms|), not a rounded output; callers compare the GPU's
@@ -106,6 +110,17 @@ def _load():
     lib.orc_e4m3_encode_bits_range.argtypes = [ctypes.c_uint32, I64, P]
     lib.orc_e4m3_decode_array.argtypes = [P, I64, P]
     lib.orc_bf16_round_array.argtypes = [P, I64, P]
+    U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.orc_philox4x32_10.argtypes = [P, P, P]
+    lib.orc_sr_word.restype = ctypes.c_uint32
+    lib.orc_sr_word.argtypes = [U64, U32, I64, I64]
+    lib.orc_e4m3_encode_sr.restype = ctypes.c_uint8
+    lib.orc_e4m3_encode_sr.argtypes = [F, U32]
+    lib.orc_e4m3_encode_sr_array.argtypes = [P, P, I64, P]
+    lib.orc_sr_words.argtypes = [U64, U32, I64, I64, I64, I64, P]
+    lib.orc_quantize_1x128_sr.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, U64, U32]
+    lib.orc_quantize_128x1_sr.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, U64, U32]
+    lib.orc_quantize_128x128_sr.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, P, U64, U32]
     lib.orc_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -275,6 +290,75 @@ def requant_128x1_ue8m0(q, e):
     eT = np.empty((_cdiv(R, TILE), C), np.uint8)
     _load().orc_requant_128x1_ue8m0(_ptr(q), R, C, C, _ptr(e), R, _ptr(qT), Rp, _ptr(eT), C)
     return qT, eT
+
+
+# --------------------------------------------------------------------------
+# Stochastic rounding: the same tile scales, the cast picks the lower or upper
+# E4M3 magnitude neighbour with a Philox4x32-10 word per element (prime-rl
+# PR #4073 conventions row "SR agreement": stateless seed/salt/counter, Philox,
+# lower/upper-magnitude rule; the word layout is a reading, see fgb_oracle.c).
+# --------------------------------------------------------------------------
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """One Philox4x32-10 block: ctr 4 x uint32, key 2 x uint32 -> 4 x uint32."""
+    c = _c(ctr, np.uint32)
+    k = _c(key, np.uint32)
+    assert c.shape == (4,) and k.shape == (2,)
+    out = np.empty(4, np.uint32)
+    _load().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_words(seed: int, salt: int, r0: int, R: int, c0: int, C: int) -> np.ndarray:
+    """The random words of elements (r0..r0+R-1) x (c0..c0+C-1) -> uint32 [R, C]."""
+    out = np.empty((R, C), np.uint32)
+    _load().orc_sr_words(seed, salt, r0, R, c0, C, _ptr(out))
+    return out
+
+
+def e4m3_encode_sr(v, u) -> np.ndarray:
+    """SR codes of fp32 values v with 32-bit words u (same shape)."""
+    v = _c(v, np.float32)
+    u = _c(u, np.uint32)
+    assert v.shape == u.shape
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_e4m3_encode_sr_array(_ptr(v), _ptr(u), v.size, _ptr(out))
+    return out
+
+
+def quantize_1x128_sr(x_bits, seed: int, salt: int, amax_floor: float = 0.0):
+    """As quantize_1x128 with the SR cast."""
+    x = _c(x_bits, np.uint16)
+    R, C = x.shape
+    q = np.empty((R, C), np.uint8)
+    s = np.empty((_cdiv(C, TILE), R), np.float32)
+    _load().orc_quantize_1x128_sr(_ptr(x), R, C, C, ctypes.c_float(amax_floor), _ptr(q), C, _ptr(s), R,
+                                  seed, salt)
+    return q, s
+
+
+def quantize_128x1_sr(x_bits, seed: int, salt: int, amax_floor: float = 0.0):
+    """As quantize_128x1 with the SR cast (element (r, c) of x draws word (r, c))."""
+    x = _c(x_bits, np.uint16)
+    R, C = x.shape
+    Rp = _cdiv(R, TILE) * TILE
+    qT = np.empty((C, Rp), np.uint8)
+    sT = np.empty((_cdiv(R, TILE), C), np.float32)
+    _load().orc_quantize_128x1_sr(_ptr(x), R, C, C, ctypes.c_float(amax_floor), _ptr(qT), Rp, _ptr(sT), C,
+                                  seed, salt)
+    return qT, sT
+
+
+def quantize_128x128_sr(w_bits, seed: int, salt: int, amax_floor: float = 0.0):
+    """As quantize_128x128 with the SR cast (q and qT hold the same codes)."""
+    w = _c(w_bits, np.uint16)
+    K, N = w.shape
+    q = np.empty((K, N), np.uint8)
+    qT = np.empty((N, K), np.uint8)
+    s = np.empty((_cdiv(K, TILE), _cdiv(N, TILE)), np.float32)
+    _load().orc_quantize_128x128_sr(_ptr(w), K, N, N, ctypes.c_float(amax_floor), _ptr(q), N, _ptr(qT), K,
+                                    _ptr(s), seed, salt)
+    return q, qT, s
 
 
 # --------------------------------------------------------------------------

@@ -513,3 +513,202 @@ int orc_max_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------ */
+/* Stochastic rounding (SR)                                            */
+/* ------------------------------------------------------------------ */
+/*
+ * prime-rl PR #4073, conventions row "SR agreement": SR draws from a
+ * stateless seed / salt / counter contract through a Philox helper and picks
+ * the lower- or upper-magnitude neighbour; the exact contract lives in a PR
+ * the pages do not include.  Reading used here:
+ *
+ *  - random word: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ *    numbers: as easy as 1, 2, 3", SC'11) with key (seed mod 2^32,
+ *    seed div 2^32) and counter (c div 4, r, salt, 0) for the element at row r,
+ *    column c of the tensor being quantized (the source tensor, whatever the
+ *    output layout); the element takes word c mod 4 of the output block;
+ *  - the tile scale is the round-to-nearest quantizer's (s = a'/448, the same
+ *    v = fl32(x * inv)); only the final cast changes;
+ *  - with m = |v|, lo = the largest E4M3 magnitude <= m and hi = the smallest
+ *    E4M3 magnitude >= m, the cast takes hi when u < (m - lo)/(hi - lo) * 2^32
+ *    (u the 32-bit word, compared as real numbers) and lo otherwise, so
+ *    P(hi) = (m - lo)/(hi - lo) up to 2^-32 and E[dec(q)] = v; m >= 448
+ *    saturates to 448, NaN gives S.1111.111, the sign of v is kept (-0 too).
+ */
+
+/* One Philox4x32-10 block: ten rounds of the two 32x32 -> 64-bit products
+ * with multipliers 0xD2511F53 and 0xCD9E8D57, the key bumped by the Weyl
+ * constants 0x9E3779B9 and 0xBB67AE85 between rounds. */
+void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0;
+        uint32_t n1 = lo1;
+        uint32_t n2 = hi0 ^ c3 ^ k1;
+        uint32_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The random word of element (r, c) under (seed, salt). */
+uint32_t orc_sr_word(uint64_t seed, uint32_t salt, int64_t r, int64_t c)
+{
+    uint32_t ctr[4] = {(uint32_t)(c / 4), (uint32_t)r, salt, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    orc_philox4x32_10(ctr, key, out);
+    return out[c % 4];
+}
+
+/* The 127 finite non-negative E4M3 magnitudes in increasing order (codes
+ * 0x00 .. 0x7E decode to increasing values). */
+static double e4m3_magnitude(int code) { return orc_e4m3_decode((uint8_t)code); }
+
+/* E4M3 code of v under stochastic rounding with random word u. */
+uint8_t orc_e4m3_encode_sr(float v, uint32_t u)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;
+    double m = fabs((double)v);
+    if (m >= 448.0) return sign | 0x7E;
+    /* lo: largest code whose magnitude is <= m (binary search over 0..0x7E) */
+    int a = 0, b = 0x7E;          /* invariant: mag(a) <= m < mag(b) */
+    while (b - a > 1) {
+        int mid = (a + b) / 2;
+        if (e4m3_magnitude(mid) <= m) a = mid; else b = mid;
+    }
+    double lo = e4m3_magnitude(a);
+    if (lo == m) return sign | (uint8_t)a;
+    double hi = e4m3_magnitude(a + 1);
+    double frac = (m - lo) / (hi - lo);              /* exact: hi - lo is a power of two */
+    int up = (double)u < frac * 4294967296.0;        /* exact comparison in double */
+    return sign | (uint8_t)(up ? a + 1 : a);
+}
+
+/* One tile as quantize_tile, with the SR cast; u[i] is element i's word. */
+static void quantize_tile_sr(const float* v, const uint32_t* u, int64_t n, float amax_floor,
+                             float* s_out, uint8_t* q_out)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float av = fabsf(v[i]);
+        if (isnan(av) || av > a) a = av;
+        if (isnan(a)) break;
+    }
+    if (amax_floor > a) a = amax_floor;
+    float s = a / 448.0f;
+    float inv;
+    if (a == 0.0f) {
+        inv = 0.0f;
+    } else {
+        inv = 448.0f / a;
+        if (inv > FLT_MAX) inv = FLT_MAX;
+    }
+    *s_out = s;
+    for (int64_t i = 0; i < n; ++i) q_out[i] = orc_e4m3_encode_sr(v[i] * inv, u[i]);
+}
+
+/* As orc_quantize_1x128 with the SR cast. */
+void orc_quantize_1x128_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                           float amax_floor, uint8_t* q, int64_t ldq,
+                           float* s, int64_t lds, uint64_t seed, uint32_t salt)
+{
+    int64_t nb = ceil_div(C, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        float v[ORC_TILE];
+        uint32_t u[ORC_TILE];
+        uint8_t code[ORC_TILE];
+        for (int64_t j = 0; j < nb; ++j) {
+            int64_t c0 = j * ORC_TILE;
+            int64_t n = (C - c0 < ORC_TILE) ? C - c0 : ORC_TILE;
+            for (int64_t i = 0; i < n; ++i) {
+                v[i] = orc_bf16_to_float(x[r * ldx + c0 + i]);
+                u[i] = orc_sr_word(seed, salt, r, c0 + i);
+            }
+            quantize_tile_sr(v, u, n, amax_floor, &s[j * lds + r], code);
+            for (int64_t i = 0; i < n; ++i) q[r * ldq + c0 + i] = code[i];
+        }
+    }
+}
+
+/* As orc_quantize_128x1 with the SR cast; element (r, c) of x draws word (r, c). */
+void orc_quantize_128x1_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                           float amax_floor, uint8_t* qT, int64_t ldqT,
+                           float* sT, int64_t ldsT, uint64_t seed, uint32_t salt)
+{
+    int64_t nb = ceil_div(R, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        float v[ORC_TILE];
+        uint32_t u[ORC_TILE];
+        uint8_t code[ORC_TILE];
+        for (int64_t i = 0; i < nb; ++i) {
+            int64_t r0 = i * ORC_TILE;
+            int64_t n = (R - r0 < ORC_TILE) ? R - r0 : ORC_TILE;
+            for (int64_t k = 0; k < n; ++k) {
+                v[k] = orc_bf16_to_float(x[(r0 + k) * ldx + c]);
+                u[k] = orc_sr_word(seed, salt, r0 + k, c);
+            }
+            quantize_tile_sr(v, u, n, amax_floor, &sT[i * ldsT + c], code);
+            for (int64_t k = 0; k < ORC_TILE; ++k)
+                qT[c * ldqT + r0 + k] = (k < n) ? code[k] : 0x00;
+        }
+    }
+}
+
+/* As orc_quantize_128x128 with the SR cast; element (k, n) of w draws word (k, n),
+ * and q and qT hold the same codes. */
+void orc_quantize_128x128_sr(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
+                             float amax_floor, uint8_t* q, int64_t ldq,
+                             uint8_t* qT, int64_t ldqT, float* s, uint64_t seed, uint32_t salt)
+{
+    int64_t kb = ceil_div(K, ORC_TILE), nb = ceil_div(N, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < kb * nb; ++t) {
+        int64_t i = t / nb, j = t % nb;
+        int64_t k0 = i * ORC_TILE, n0 = j * ORC_TILE;
+        int64_t kn = (K - k0 < ORC_TILE) ? K - k0 : ORC_TILE;
+        int64_t nn = (N - n0 < ORC_TILE) ? N - n0 : ORC_TILE;
+        float* v = (float*)malloc(sizeof(float) * ORC_TILE * ORC_TILE);
+        uint32_t* u = (uint32_t*)malloc(sizeof(uint32_t) * ORC_TILE * ORC_TILE);
+        uint8_t* code = (uint8_t*)malloc(ORC_TILE * ORC_TILE);
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b) {
+                v[a * nn + b] = orc_bf16_to_float(w[(k0 + a) * ldw + n0 + b]);
+                u[a * nn + b] = orc_sr_word(seed, salt, k0 + a, n0 + b);
+            }
+        quantize_tile_sr(v, u, kn * nn, amax_floor, &s[i * nb + j], code);
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b) {
+                if (q) q[(k0 + a) * ldq + n0 + b] = code[a * nn + b];
+                if (qT) qT[(n0 + b) * ldqT + k0 + a] = code[a * nn + b];
+            }
+        free(v); free(u); free(code);
+    }
+}
+
+/* Vector helper for the tests: codes of v[i] with words u[i]. */
+void orc_e4m3_encode_sr_array(const float* v, const uint32_t* u, int64_t n, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode_sr(v[i], u[i]);
+}
+
+/* Words of elements (r0 .. r0+R-1) x (c0 .. c0+C-1), row-major into out. */
+void orc_sr_words(uint64_t seed, uint32_t salt, int64_t r0, int64_t R, int64_t c0, int64_t C, uint32_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j) out[i * C + j] = orc_sr_word(seed, salt, r0 + i, c0 + j);
+}

@@ -13,7 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_codec.py", "tests/test_oracle_quant.py", "tests/test_oracle_gemm.py",
-             "tests/test_oracle_ue8m0.py"]
+             "tests/test_oracle_ue8m0.py", "tests/test_oracle_sr.py"]
 
 # name -> (text in oracle/fgb_oracle.c, replacement); every occurrence of the text is
 # replaced (a mistake copied into both scale formats' code)
@@ -54,6 +54,21 @@ MUTANTS = {
     "ue8m0_clamp_at_minus_126": ("    int e = -127;\n", "    int e = -126;\n"),
     "e8m0_decode_bias_126": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)"),
     "requant_ue8m0_first_block_byte": ("orc_e8m0_decode(e[(c / ORC_TILE) * lde + r])", "orc_e8m0_decode(e[r])"),
+    "philox_multiplier_typo": ("(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F57u * c0"),
+    "philox_nine_rounds": ("for (int round = 0; round < 10; ++round)", "for (int round = 0; round < 9; ++round)"),
+    "philox_weyl_constants_swapped": ("k0 += 0x9E3779B9u;\n        k1 += 0xBB67AE85u;",
+                                      "k0 += 0xBB67AE85u;\n        k1 += 0x9E3779B9u;"),
+    "sr_word_index_shifted": ("return out[c % 4];", "return out[(c + 1) % 4];"),
+    "sr_counter_row_col_swapped": ("{(uint32_t)(c / 4), (uint32_t)r, salt, 0u}", "{(uint32_t)(r / 4), (uint32_t)c, salt, 0u}"),
+    "sr_key_halves_swapped": ("{(uint32_t)seed, (uint32_t)(seed >> 32)}", "{(uint32_t)(seed >> 32), (uint32_t)seed}"),
+    "sr_salt_ignored": ("(uint32_t)r, salt, 0u}", "(uint32_t)r, 0u, 0u}"),
+    "sr_compare_le": ("int up = (double)u < frac * 4294967296.0;", "int up = (double)u <= frac * 4294967296.0;"),
+    "sr_direction_inverted": ("int up = (double)u < frac * 4294967296.0;", "int up = (double)u >= frac * 4294967296.0;"),
+    "sr_128x1_word_transposed": ("u[k] = orc_sr_word(seed, salt, r0 + k, c);", "u[k] = orc_sr_word(seed, salt, c, r0 + k);"),
+    "sr_128x128_word_transposed": ("u[a * nn + b] = orc_sr_word(seed, salt, k0 + a, n0 + b);",
+                                   "u[a * nn + b] = orc_sr_word(seed, salt, n0 + b, k0 + a);"),
+    "sr_negative_zero_dropped": ("uint8_t sign = signbit(v) ? 0x80 : 0x00;", "uint8_t sign = (v < 0.0f) ? 0x80 : 0x00;"),
+    "sr_saturation_to_nan": ("if (m >= 448.0) return sign | 0x7E;", "if (m >= 448.0) return sign | 0x7F;"),
 }
 
 
