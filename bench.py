@@ -18,6 +18,9 @@ CPU oracle on a bounded sample of the same step.
 `--recipe ue8m0` runs the same step with power-of-two (UE8M0) scales, which the
 matrix core applies itself (no vector-ALU rescale).
 
+`--rounding sr` quantizes X, W and dY with stochastic rounding (one Philox
+word per element); the requant of the saved X stays round-to-nearest.
+
 `--workload moe_grouped` times the grouped expert GEMMs of one GPU's MoE share
 instead (32 experts, 8192 tokens routed top-8, gate/up and down projections,
 forward and backward); `value` then counts the routed rows' GEMM FLOP.
@@ -84,6 +87,9 @@ def parse():
                         "moe_grouped: the grouped expert GEMMs of one GPU's MoE share (no CPU baseline)")
     p.add_argument("--recipe", choices=["fp32", "ue8m0"], default="fp32",
                    help="fp32: scales absmax/448 (default); ue8m0: power-of-two scales, applied by the matrix core")
+    p.add_argument("--rounding", choices=["rn", "sr"], default="rn",
+                   help="rn: round-to-nearest casts (default); sr: stochastic rounding of the X, W and dY "
+                        "casts (Philox words; the requant of X stays round-to-nearest)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--separate-dy-casts", action="store_true",
                    help="quantize dY with two kernels (1x128, then 128x1) instead of the fused one")
@@ -109,7 +115,7 @@ def algorithmic_bytes(M, K, N):
     }
 
 
-def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False):
+def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False):
     """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work)
     per kernel, work = {"flop": ...} or {"bytes": ...} (algorithmic)."""
     import numpy as np
@@ -134,23 +140,26 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False):
     }
     ab = algorithmic_bytes(M, K, N)
     flop = {"flop": 2.0 * M * N * K}
+    # stochastic rounding: one (seed, salt) per step, a salt per tensor
+    srk = (lambda salt: (0x5EED, salt)) if sr else (lambda salt: None)
     if separate_dy:
         dy_casts = [
-            ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"], ue8m0=ue8m0),
+            ("quantize_1x128_dy", lambda: fgb.quantize_1x128(dy, q=b["qdy"], s=b["sdy"], ue8m0=ue8m0, sr=srk(3)),
              {"bytes": ab["quantize_1x128_dy"]}),
-            ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"], ue8m0=ue8m0),
+            ("quantize_128x1_dy", lambda: fgb.quantize_128x1(dy, qT=b["qdyT"], sT=b["sdyT"], ue8m0=ue8m0, sr=srk(3)),
              {"bytes": ab["quantize_128x1_dy"]}),
         ]
     else:
         dy_casts = [
             ("quantize_dual_dy", lambda: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"],
-                                                          ue8m0=ue8m0),
+                                                          ue8m0=ue8m0, sr=srk(3)),
              {"bytes": ab["quantize_dual_dy"]}),
         ]
     steps = [
-        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"], ue8m0=ue8m0),
+        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"], ue8m0=ue8m0, sr=srk(1)),
          {"bytes": ab["quantize_1x128_x"]}),
-        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"], ue8m0=ue8m0),
+        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"], ue8m0=ue8m0,
+                                                            sr=srk(2)),
          {"bytes": ab["quantize_128x128_w"]}),
         ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"], ue8m0=ue8m0), flop),
     ] + dy_casts + [
@@ -162,6 +171,8 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False):
     ]
     if ue8m0:
         steps = [(name + "_ue8m0", fn, work) for name, fn, work in steps]
+    if sr:
+        steps = [(name + ("_sr" if name.startswith("quantize") else ""), fn, work) for name, fn, work in steps]
     return steps
 
 
@@ -239,10 +250,15 @@ def main():
     if args.workload == "linear_dsv3_attn":
         d = wl.linear_dsv3_attn()
         ue8m0 = args.recipe == "ue8m0"
-        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts, ue8m0=ue8m0)
+        sr = args.rounding == "sr"
+        if ue8m0 and sr:
+            print("bench.py: stochastic rounding uses absmax/448 scales (--recipe fp32)", file=sys.stderr)
+            sys.exit(2)
+        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts, ue8m0=ue8m0, sr=sr)
         config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]"
-                              + (", power-of-two (UE8M0) scales" if ue8m0 else ""),
-                  "M": d["M"], "K": d["K"], "N": d["N"], "scales": args.recipe}
+                              + (", power-of-two (UE8M0) scales" if ue8m0 else "")
+                              + (", stochastic rounding of the X, W and dY casts" if sr else ""),
+                  "M": d["M"], "K": d["K"], "N": d["N"], "scales": args.recipe, "rounding": args.rounding}
         data = "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)"
     else:
         d = wl.moe_grouped()
@@ -333,11 +349,12 @@ def main():
         del a, c
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl.linear_dsv3_attn(), args.cpu_rows, args.recipe == "ue8m0")
+        out["cpu_baseline"] = cpu_baseline(wl.linear_dsv3_attn(), args.cpu_rows, args.recipe == "ue8m0",
+                                           args.rounding == "sr")
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(d, rows_arg, ue8m0=False):
+def cpu_baseline(d, rows_arg, ue8m0=False, sr=False):
     """The CPU oracle, as it stands, on a bounded sample of the same step: the
     three quantizers of X/dY and W on full tensors, then Fprop, Dgrad and Wgrad
     on a sample of output rows (all columns, full contraction).  Reported as the
@@ -355,6 +372,12 @@ def cpu_baseline(d, rows_arg, ue8m0=False):
         qdyT, edyT = oracle.quantize_128x1_ue8m0(d["dy"])
         qxT, exT = oracle.requant_128x1_ue8m0(qx, ex)
         sx, sw, sdy, sdyT, sxT = dec(ex), dec(ew), dec(edy), dec(edyT), dec(exT)
+    elif sr:
+        qx, sx = oracle.quantize_1x128_sr(d["x"], 0x5EED, 1)
+        q, qT, sw = oracle.quantize_128x128_sr(d["w"], 0x5EED, 2)
+        qdy, sdy = oracle.quantize_1x128_sr(d["dy"], 0x5EED, 3)
+        qdyT, sdyT = oracle.quantize_128x1_sr(d["dy"], 0x5EED, 3)
+        qxT, sxT = oracle.requant_128x1(qx, sx)
     else:
         qx, sx = oracle.quantize_1x128(d["x"])
         q, qT, sw = oracle.quantize_128x128(d["w"])

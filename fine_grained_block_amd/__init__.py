@@ -22,6 +22,10 @@ scales = ``torch.float32``):
 Every quantizer and GEMM takes ``ue8m0=True`` for the power-of-two-scale twin
 (``..._ue8m0`` entry points): scales are exact powers of two in fp32 and the
 GEMMs let the matrix core apply them.
+
+The 1x128, 128x1, dual and 128x128 quantizers take ``sr=(seed, salt)`` for the
+stochastic-rounding twin (``..._sr`` entry points): same scales, the cast picks
+the lower or upper E4M3 neighbour with one Philox4x32-10 word per element.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ STATUS = {0: "FGB_OK", -1: "FGB_E_NULL", -2: "FGB_E_SHAPE", -3: "FGB_E_ALIGN", -
 
 # name -> ctypes argument types (P = pointer, I = int64, F = float, N = int)
 _P, _I, _F, _N = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_U64, _U32 = ctypes.c_uint64, ctypes.c_uint32
 SIGNATURES = {
     "fgb_quantize_1x128": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
     "fgb_quantize_128x1": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P],
@@ -62,6 +67,10 @@ SIGNATURES = {
     "fgb_gemm_fprop_grouped_ue8m0": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
     "fgb_gemm_dgrad_grouped_ue8m0": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P],
     "fgb_gemm_wgrad_grouped_ue8m0": [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _N, _P],
+    "fgb_quantize_1x128_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _U64, _U32, _P],
+    "fgb_quantize_128x1_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _U64, _U32, _P],
+    "fgb_quantize_dual_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _U64, _U32, _P],
+    "fgb_quantize_128x128_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _U64, _U32, _P],
     "fgb_status_string": [_N],
     "fgb_version": [],
 }
@@ -124,6 +133,17 @@ def _fn(name: str, ue8m0: bool):
     return getattr(lib(), name + "_ue8m0" if ue8m0 else name)
 
 
+def _quant_call(name: str, ue8m0: bool, sr, args):
+    """Call quantizer `name` (round to nearest), its _ue8m0 twin, or with sr = (seed,
+    salt) its stochastic-rounding twin `name`_sr; the stream stays the last argument."""
+    if sr is None:
+        return _fn(name, ue8m0)(*args)
+    if ue8m0:
+        raise FgbError(f"{name}: stochastic rounding uses absmax/448 scales (no ue8m0 twin)")
+    seed, salt = sr
+    return getattr(lib(), name + "_sr")(*args[:-1], ctypes.c_uint64(seed), ctypes.c_uint32(salt), args[-1])
+
+
 def version() -> int:
     return lib().fgb_version()
 
@@ -132,31 +152,34 @@ def version() -> int:
 # Quantizers
 # ---------------------------------------------------------------------------
 
-def quantize_1x128(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, ue8m0: bool = False):
+def quantize_1x128(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, ue8m0: bool = False, sr=None):
     R, C = x.shape
     ldx = _rows(x, torch.bfloat16, "x")
     if q is None:
         q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device)
-    _check(_fn("fgb_quantize_1x128", ue8m0)(_ptr(x), R, C, ldx, amax_floor, _ptr(q), _rows(q, torch.uint8, "q"),
-                                    _ptr(s), _rows(s, torch.float32, "s"), _stream(x)), "quantize_1x128")
+    _check(_quant_call("fgb_quantize_1x128", ue8m0, sr, (_ptr(x), R, C, ldx, amax_floor, _ptr(q),
+                       _rows(q, torch.uint8, "q"), _ptr(s), _rows(s, torch.float32, "s"), _stream(x))),
+           "quantize_1x128")
     return q, s
 
 
-def quantize_128x1(x: torch.Tensor, amax_floor: float = 0.0, qT=None, sT=None, ue8m0: bool = False):
+def quantize_128x1(x: torch.Tensor, amax_floor: float = 0.0, qT=None, sT=None, ue8m0: bool = False, sr=None):
     R, C = x.shape
     ldx = _rows(x, torch.bfloat16, "x")
     if qT is None:
         qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=x.device)
     if sT is None:
         sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=x.device)
-    _check(_fn("fgb_quantize_128x1", ue8m0)(_ptr(x), R, C, ldx, amax_floor, _ptr(qT), _rows(qT, torch.uint8, "qT"),
-                                    _ptr(sT), _rows(sT, torch.float32, "sT"), _stream(x)), "quantize_128x1")
+    _check(_quant_call("fgb_quantize_128x1", ue8m0, sr, (_ptr(x), R, C, ldx, amax_floor, _ptr(qT),
+                       _rows(qT, torch.uint8, "qT"), _ptr(sT), _rows(sT, torch.float32, "sT"), _stream(x))),
+           "quantize_128x1")
     return qT, sT
 
 
-def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=None, sT=None, ue8m0: bool = False):
+def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=None, sT=None, ue8m0: bool = False,
+                  sr=None):
     """Both orientations from one read: (q, s) as quantize_1x128, (qT, sT) as quantize_128x1."""
     R, C = x.shape
     ldx = _rows(x, torch.bfloat16, "x")
@@ -168,15 +191,15 @@ def quantize_dual(x: torch.Tensor, amax_floor: float = 0.0, q=None, s=None, qT=N
         qT = torch.empty((C, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=x.device)
     if sT is None:
         sT = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=x.device)
-    _check(_fn("fgb_quantize_dual", ue8m0)(_ptr(x), R, C, ldx, amax_floor,
-                                   _ptr(q), _rows(q, torch.uint8, "q"), _ptr(s), _rows(s, torch.float32, "s"),
-                                   _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT), _rows(sT, torch.float32, "sT"),
-                                   _stream(x)), "quantize_dual")
+    _check(_quant_call("fgb_quantize_dual", ue8m0, sr, (_ptr(x), R, C, ldx, amax_floor,
+                       _ptr(q), _rows(q, torch.uint8, "q"), _ptr(s), _rows(s, torch.float32, "s"),
+                       _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT), _rows(sT, torch.float32, "sT"),
+                       _stream(x))), "quantize_dual")
     return q, s, qT, sT
 
 
 def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = True, want_qT: bool = True,
-                     q=None, qT=None, s=None, ue8m0: bool = False):
+                     q=None, qT=None, s=None, ue8m0: bool = False, sr=None):
     K, N = w.shape
     ldw = _rows(w, torch.bfloat16, "w")
     if want_q and q is None:
@@ -187,8 +210,8 @@ def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = Tr
         s = torch.empty((_cdiv(K, TILE), _cdiv(N, TILE)), dtype=torch.float32, device=w.device)
     ldq = _rows(q, torch.uint8, "q") if q is not None else 0
     ldqT = _rows(qT, torch.uint8, "qT") if qT is not None else 0
-    _check(_fn("fgb_quantize_128x128", ue8m0)(_ptr(w), K, N, ldw, amax_floor, _ptr(q), ldq, _ptr(qT), ldqT,
-                                      _ptr(s), _stream(w)), "quantize_128x128")
+    _check(_quant_call("fgb_quantize_128x128", ue8m0, sr, (_ptr(w), K, N, ldw, amax_floor, _ptr(q), ldq, _ptr(qT),
+                       ldqT, _ptr(s), _stream(w))), "quantize_128x128")
     return q, qT, s
 
 

@@ -81,7 +81,8 @@ const char* fgb_status_string(int status)
 static int check_sc(const float* p, int64_t ld, int64_t need, bool) { return check_scales(p, ld, need); }
 
 static int quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
-                          uint8_t* q, int64_t ldq, float* s, int64_t lds, bool po2, void* stream)
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds, bool po2, void* stream,
+                          const fgb::SrParams* sr = nullptr)
 {
     if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
@@ -89,11 +90,12 @@ static int quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, 
     FGB_TRY(check_bf16(x, ldx, C));
     FGB_TRY(check_codes(q, ldq, C, 8));
     FGB_TRY(check_sc(s, lds, R, po2));
-    return hip_status(fgb::launch_quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, po2, as_stream(stream)));
+    return hip_status(fgb::launch_quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, po2, as_stream(stream), sr));
 }
 
 static int quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
-                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream)
+                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream,
+                          const fgb::SrParams* sr = nullptr)
 {
     if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
@@ -102,12 +104,14 @@ static int quantize_128x1(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, 
     FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
     FGB_TRY(check_sc(sT, ldsT, C, po2));
     return hip_status(fgb::launch_tile128(fgb::kTile128x1, x, R, C, ldx, nullptr, 0, amax_floor,
-                                          nullptr, 0, qT, ldqT, sT, ldsT, po2, as_stream(stream)));
+                                          nullptr, 0, qT, ldqT, sT, ldsT, po2, as_stream(stream),
+                                          nullptr, 0, sr));
 }
 
 static int quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
                          uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream)
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream,
+                         const fgb::SrParams* sr = nullptr)
 {
     if (R < 0 || C < 0 || C % 8 != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
@@ -118,11 +122,12 @@ static int quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, f
     FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
     FGB_TRY(check_sc(sT, ldsT, C, po2));
     return hip_status(fgb::launch_tile128(fgb::kTileDual, x, R, C, ldx, nullptr, 0, amax_floor,
-                                          q, ldq, qT, ldqT, sT, ldsT, po2, as_stream(stream), s, lds));
+                                          q, ldq, qT, ldqT, sT, ldsT, po2, as_stream(stream), s, lds, sr));
 }
 
 static int quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
-                            uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, bool po2, void* stream)
+                            uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, bool po2, void* stream,
+                            const fgb::SrParams* sr = nullptr)
 {
     if (K < 0 || N < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
     if (bad_floor(amax_floor)) return FGB_E_ARG;
@@ -133,7 +138,7 @@ static int quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw
     if (qT) FGB_TRY(check_codes(qT, ldqT, K, 16));
     FGB_TRY(check_sc(s, N / T, N / T, po2));
     return hip_status(fgb::launch_tile128(fgb::kTile128x128, w, K, N, ldw, nullptr, 0, amax_floor,
-                                          q, ldq, qT, ldqT, s, N / T, po2, as_stream(stream)));
+                                          q, ldq, qT, ldqT, s, N / T, po2, as_stream(stream), nullptr, 0, sr));
 }
 
 static int requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq, const float* s, int64_t lds,
@@ -209,6 +214,42 @@ int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream)
 {
     return requant_128x1(q, R, C, ldq, s, lds, qT, ldqT, sT, ldsT, true, stream);
+}
+
+// Stochastic-rounding twins (absmax/448 scales): the same tiles and scales, the
+// cast picks the lower or upper E4M3 neighbour with one Philox4x32-10 word per
+// element.
+int fgb_quantize_1x128_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds, uint64_t seed, uint32_t salt,
+                          void* stream)
+{
+    const fgb::SrParams sr{seed, salt};
+    return quantize_1x128(x, R, C, ldx, amax_floor, q, ldq, s, lds, false, stream, &sr);
+}
+
+int fgb_quantize_128x1_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, uint64_t seed, uint32_t salt,
+                          void* stream)
+{
+    const fgb::SrParams sr{seed, salt};
+    return quantize_128x1(x, R, C, ldx, amax_floor, qT, ldqT, sT, ldsT, false, stream, &sr);
+}
+
+int fgb_quantize_dual_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, uint64_t seed, uint32_t salt,
+                         void* stream)
+{
+    const fgb::SrParams sr{seed, salt};
+    return quantize_dual(x, R, C, ldx, amax_floor, q, ldq, s, lds, qT, ldqT, sT, ldsT, false, stream, &sr);
+}
+
+int fgb_quantize_128x128_sr(const uint16_t* w, int64_t K, int64_t N, int64_t ldw, float amax_floor,
+                            uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
+                            uint64_t seed, uint32_t salt, void* stream)
+{
+    const fgb::SrParams sr{seed, salt};
+    return quantize_128x128(w, K, N, ldw, amax_floor, q, ldq, qT, ldqT, s, false, stream, &sr);
 }
 
 static int gemm_fprop_impl(int64_t M, int64_t N, int64_t K,

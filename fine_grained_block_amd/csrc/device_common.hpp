@@ -86,6 +86,85 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
 }
 
 // ---------------------------------------------------------------------------
+// Stochastic rounding (prime-rl PR #4073, conventions row "SR agreement": a
+// stateless seed / salt / counter Philox word per element, and the lower- or
+// upper-magnitude E4M3 neighbour).
+//
+// philox4x32_10: the Philox4x32 generator with 10 rounds (Salmon, Moraes,
+// Dror, Shaw, SC'11).  Element (r, c) of the tensor being quantized takes
+// word c % 4 of the block at counter (c / 4, r, salt, 0), key (seed low,
+// seed high); the key is wave-uniform.
+// ---------------------------------------------------------------------------
+struct SrArgs {
+    uint32_t k0 = 0, k1 = 0;      // seed, low and high 32 bits
+    uint32_t salt = 0;
+};
+
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1, uint32_t (&out)[4]) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+// Words of the 8 consecutive elements (r, c .. c+7), c a multiple of 8.
+__device__ __forceinline__ void sr_words8(const SrArgs& a, int64_t r, int64_t c, uint32_t (&u)[8]) {
+    uint32_t w0[4], w1[4];
+    philox4x32_10((uint32_t)(c >> 2), (uint32_t)r, a.salt, 0u, a.k0, a.k1, w0);
+    philox4x32_10((uint32_t)(c >> 2) + 1u, (uint32_t)r, a.salt, 0u, a.k0, a.k1, w1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { u[i] = w0[i]; u[4 + i] = w1[i]; }
+}
+
+// The E4M3 value that stochastic rounding of v with word u selects (an exact
+// grid value, sign kept, |v| >= 448 -> 448; NaN passes through): with m = |v|,
+// lo/hi its lower/upper grid neighbours, hi when u < (m - lo)/(hi - lo) * 2^32.
+//   m >= 2^-6 (E4M3 normals): the grid keeps 3 of the 23 fp32 mantissa bits;
+//     (m - lo)/(hi - lo) = D / 2^20 for D the 20 dropped bits, so hi iff
+//     (u >> 12) < D, and hi = lo + one unit of the kept mantissa (IEEE carry).
+//   m < 2^-6: spacing 2^-9; t = 512 m is exact, frac = t - floor(t) exact,
+//     frac * 2^32 exact, and u < frac * 2^32 iff u < ceil(frac * 2^32); frac
+//     has at most 24 significant bits, so ceil(frac * 2^32) <= 2^32 - 2^8 fits
+//     in 32 bits.
+__device__ __forceinline__ float e4m3_sr_value(float v, uint32_t u) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t mb = b & 0x7FFFFFFFu;
+    if (mb > 0x7F800000u) return v;                       // NaN
+    if (mb >= 0x43E00000u) return __uint_as_float((b & 0x80000000u) | 0x43E00000u);   // >= 448
+    float mag;
+    if (mb >= 0x3C800000u) {                              // >= 2^-6
+        const uint32_t d = mb & 0xFFFFFu;
+        const uint32_t up = (u >> 12) < d ? 1u : 0u;
+        mag = __uint_as_float((mb & ~0xFFFFFu) + (up << 20));
+    } else {
+        const float t = __uint_as_float(mb) * 512.0f;
+        const float fl = floorf(t);
+        const float thr = (t - fl) * 4294967296.0f;
+        const uint32_t tc = (uint32_t)ceilf(thr);
+        const float up = u < tc ? 1.0f : 0.0f;
+        mag = (fl + up) * 0.001953125f;                   // (fl + up) * 2^-9, exact
+    }
+    return __uint_as_float(__float_as_uint(mag) | (b & 0x80000000u));
+}
+
+// Four SR codes (byte i = code of value i).
+__device__ __forceinline__ uint32_t e4m3x4_sr(float a, float b, float c, float d,
+                                              uint32_t ua, uint32_t ub, uint32_t uc, uint32_t ud) {
+    return e4m3x4(e4m3_sr_value(a, ua), e4m3_sr_value(b, ub), e4m3_sr_value(c, uc), e4m3_sr_value(d, ud));
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane unsigned max.  DPP within a row of 16 lanes, then swizzles.
 // ---------------------------------------------------------------------------
 template <int CTRL>

@@ -8,10 +8,16 @@
 namespace fgb {
 
 // ----------------------------- quantizers ---------------------------------
+// Stochastic rounding of the cast: Philox4x32-10 words keyed by seed, with the
+// salt in the counter (NULL = round to nearest).
+struct SrParams { uint64_t seed; uint32_t salt; };
+
 // po2: power-of-two scales (the UE8M0 value set, in fp32); otherwise absmax/448.
+// sr (absmax/448 scales only): stochastic rounding; NULL = round to nearest.
 hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                                  float amax_floor, uint8_t* q, int64_t ldq,
-                                 float* s, int64_t lds, bool po2, hipStream_t stream);
+                                 float* s, int64_t lds, bool po2, hipStream_t stream,
+                                 const SrParams* sr = nullptr);
 
 enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 3 };
 
@@ -22,11 +28,12 @@ enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 
 //   kTileDual:    bf16 in, both the 1x128 codes and scales (q, s_row) and the
 //                 128x1 transposed codes and scales (qT, sT) from one read
 // po2 as above for every scale written (scales read by the requant are fp32 either way).
+// sr: stochastic rounding for kTile128x1, kTile128x128 and kTileDual (absmax/448).
 hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                           float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
-                          float* s_row = nullptr, int64_t lds_row = 0);
+                          float* s_row = nullptr, int64_t lds_row = 0, const SrParams* sr = nullptr);
 
 // ------------------------------- GEMMs -------------------------------------
 // out[m][n] = sum_b SA(m,b) * SB(n,b) * sum_{t in block b} dec(A[m][t]) dec(B[n][t])

@@ -25,11 +25,13 @@ namespace fgb {
 constexpr int kQ1Rows = 64;
 
 // PO2: power-of-two scales (the UE8M0 values, held in fp32); otherwise absmax/448.
-template <bool PO2>
+// SR: stochastic rounding of the cast with the words of `sr` (absmax/448 scales).
+template <bool PO2, bool SR>
 __global__ __launch_bounds__(256) void k_quantize_1x128(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx, float amax_floor,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds)
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds, SrArgs sr)
 {
+    static_assert(!(PO2 && SR), "stochastic rounding uses absmax/448 scales");
     const int lane16 = threadIdx.x & 15;
     const int grp = threadIdx.x >> 4;
     const int64_t rb = (int64_t)blockIdx.x * kQ1Rows;
@@ -58,10 +60,18 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
         uint32_t eb = 0;
         if constexpr (PO2) tile_scale_ue8m0(a, eb, inv);
         else tile_scale(a, sc, inv);
-        const uint32_t o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv,
-                                   bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
-        const uint32_t o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv,
-                                   bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
+        uint32_t o0, o1;
+        if constexpr (SR) {
+            uint32_t u[8];
+            sr_words8(sr, r, c, u);
+            o0 = e4m3x4_sr(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv,
+                           u[0], u[1], u[2], u[3]);
+            o1 = e4m3x4_sr(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv,
+                           u[4], u[5], u[6], u[7]);
+        } else {
+            o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
+            o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
+        }
         if (cok && r < R) {
             st8(q + r * ldq + c, make_uint2(o0, o1));
             if (lane16 == 0) s[j * lds + r] = PO2 ? e8m0_to_f32(eb) : sc;
@@ -69,17 +79,33 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     }
 }
 
+static SrArgs sr_args(const SrParams* sr)
+{
+    SrArgs a;
+    if (sr) {
+        a.k0 = (uint32_t)sr->seed;
+        a.k1 = (uint32_t)(sr->seed >> 32);
+        a.salt = sr->salt;
+    }
+    return a;
+}
+
 hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                                  float amax_floor, uint8_t* q, int64_t ldq,
-                                 float* s, int64_t lds, bool po2, hipStream_t stream)
+                                 float* s, int64_t lds, bool po2, hipStream_t stream, const SrParams* sr)
 {
+    if (po2 && sr) return hipErrorInvalidValue;
     dim3 grid((unsigned)((R + kQ1Rows - 1) / kQ1Rows), (unsigned)((C + kTile - 1) / kTile));
+    const SrArgs a = sr_args(sr);
     if (po2)
-        hipLaunchKernelGGL(k_quantize_1x128<true>, grid, dim3(256), 0, stream,
-                           x, R, C, ldx, amax_floor, q, ldq, s, lds);
+        hipLaunchKernelGGL((k_quantize_1x128<true, false>), grid, dim3(256), 0, stream,
+                           x, R, C, ldx, amax_floor, q, ldq, s, lds, a);
+    else if (sr)
+        hipLaunchKernelGGL((k_quantize_1x128<false, true>), grid, dim3(256), 0, stream,
+                           x, R, C, ldx, amax_floor, q, ldq, s, lds, a);
     else
-        hipLaunchKernelGGL(k_quantize_1x128<false>, grid, dim3(256), 0, stream,
-                           x, R, C, ldx, amax_floor, q, ldq, s, lds);
+        hipLaunchKernelGGL((k_quantize_1x128<false, false>), grid, dim3(256), 0, stream,
+                           x, R, C, ldx, amax_floor, q, ldq, s, lds, a);
     return hipGetLastError();
 }
 
@@ -97,13 +123,17 @@ constexpr int kTrStride = 136;   // bytes per staged qT row (128 + 8 to spread b
 __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
 
 // PO2: the scales written are powers of two (the UE8M0 values, held in fp32).
-template <int MODE, bool PO2>
+// SR: stochastic rounding of every cast with the words of `sr` (element (r, c)
+// of the input draws word (r, c), so q, qT and the dual outputs of one element
+// use the same word); absmax/448 scales, not for the requant.
+template <int MODE, bool PO2, bool SR>
 __global__ __launch_bounds__(256) void k_tile128(
     const void* __restrict__ in, int64_t R, int64_t C, int64_t ldin,
     const float* __restrict__ s_in, int64_t lds_in, float amax_floor,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
-    float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row)
+    float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row, SrArgs sr)
 {
+    static_assert(!(SR && (PO2 || MODE == kTileRequant)), "stochastic rounding: absmax/448 scales, no requant");
     // scale of absmax a: fp32 (s = a/448, mul = 448/a) or power of two (E8M0 byte, mul = 2^-e)
     auto scale_of = [&](float a, float& sc, uint32_t& eb, float& mul) {
         if constexpr (PO2) tile_scale_ue8m0(a, eb, mul);
@@ -196,6 +226,71 @@ __global__ __launch_bounds__(256) void k_tile128(
         }
     }
 
+    if constexpr (SR) {
+        // Row by row: the 8 words of the patch row, then its codes -- with the
+        // row's own 1x128 scale (dual), the column scales (128x1, dual) or the
+        // tile scale (128x128) -- kept as row-major bytes cr[i] and transposed
+        // through LDS like the round-to-nearest path.
+        uint32_t cr[8][2];
+        float sr_own = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + rg * 8 + i;
+            uint32_t u[8];
+            sr_words8(sr, r, cc, u);
+            if constexpr (MODE == kTileDual) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
+                m = max16(m);
+                const float a = fmaxf(__uint_as_float(m), amax_floor);
+                float sc, iv;
+                tile_scale(a, sc, iv);
+                if (cg == i) sr_own = sc;
+                const uint32_t o0 = e4m3x4_sr(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv,
+                                              u[0], u[1], u[2], u[3]);
+                const uint32_t o1 = e4m3x4_sr(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv,
+                                              u[4], u[5], u[6], u[7]);
+                if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
+            }
+            cr[i][0] = e4m3x4_sr(v[i][0] * inv[0], v[i][1] * inv[1], v[i][2] * inv[2], v[i][3] * inv[3],
+                                 u[0], u[1], u[2], u[3]);
+            cr[i][1] = e4m3x4_sr(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7],
+                                 u[4], u[5], u[6], u[7]);
+            if constexpr (MODE == kTile128x128) {
+                if (q != nullptr && cok && r < R) st8(q + r * ldq + cc, make_uint2(cr[i][0], cr[i][1]));
+            }
+        }
+        if constexpr (MODE == kTileDual) {
+            const int64_t rr = r0 + rg * 8 + cg;
+            if (cg < 8 && rr < R) s_row[(int64_t)blockIdx.y * lds_row + rr] = sr_own;
+        }
+        if constexpr (MODE == kTile128x128) {
+            if (qT == nullptr) return;
+        }
+        // column k of the patch: byte k & 3 of cr[i][k >> 2] for rows i = 0..7
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int sh = (k & 3) * 8, h = k >> 2;
+            const uint32_t lo = ((cr[0][h] >> sh) & 0xFFu) | (((cr[1][h] >> sh) & 0xFFu) << 8) |
+                                (((cr[2][h] >> sh) & 0xFFu) << 16) | (((cr[3][h] >> sh) & 0xFFu) << 24);
+            const uint32_t hi = ((cr[4][h] >> sh) & 0xFFu) | (((cr[5][h] >> sh) & 0xFFu) << 8) |
+                                (((cr[6][h] >> sh) & 0xFFu) << 16) | (((cr[7][h] >> sh) & 0xFFu) << 24);
+            *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = p * 32 + (t >> 3);
+            const int seg = t & 7;
+            const int64_t c = c0 + row;
+            const uint2 a = *reinterpret_cast<const uint2*>(&tr[row * kTrStride + seg * 16]);
+            const uint2 b = *reinterpret_cast<const uint2*>(&tr[row * kTrStride + seg * 16 + 8]);
+            if (c < C) st16(qT + c * ldqT + r0 + seg * 16, make_uint4(a.x, a.y, b.x, b.y));
+        }
+        return;
+    }
+
     // Dual mode, 1x128 part: row r's tile is the block's 128 columns of row r,
     // held by the 16 lanes that share rg; their absmax is one DPP reduction.
     if constexpr (MODE == kTileDual) {
@@ -256,28 +351,30 @@ __global__ __launch_bounds__(256) void k_tile128(
     }
 }
 
-template <bool PO2>
+template <bool PO2, bool SR>
 static void launch_tile128_t(TileMode mode, dim3 grid, const void* in, int64_t R, int64_t C, int64_t ldin,
                              const float* s_in, int64_t lds_in, float amax_floor,
                              uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
-                             float* s_out, int64_t lds_out, hipStream_t stream, float* s_row, int64_t lds_row)
+                             float* s_out, int64_t lds_out, hipStream_t stream, float* s_row, int64_t lds_row,
+                             SrArgs a)
 {
     switch (mode) {
     case kTile128x1:
-        hipLaunchKernelGGL((k_tile128<kTile128x1, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
+        hipLaunchKernelGGL((k_tile128<kTile128x1, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
         break;
     case kTile128x128:
-        hipLaunchKernelGGL((k_tile128<kTile128x128, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
+        hipLaunchKernelGGL((k_tile128<kTile128x128, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
         break;
     case kTileRequant:
-        hipLaunchKernelGGL((k_tile128<kTileRequant, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
+        if constexpr (!SR)
+            hipLaunchKernelGGL((k_tile128<kTileRequant, PO2, false>), grid, dim3(256), 0, stream, in, R, C, ldin,
+                               s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
         break;
     case kTileDual:
-        hipLaunchKernelGGL((k_tile128<kTileDual, PO2>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row);
+        hipLaunchKernelGGL((k_tile128<kTileDual, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
         break;
     }
 }
@@ -286,15 +383,20 @@ hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, i
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                           float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
-                          float* s_row, int64_t lds_row)
+                          float* s_row, int64_t lds_row, const SrParams* sr)
 {
+    if (sr && (po2 || mode == kTileRequant)) return hipErrorInvalidValue;
     dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
+    const SrArgs a = sr_args(sr);
     if (po2)
-        launch_tile128_t<true>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                               s_out, lds_out, stream, s_row, lds_row);
+        launch_tile128_t<true, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
+                                      s_out, lds_out, stream, s_row, lds_row, a);
+    else if (sr)
+        launch_tile128_t<false, true>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
+                                      s_out, lds_out, stream, s_row, lds_row, a);
     else
-        launch_tile128_t<false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                s_out, lds_out, stream, s_row, lds_row);
+        launch_tile128_t<false, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
+                                       s_out, lds_out, stream, s_row, lds_row, a);
     return hipGetLastError();
 }
 

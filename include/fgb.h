@@ -146,6 +146,42 @@ int fgb_requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * Stochastic rounding ([sr]: prime-rl PR #4073, conventions row "SR
+ * agreement" -- a stateless seed/salt/counter Philox word per element and the
+ * lower- or upper-magnitude E4M3 neighbour; the word layout is this
+ * library's reading).  Each call below is its round-to-nearest twin with the
+ * same arguments, tiles and scales (s = a/448 bit for bit), except the cast:
+ *   v = fl32(x * inv), m = |v|; lo, hi = the E4M3 magnitudes with
+ *   lo <= m <= hi adjacent on the grid (lo = hi when m is on it);
+ *   code = hi when u < (m - lo)/(hi - lo) * 2^32 (real comparison), else lo;
+ *   m >= 448 -> 448; the sign of v is kept (-0 too).
+ * u, the element's word: element (r, c) of the INPUT tensor (x[r][c] or
+ * w[r][c], whatever the output layout) takes word c % 4 of the
+ * Philox4x32-10 block with counter (c / 4, r, salt, 0) and key
+ * (seed & 0xFFFFFFFF, seed >> 32).  So one element gets the same word in
+ * q, qT and in both outputs of the dual call, and equal (seed, salt) give
+ * equal codes (calls are deterministic).  Scales are absmax/448 (no _ue8m0
+ * twin); there is no stochastic requant.
+ * ---------------------------------------------------------------------- */
+int fgb_quantize_1x128_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                          float amax_floor,
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                          uint64_t seed, uint32_t salt, void* stream);
+int fgb_quantize_128x1_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                          float amax_floor,
+                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                          uint64_t seed, uint32_t salt, void* stream);
+int fgb_quantize_dual_sr(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                         float amax_floor,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                         uint64_t seed, uint32_t salt, void* stream);
+int fgb_quantize_128x128_sr(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
+                            float amax_floor,
+                            uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                            float* s, uint64_t seed, uint32_t salt, void* stream);
+
+/* ------------------------------------------------------------------------
  * Power-of-two scales ([po2]).  Each quantizer above has a _ue8m0 twin with
  * the same arguments and layouts whose scales are powers of two:
  *     e = the smallest integer with 448 * 2^e >= a, clamped to [-127, 127]

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = fgb.lib()
     names = header_functions()
-    assert len(names) == 24
+    assert len(names) == 28
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fgb.SIGNATURES)
@@ -174,3 +174,29 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(fgb.FgbError):
         fgb.quantize_1x128(x)
+
+
+def test_stochastic_rounding_validation():
+    """The _sr twins validate exactly like their round-to-nearest twins (no launch
+    on any error, empty inputs are no-ops)."""
+    L = fgb.lib()
+    U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+    seed, salt = U64(123), U32(4)
+
+    def q1(R=256, C=256, x=A, ldx=256, fl=0.0, q=B, ldq=256, s=C_, lds=256):
+        return L.fgb_quantize_1x128_sr(x, R, C, ldx, fl, q, ldq, s, lds, seed, salt, None)
+
+    assert q1(C=12) == E_SHAPE
+    assert q1(x=P(0)) == E_NULL
+    assert q1(ldq=64) == E_LD
+    assert q1(x=MIS) == E_ALIGN
+    assert q1(fl=-1.0) == E_ARG
+    assert q1(R=0, x=P(0), q=P(0), s=P(0)) == OK
+    assert L.fgb_quantize_128x1_sr(A, 200, 256, 256, 0.0, B, 128, C_, 256, seed, salt, None) == E_LD
+    assert L.fgb_quantize_128x1_sr(A, 200, 12, 256, 0.0, B, 256, C_, 256, seed, salt, None) == E_SHAPE
+    assert L.fgb_quantize_dual_sr(A, 256, 256, 256, 0.0, B, 256, C_, 256, P(0), 256, D, 256,
+                                  seed, salt, None) == E_NULL
+    assert L.fgb_quantize_128x128_sr(A, 200, 256, 256, 0.0, B, 256, C_, 256, D, seed, salt, None) == E_SHAPE
+    assert L.fgb_quantize_128x128_sr(A, 256, 256, 256, 0.0, P(0), 256, P(0), 256, D, seed, salt, None) == E_NULL
+    with pytest.raises(fgb.FgbError):
+        fgb._quant_call("fgb_quantize_1x128", True, (1, 2), (A, 1, 8, 8, 0.0, B, 8, C_, 1, None))
