@@ -28,6 +28,9 @@ function computes, with the passage it follows:
 * ``*_ue8m0`` quantizers -- power-of-two scales stored as E8M0 bytes (prime-rl
   PR #4073 "Results": the power-of-two scale format); the GEMMs take them as
   fp32 scales through ``e8m0_decode``.
+* ``swiglu_*`` -- SwiGLU with its casts fused into the producer kernels ("scratch"
+  page, same section: the SwiGLU input saved as E4M3, backward casts emitting
+  both orientations, backward computing in BF16 from the dequantized input).
 * ``*_sr`` quantizers, ``philox4x32_10``, ``e4m3_encode_sr`` -- stochastic
   rounding of the cast (prime-rl PR #4073 conventions row "SR agreement":
   stateless seed/salt/counter words from Philox, lower/upper-magnitude
@@ -121,6 +124,8 @@ def _load():
     lib.orc_quantize_1x128_sr.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, U64, U32]
     lib.orc_quantize_128x1_sr.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, U64, U32]
     lib.orc_quantize_128x128_sr.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, P, U64, U32]
+    lib.orc_swiglu_h.argtypes = [P, I64, I64, I64, P, I64]
+    lib.orc_swiglu_dgu.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64]
     lib.orc_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -359,6 +364,57 @@ def quantize_128x128_sr(w_bits, seed: int, salt: int, amax_floor: float = 0.0):
     _load().orc_quantize_128x128_sr(_ptr(w), K, N, N, ctypes.c_float(amax_floor), _ptr(q), N, _ptr(qT), K,
                                     _ptr(s), seed, salt)
     return q, qT, s
+
+
+# --------------------------------------------------------------------------
+# SwiGLU with its casts fused ("scratch" page, section "What is asserted, and
+# from where": the SwiGLU input saved as E4M3, the forward emitting the next
+# GEMM's E4M3 operand, the backward emitting both tile orientations and
+# computing in BF16 from the dequantized input).  [G | U] is one [R, 2F]
+# tensor; the exact values are rounded once to BF16 (see fgb_oracle.c).
+# --------------------------------------------------------------------------
+
+def swiglu_h(gu_bits):
+    """H = bf16(silu(G) * U) for GU [R, 2F] bf16 bits -> bf16 bits [R, F]."""
+    gu = _c(gu_bits, np.uint16)
+    R, F2 = gu.shape
+    assert F2 % 2 == 0
+    F = F2 // 2
+    h = np.empty((R, F), np.uint16)
+    _load().orc_swiglu_h(_ptr(gu), R, F, F2, _ptr(h), F)
+    return h
+
+
+def swiglu_dgu(q_gu, s_gu, dh_bits):
+    """[dG | dU] bf16 bits [R, 2F] from the 1x128 stash (q_gu [R, 2F], s_gu
+    [2F/128, R]) and dH [R, F] bf16 bits."""
+    q = _c(q_gu, np.uint8)
+    s = _c(s_gu, np.float32)
+    dh = _c(dh_bits, np.uint16)
+    R, F2 = q.shape
+    F = F2 // 2
+    assert dh.shape == (R, F) and s.shape == (_cdiv(F2, TILE), R)
+    out = np.empty((R, F2), np.uint16)
+    _load().orc_swiglu_dgu(_ptr(q), R, F, F2, _ptr(s), R, _ptr(dh), F, _ptr(out), F2)
+    return out
+
+
+def swiglu_fwd_quant(gu_bits, amax_floor: float = 0.0):
+    """The fused forward: (q_gu, s_gu) = 1x128 stash of [G | U]; (q_h, s_h) = 1x128
+    of H; h = H's bf16 bits."""
+    q_gu, s_gu = quantize_1x128(gu_bits, amax_floor)
+    h = swiglu_h(gu_bits)
+    q_h, s_h = quantize_1x128(h, amax_floor)
+    return q_gu, s_gu, q_h, s_h, h
+
+
+def swiglu_bwd_quant(q_gu, s_gu, dh_bits, amax_floor: float = 0.0):
+    """The fused backward: dgu = [dG | dU] bf16 bits, then both tile orientations
+    (q, s) = 1x128 and (qT, sT) = 128x1 of it."""
+    dgu = swiglu_dgu(q_gu, s_gu, dh_bits)
+    q, s = quantize_1x128(dgu, amax_floor)
+    qT, sT = quantize_128x1(dgu, amax_floor)
+    return dgu, q, s, qT, sT
 
 
 # --------------------------------------------------------------------------

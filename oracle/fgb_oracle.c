@@ -712,3 +712,157 @@ void orc_sr_words(uint64_t seed, uint32_t salt, int64_t r0, int64_t R, int64_t c
     for (int64_t i = 0; i < R; ++i)
         for (int64_t j = 0; j < C; ++j) out[i * C + j] = orc_sr_word(seed, salt, r0 + i, c0 + j);
 }
+
+/* ------------------------------------------------------------------ */
+/* SwiGLU with its casts fused (the producer vector kernels)          */
+/* ------------------------------------------------------------------ */
+/*
+ * "scratch: the backward pass, unrolled", section "What is asserted, and from
+ * where": the SwiGLU input is saved as E4M3 (a quantize box); a cast rides the
+ * nearest vector kernel, so the SwiGLU forward emits the next GEMM's E4M3
+ * operand and the SwiGLU backward emits the next dgrad's and wgrad's operands
+ * in both tile orientations (+T); the backward computes in BF16 from the
+ * dequantized E4M3 input (marked as inferred on the page).
+ *
+ * Readings used here:
+ *  - the gate/up output is one tensor [G | U] of shape [R][2F] (G = columns
+ *    0..F-1, U = columns F..2F-1), in BF16;
+ *  - forward:  H = bf16(silu(G) * U), silu(g) = g / (1 + exp(-g)), the exact
+ *    value rounded once (RNE) -- computed here in long double, with the exact
+ *    g*u/2 split off for tiny g so that a tie of g*u/2 is broken by the sign
+ *    of the correction, as the exact value breaks it;
+ *  - backward: G~ = bf16(fl32(dec(q_g) * s_g)), U~ likewise (the requant's
+ *    fp32 dequantization, then the BF16 compute dtype);
+ *    dG = bf16(dH * U~ * silu'(G~)), dU = bf16(dH * silu(G~)),
+ *    silu'(g) = sigma(g) * (1 + g * (1 - sigma(g))), each exact value rounded
+ *    once;
+ *  - the fused casts are exactly the quantizers above applied to [G | U]
+ *    (1x128, the stash), to H (1x128) and to [dG | dU] (1x128 and 128x1).
+ */
+
+/* Round a long double once to bfloat16 bits (to nearest, ties to even); the
+ * value is finite and its magnitude below 2^128. */
+static uint16_t bf16_round_ld(long double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    long double a = fabsl(v);
+    if (a == 0.0L) return sign;
+    int e2;
+    frexpl(a, &e2);
+    int ex = e2 - 1;                         /* a in [2^ex, 2^(ex+1)) */
+    if (ex < -126) ex = -126;                /* bf16 subnormals: quantum 2^-133 */
+    long double q = ldexpl(a, 7 - ex);       /* a / ulp, exact */
+    long double lo = floorl(q), frac = q - lo;
+    long double m = frac > 0.5L ? lo + 1.0L : (frac < 0.5L ? lo : (fmodl(lo, 2.0L) == 0.0L ? lo : lo + 1.0L));
+    float fv = (float)ldexpl(m, ex - 7);     /* exact: m has at most 9 bits */
+    uint32_t bits;
+    memcpy(&bits, &fv, sizeof bits);
+    return sign | (uint16_t)(bits >> 16);
+}
+
+/* One RNE rounding to bfloat16 of the exact value hi * (1 + c), where hi has at
+ * most 17 significant bits (a product of bf16 values, or half of one) and
+ * |c| <= 2^-10, whose sign is c_sign (+1, -1, or 0 when the correction is
+ * exactly zero; c itself may underflow to 0 for a huge gate).  A value with at most
+ * 17 significant bits that is not a bf16 midpoint lies at least 2^-17 |hi|
+ * from every midpoint, so when |c| < 2^-40 the correction only breaks a tie:
+ * a positive c rounds the magnitude up, a negative c down.  Otherwise
+ * hi + hi*c is formed in long double, where the correction (>= 2^-40
+ * relative) survives. */
+static uint16_t bf16_of_scaled(long double hi, long double c, int c_sign)
+{
+    if (fabsl(c) >= ldexpl(1.0L, -40)) return bf16_round_ld(hi + hi * c);
+    if (hi == 0.0L || c_sign == 0) return bf16_round_ld(hi);
+    uint16_t sign = signbit(hi) ? 0x8000 : 0x0000;
+    long double a = fabsl(hi);
+    int e2;
+    frexpl(a, &e2);
+    int ex = e2 - 1;
+    if (ex < -126) ex = -126;
+    long double q = ldexpl(a, 7 - ex);
+    long double lo = floorl(q);
+    if (q - lo != 0.5L) return bf16_round_ld(hi);
+    long double m = c_sign > 0 ? lo + 1.0L : lo;
+    float fv = (float)ldexpl(m, ex - 7);
+    uint32_t bits;
+    memcpy(&bits, &fv, sizeof bits);
+    return sign | (uint16_t)(bits >> 16);
+}
+
+/* sigma(g) = 1/(1 + e^-g) and 1 - sigma(g), each without cancellation. */
+static void sigma_ld(long double g, long double* sig, long double* one_minus)
+{
+    if (g >= 0.0L) {
+        long double e = expl(-g);
+        *sig = 1.0L / (1.0L + e);
+        *one_minus = e / (1.0L + e);
+    } else {
+        long double e = expl(g);
+        *sig = e / (1.0L + e);
+        *one_minus = 1.0L / (1.0L + e);
+    }
+}
+
+/* bf16(silu(g) * f), f a bf16 value or a product of two.  silu(g) = g sigma(g)
+ *   = (g/2) (1 + tanh(g/2))        split off for |g| < 2^-10,
+ *   = g (1 - (1 - sigma(g)))        split off where 1 - sigma(g) < 2^-10,
+ * so that an exact product on a bf16 midpoint is moved off it the way the
+ * exact value is; elsewhere g f sigma(g) in long double. */
+static uint16_t bf16_silu_times(long double g, long double f)
+{
+    if (fabsl(g) < ldexpl(1.0L, -10))
+        return bf16_of_scaled(g * f * 0.5L, tanhl(0.5L * g), g > 0.0L ? 1 : (g < 0.0L ? -1 : 0));
+    long double sig, om;
+    sigma_ld(g, &sig, &om);
+    if (om < ldexpl(1.0L, -10)) return bf16_of_scaled(g * f, -om, -1);
+    return bf16_round_ld(g * f * sig);
+}
+
+/* bf16(silu'(g) * f).  silu'(g) = sigma (1 + g (1 - sigma))
+ *   = (1/2) (1 + tanh(g/2) + g / (2 cosh^2(g/2)))   split off for |g| < 2^-10,
+ *   = 1 + (1 - sigma) (g sigma - 1)                  split off where that term
+ *                                                    is below 2^-10,
+ * elsewhere f sigma (1 + g (1 - sigma)) in long double. */
+static uint16_t bf16_dsilu_times(long double g, long double f)
+{
+    if (fabsl(g) < ldexpl(1.0L, -10)) {
+        long double ch = coshl(0.5L * g);
+        return bf16_of_scaled(f * 0.5L, tanhl(0.5L * g) + g / (2.0L * ch * ch),
+                              g > 0.0L ? 1 : (g < 0.0L ? -1 : 0));
+    }
+    long double sig, om;
+    sigma_ld(g, &sig, &om);
+    long double c = om * (g * sig - 1.0L);
+    if (g > 2.0L && fabsl(c) < ldexpl(1.0L, -10)) return bf16_of_scaled(f, c, 1);   /* g sigma > 1 */
+    return bf16_round_ld(f * (sig * (1.0L + g * om)));
+}
+
+/* H [R][F] bf16 bits from GU [R][2F] (ld ldgu). */
+void orc_swiglu_h(const uint16_t* gu, int64_t R, int64_t F, int64_t ldgu, uint16_t* h, int64_t ldh)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < F; ++c) {
+            long double g = orc_bf16_to_float(gu[r * ldgu + c]);
+            long double u = orc_bf16_to_float(gu[r * ldgu + F + c]);
+            h[r * ldh + c] = bf16_silu_times(g, u);
+        }
+}
+
+/* [dG | dU] [R][2F] bf16 bits from the 1x128 stash (codes q [R][2F], scales
+ * s [2F/128][R]) and dH [R][F] bf16. */
+void orc_swiglu_dgu(const uint8_t* q, int64_t R, int64_t F, int64_t ldq, const float* s, int64_t lds,
+                    const uint16_t* dh, int64_t lddh, uint16_t* dgu, int64_t lddgu)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < F; ++c) {
+            float gq = (float)(orc_e4m3_decode(q[r * ldq + c]) * (double)s[(c / ORC_TILE) * lds + r]);
+            float uq = (float)(orc_e4m3_decode(q[r * ldq + F + c]) * (double)s[((F + c) / ORC_TILE) * lds + r]);
+            long double g = orc_bf16_to_float(orc_bf16_round((double)gq));
+            long double u = orc_bf16_to_float(orc_bf16_round((double)uq));
+            long double d = orc_bf16_to_float(dh[r * lddh + c]);
+            dgu[r * lddgu + c] = bf16_dsilu_times(g, d * u);      /* d * u exact */
+            dgu[r * lddgu + F + c] = bf16_silu_times(g, d);
+        }
+}

@@ -13,7 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_codec.py", "tests/test_oracle_quant.py", "tests/test_oracle_gemm.py",
-             "tests/test_oracle_ue8m0.py", "tests/test_oracle_sr.py"]
+             "tests/test_oracle_ue8m0.py", "tests/test_oracle_sr.py", "tests/test_oracle_swiglu.py"]
 
 # name -> (text in oracle/fgb_oracle.c, replacement); every occurrence of the text is
 # replaced (a mistake copied into both scale formats' code)
@@ -69,6 +69,26 @@ MUTANTS = {
                                    "u[a * nn + b] = orc_sr_word(seed, salt, n0 + b, k0 + a);"),
     "sr_negative_zero_dropped": ("uint8_t sign = signbit(v) ? 0x80 : 0x00;", "uint8_t sign = (v < 0.0f) ? 0x80 : 0x00;"),
     "sr_saturation_to_nan": ("if (m >= 448.0) return sign | 0x7E;", "if (m >= 448.0) return sign | 0x7F;"),
+    "silu_tanh_sign_flipped": ("return bf16_of_scaled(g * f * 0.5L, tanhl(0.5L * g),",
+                               "return bf16_of_scaled(g * f * 0.5L, tanhl(-0.5L * g),"),
+    "silu_large_gate_tie_up": ("return bf16_of_scaled(g * f, -om, -1);", "return bf16_of_scaled(g * f, -om, 1);"),
+    "silu_small_gate_tie_sign": ("g > 0.0L ? 1 : (g < 0.0L ? -1 : 0));\n    long double sig",
+                                 "g > 0.0L ? -1 : (g < 0.0L ? 1 : 0));\n    long double sig"),
+    "dsilu_cosh_term_dropped": ("tanhl(0.5L * g) + g / (2.0L * ch * ch)", "tanhl(0.5L * g)"),
+    "dsilu_uses_sigma_twice": ("return bf16_round_ld(f * (sig * (1.0L + g * om)));",
+                               "return bf16_round_ld(f * (sig * (1.0L + g * sig)));"),
+    "dsilu_large_gate_split_sign": ("return bf16_of_scaled(f, c, 1);", "return bf16_of_scaled(f, c, -1);"),
+    "sigma_negative_branch": ("*sig = e / (1.0L + e);", "*sig = 1.0L / (1.0L + e);"),
+    "bf16_ld_ties_up": ("(fmodl(lo, 2.0L) == 0.0L ? lo : lo + 1.0L)", "(lo + 1.0L)"),
+    "zero_gate_tie_broken": ("if (hi == 0.0L || c_sign == 0) return bf16_round_ld(hi);",
+                             "if (hi == 0.0L) return bf16_round_ld(hi);"),
+    "swiglu_up_read_from_gate": ("long double u = orc_bf16_to_float(gu[r * ldgu + F + c]);",
+                                 "long double u = orc_bf16_to_float(gu[r * ldgu + c]);"),
+    "swiglu_bwd_dequant_no_bf16": ("long double g = orc_bf16_to_float(orc_bf16_round((double)gq));",
+                                   "long double g = gq;"),
+    "swiglu_bwd_up_scale_block": ("s[((F + c) / ORC_TILE) * lds + r]", "s[(c / ORC_TILE) * lds + r]"),
+    "swiglu_bwd_outputs_swapped": ("dgu[r * lddgu + c] = bf16_dsilu_times(g, d * u);",
+                                   "dgu[r * lddgu + c] = bf16_silu_times(g, d);"),
 }
 
 
