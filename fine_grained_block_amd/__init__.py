@@ -71,6 +71,8 @@ SIGNATURES = {
     "fgb_quantize_128x1_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _U64, _U32, _P],
     "fgb_quantize_dual_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _U64, _U32, _P],
     "fgb_quantize_128x128_sr": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _U64, _U32, _P],
+    "fgb_swiglu_fwd_quant": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P],
+    "fgb_swiglu_bwd_quant": [_P, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P],
     "fgb_status_string": [_N],
     "fgb_version": [],
 }
@@ -226,6 +228,58 @@ def requant_128x1(q: torch.Tensor, s: torch.Tensor, qT=None, sT=None, ue8m0: boo
                                    _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT),
                                    _rows(sT, torch.float32, "sT"), _stream(q)), "requant_128x1")
     return qT, sT
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU with fused casts ([G | U] is one [R, 2F] bf16 tensor)
+# ---------------------------------------------------------------------------
+
+def swiglu_fwd_quant(gu: torch.Tensor, amax_floor: float = 0.0, stash: bool = True, want_h: bool = False,
+                     q_gu=None, s_gu=None, q_h=None, s_h=None, h=None):
+    """H = bf16(silu(G) U): returns (q_gu, s_gu, q_h, s_h, h) -- the 1x128 stash of
+    [G | U] (None when stash=False), the 1x128 codes/scales of H, and H (when want_h)."""
+    R, F2 = gu.shape
+    F = F2 // 2
+    ldgu = _rows(gu, torch.bfloat16, "gu")
+    dev = gu.device
+    if stash:
+        q_gu = torch.empty((R, F2), dtype=torch.uint8, device=dev) if q_gu is None else q_gu
+        s_gu = torch.empty((_cdiv(F2, TILE), R), dtype=torch.float32, device=dev) if s_gu is None else s_gu
+    q_h = torch.empty((R, F), dtype=torch.uint8, device=dev) if q_h is None else q_h
+    s_h = torch.empty((_cdiv(F, TILE), R), dtype=torch.float32, device=dev) if s_h is None else s_h
+    if want_h and h is None:
+        h = torch.empty((R, F), dtype=torch.bfloat16, device=dev)
+    _check(lib().fgb_swiglu_fwd_quant(
+        _ptr(gu), R, F, ldgu, amax_floor,
+        _ptr(q_gu), _rows(q_gu, torch.uint8, "q_gu") if q_gu is not None else 0,
+        _ptr(s_gu), _rows(s_gu, torch.float32, "s_gu") if s_gu is not None else 0,
+        _ptr(q_h), _rows(q_h, torch.uint8, "q_h"), _ptr(s_h), _rows(s_h, torch.float32, "s_h"),
+        _ptr(h), _rows(h, torch.bfloat16, "h") if h is not None else 0, _stream(gu)), "swiglu_fwd_quant")
+    return q_gu, s_gu, q_h, s_h, h
+
+
+def swiglu_bwd_quant(q_gu: torch.Tensor, s_gu: torch.Tensor, dh: torch.Tensor, amax_floor: float = 0.0,
+                     want_dgu: bool = False, q=None, s=None, qT=None, sT=None, dgu=None):
+    """[dG | dU] from the stash and dH, quantized both ways: returns (q, s, qT, sT, dgu)
+    with (q, s) as quantize_1x128 and (qT, sT) as quantize_128x1 of [dG | dU]
+    (dgu itself when want_dgu)."""
+    R, F2 = q_gu.shape
+    F = F2 // 2
+    dev = q_gu.device
+    q = torch.empty((R, F2), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((_cdiv(F2, TILE), R), dtype=torch.float32, device=dev) if s is None else s
+    qT = torch.empty((F2, _cdiv(R, TILE) * TILE), dtype=torch.uint8, device=dev) if qT is None else qT
+    sT = torch.empty((_cdiv(R, TILE), F2), dtype=torch.float32, device=dev) if sT is None else sT
+    if want_dgu and dgu is None:
+        dgu = torch.empty((R, F2), dtype=torch.bfloat16, device=dev)
+    _check(lib().fgb_swiglu_bwd_quant(
+        _ptr(q_gu), R, F, _rows(q_gu, torch.uint8, "q_gu"), _ptr(s_gu), _rows(s_gu, torch.float32, "s_gu"),
+        _ptr(dh), _rows(dh, torch.bfloat16, "dh"), amax_floor,
+        _ptr(q), _rows(q, torch.uint8, "q"), _ptr(s), _rows(s, torch.float32, "s"),
+        _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT), _rows(sT, torch.float32, "sT"),
+        _ptr(dgu), _rows(dgu, torch.bfloat16, "dgu") if dgu is not None else 0, _stream(q_gu)),
+        "swiglu_bwd_quant")
+    return q, s, qT, sT, dgu
 
 
 # ---------------------------------------------------------------------------

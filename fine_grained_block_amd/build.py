@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfgb.so")
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "swiglu.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -216,6 +216,49 @@ int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
     return requant_128x1(q, R, C, ldq, s, lds, qT, ldqT, sT, ldsT, true, stream);
 }
 
+// ------------------------------- SwiGLU ------------------------------------
+int fgb_swiglu_fwd_quant(const uint16_t* gu, int64_t R, int64_t F, int64_t ldgu, float amax_floor,
+                         uint8_t* q_gu, int64_t ldq_gu, float* s_gu, int64_t lds_gu,
+                         uint8_t* q_h, int64_t ldq_h, float* s_h, int64_t lds_h,
+                         uint16_t* h, int64_t ldh, void* stream)
+{
+    if (R < 0 || F < 0 || F % T != 0) return FGB_E_SHAPE;
+    if (bad_floor(amax_floor)) return FGB_E_ARG;
+    if (R == 0 || F == 0) return FGB_OK;
+    FGB_TRY(check_bf16(gu, ldgu, 2 * F));
+    if ((q_gu == nullptr) != (s_gu == nullptr)) return FGB_E_NULL;
+    if (q_gu) {
+        FGB_TRY(check_codes(q_gu, ldq_gu, 2 * F, 8));
+        FGB_TRY(check_scales(s_gu, lds_gu, R));
+    }
+    FGB_TRY(check_codes(q_h, ldq_h, F, 8));
+    FGB_TRY(check_scales(s_h, lds_h, R));
+    if (h) FGB_TRY(check_bf16(h, ldh, F));
+    return hip_status(fgb::launch_swiglu_fwd(gu, R, F, ldgu, amax_floor, q_gu, ldq_gu, s_gu, lds_gu,
+                                             q_h, ldq_h, s_h, lds_h, h, ldh, as_stream(stream)));
+}
+
+int fgb_swiglu_bwd_quant(const uint8_t* q_gu, int64_t R, int64_t F, int64_t ldq_gu, const float* s_gu, int64_t lds_gu,
+                         const uint16_t* dh, int64_t lddh, float amax_floor,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                         uint16_t* dgu, int64_t lddgu, void* stream)
+{
+    if (R < 0 || F < 0 || F % T != 0) return FGB_E_SHAPE;
+    if (bad_floor(amax_floor)) return FGB_E_ARG;
+    if (R == 0 || F == 0) return FGB_OK;
+    FGB_TRY(check_codes(q_gu, ldq_gu, 2 * F, 8));
+    FGB_TRY(check_scales(s_gu, lds_gu, R));
+    FGB_TRY(check_bf16(dh, lddh, F));
+    FGB_TRY(check_codes(q, ldq, 2 * F, 8));
+    FGB_TRY(check_scales(s, lds, R));
+    FGB_TRY(check_codes(qT, ldqT, rup(R, T), 16));
+    FGB_TRY(check_scales(sT, ldsT, 2 * F));
+    if (dgu) FGB_TRY(check_bf16(dgu, lddgu, 2 * F));
+    return hip_status(fgb::launch_swiglu_bwd(q_gu, R, F, ldq_gu, s_gu, lds_gu, dh, lddh, amax_floor,
+                                             q, ldq, s, lds, qT, ldqT, sT, ldsT, dgu, lddgu, as_stream(stream)));
+}
+
 // Stochastic-rounding twins (absmax/448 scales): the same tiles and scales, the
 // cast picks the lower or upper E4M3 neighbour with one Philox4x32-10 word per
 // element.

@@ -35,6 +35,23 @@ hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, i
                           float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
                           float* s_row = nullptr, int64_t lds_row = 0, const SrParams* sr = nullptr);
 
+// ------------------------------- SwiGLU ------------------------------------
+// [G | U] is one [R][2F] bf16 tensor, F % 128 == 0.  Forward: the 1x128 stash
+// of [G | U] (q_gu, s_gu; both NULL to skip), the 1x128 codes of
+// H = bf16(silu(G) U) (q_h, s_h), and H itself (h, NULL to skip).
+hipError_t launch_swiglu_fwd(const uint16_t* gu, int64_t R, int64_t F, int64_t ldgu, float amax_floor,
+                             uint8_t* q_gu, int64_t ldq_gu, float* s_gu, int64_t lds_gu,
+                             uint8_t* q_h, int64_t ldq_h, float* s_h, int64_t lds_h,
+                             uint16_t* h, int64_t ldh, hipStream_t stream);
+// Backward: from the stash and dH [R][F], [dG | dU] [R][2F] quantized 1x128
+// (q, s) and 128x1 (qT [2F][ldqT >= roundup(R,128)] zero padded, sT), and
+// [dG | dU] itself (dgu, NULL to skip).
+hipError_t launch_swiglu_bwd(const uint8_t* q_gu, int64_t R, int64_t F, int64_t ldq_gu,
+                             const float* s_gu, int64_t lds_gu, const uint16_t* dh, int64_t lddh,
+                             float amax_floor, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                             uint16_t* dgu, int64_t lddgu, hipStream_t stream);
+
 // ------------------------------- GEMMs -------------------------------------
 // out[m][n] = sum_b SA(m,b) * SB(n,b) * sum_{t in block b} dec(A[m][t]) dec(B[n][t])
 //   A [M][lda], B [N][ldb]: both contraction-contiguous E4M3 codes

@@ -1,0 +1,406 @@
+// SwiGLU with its E4M3 casts fused into the producer kernels, for gfx950.
+//
+// "scratch: the backward pass, unrolled", section "What is asserted, and from
+// where": the SwiGLU input is saved as E4M3; a cast rides the nearest vector
+// kernel, so the SwiGLU forward emits the down projection's E4M3 operand and
+// the SwiGLU backward emits the gate/up projection's dgrad and wgrad operands
+// in both tile orientations; the backward computes in BF16 from the
+// dequantized E4M3 input.
+//
+// The gate/up output is one tensor [G | U] of shape [R][2F] (G = columns
+// 0..F-1, U = F..2F-1).  Values:
+//   forward   H  = bf16(silu(G) * U)                          (one rounding of the exact value)
+//   backward  G~ = bf16(fl32(dec(q_g) * s_g)), U~ likewise     (dequantize, then the BF16 dtype)
+//             dG = bf16(dH * U~ * silu'(G~)), dU = bf16(dH * silu(G~))
+// and the casts are the 1x128 / 128x1 tile quantizers of quant.hip applied to
+// [G | U] (the stash), H, and [dG | dU].
+//
+// Exact rounding.  Each value is first formed in fp32 (expf, IEEE division).
+// Its relative error is a few fp32 ulps (the expf error plus four roundings;
+// for silu' the cancellation in 1 + g (1 - sigma) is carried in a per-element
+// bound).  When the fp32 value lies farther than that bound from every bf16
+// rounding midpoint, its bf16 rounding is the exact value's.  Otherwise, and
+// for |g| > 80, the value is recomputed in fp64, where an exact product on a
+// midpoint (g*u/2 for tiny g, g*u or f for a saturated sigmoid) is moved off
+// it by the sign of the exact correction.
+
+#include "device_common.hpp"
+#include "fgb_internal.hpp"
+
+namespace fgb {
+
+namespace {
+
+// One RNE rounding of a finite double (|v| < 2^128) to bf16 bits: round to
+// fp32 with round-to-odd (truncate, set the last bit when inexact), then RNE
+// to bf16 -- round-to-odd with >= 2 extra bits makes the second rounding exact.
+__device__ uint32_t bf16_rne_f64(double v) {
+    float f = (float)v;
+    const double back = (double)f;
+    if (back != v) {
+        uint32_t b = __float_as_uint(f);
+        if (fabs(back) > fabs(v)) b -= 1u;          // the magnitude was rounded up: step back
+        f = __uint_as_float(b | 1u);
+    }
+    return f32_to_bf16_rne(f) & 0xFFFFu;
+}
+
+// bf16 bits of the exact hi * (1 + c): hi has at most 17 significant bits,
+// |c| <= 2^-10 with sign c_sign (0: c is exactly 0; c may underflow to 0 for
+// a huge gate).  A 17-bit value that is not a bf16 midpoint lies >= 2^-17 |hi|
+// from every midpoint, so below |c| = 2^-36 the correction only breaks a tie;
+// above it hi + hi*c keeps the correction in fp64 (17 + 36 = 53 bits).
+__device__ uint32_t bf16_scaled_f64(double hi, double c, int c_sign) {
+    if (fabs(c) >= 0x1p-36) return bf16_rne_f64(hi + hi * c);
+    if (hi == 0.0 || c_sign == 0) return bf16_rne_f64(hi);
+    int ex;
+    frexp(fabs(hi), &ex);
+    ex -= 1;                                        // |hi| in [2^ex, 2^(ex+1))
+    if (ex < -126) ex = -126;                       // bf16 subnormal quantum 2^-133
+    const double q = ldexp(fabs(hi), 7 - ex);       // exact
+    const double fl = floor(q);
+    if (q - fl != 0.5) return bf16_rne_f64(hi);
+    const double m = c_sign > 0 ? fl + 1.0 : fl;    // the tie goes the correction's way
+    const float r = (float)ldexp(m, ex - 7);        // exact
+    return (__float_as_uint(r) >> 16) | (signbit(hi) ? 0x8000u : 0u);
+}
+
+// sigma(g) and 1 - sigma(g) in fp64, each without cancellation.
+__device__ void sigma_f64(double g, double& sig, double& om) {
+    if (g >= 0.0) {
+        const double e = exp(-g);
+        sig = 1.0 / (1.0 + e);
+        om = e / (1.0 + e);
+    } else {
+        const double e = exp(g);
+        sig = e / (1.0 + e);
+        om = 1.0 / (1.0 + e);
+    }
+}
+
+// bf16(silu(g) * f) in fp64 (f exact: a bf16 value).
+//   silu(g) = (g/2)(1 + tanh(g/2)), split off for |g| < 2^-10;
+//           = g (1 - (1 - sigma)), split off where 1 - sigma < 2^-10.
+__device__ __noinline__ uint32_t silu_times_f64(float gf, float ff) {
+    const double g = gf, f = ff;
+    if (fabs(g) < 0x1p-10)
+        return bf16_scaled_f64(g * f * 0.5, tanh(0.5 * g), g > 0.0 ? 1 : (g < 0.0 ? -1 : 0));
+    double sig, om;
+    sigma_f64(g, sig, om);
+    if (om < 0x1p-10) return bf16_scaled_f64(g * f, -om, -1);
+    return bf16_rne_f64(g * f * sig);
+}
+
+// bf16(silu'(g) * d * u) in fp64 (d * u exact there: two bf16 values).
+//   silu'(g) = (1/2)(1 + tanh(g/2) + g / (2 cosh^2(g/2))), split off for |g| < 2^-10;
+//            = 1 + (1 - sigma)(g sigma - 1), split off where that term is < 2^-10 (g > 2).
+__device__ __noinline__ uint32_t dsilu_times_f64(float gf, float df, float uf) {
+    const double g = gf, f = (double)df * (double)uf;
+    if (fabs(g) < 0x1p-10) {
+        const double ch = cosh(0.5 * g);
+        return bf16_scaled_f64(f * 0.5, tanh(0.5 * g) + g / (2.0 * ch * ch), g > 0.0 ? 1 : (g < 0.0 ? -1 : 0));
+    }
+    double sig, om;
+    sigma_f64(g, sig, om);
+    const double c = om * (g * sig - 1.0);
+    if (g > 2.0 && fabs(c) < 0x1p-10) return bf16_scaled_f64(f, c, 1);
+    return bf16_rne_f64(f * (sig * (1.0 + g * om)));
+}
+
+// Distance, in fp32 ulps, from v to the nearest bf16 rounding midpoint: the
+// bits below the bf16 mantissa against 0x8000.
+__device__ __forceinline__ float midpoint_distance(float v) {
+    const uint32_t low = __float_as_uint(v) & 0xFFFFu;
+    return (float)(low > 0x8000u ? low - 0x8000u : 0x8000u - low);
+}
+
+// bf16(silu(g) * f).  fp32: e = expf(-g) (a few ulps), 1 + e, 1/(1+e), g*sigma,
+// *f: relative error < 2^-19, i.e. < 32 fp32 ulps of the result; accepted when
+// the result is more than 64 ulps from a midpoint.
+__device__ __forceinline__ uint32_t silu_times(float g, float f) {
+    if (fabsf(g) <= 80.0f) {
+        const float e = expf(-g);
+        const float sig = 1.0f / (1.0f + e);
+        const float v = (g * sig) * f;
+        if (midpoint_distance(v) > 64.0f) return f32_to_bf16_rne(v) & 0xFFFFu;
+    }
+    return silu_times_f64(g, f);
+}
+
+// bf16(silu'(g) * d * u), silu' = sigma (1 + t), t = g (1 - sigma), 1 - sigma = e sigma.
+// The fp32 error of 1 + t is < |t| 2^-20 + 2^-24 absolute (t carries the expf
+// and three roundings), so the relative error of the result is below
+// (|t| 2^-20) / |1 + t| + 2^-19; accepted when the distance to a midpoint
+// exceeds twice that bound in fp32 ulps.  f = d * u (two bf16 values, 16
+// significant bits) is exact in fp32 unless it falls below 2^-134.
+__device__ __forceinline__ uint32_t dsilu_times(float g, float d, float u) {
+    const float f = d * u;
+    if (fabsf(g) <= 80.0f && (f == 0.0f || fabsf(f) >= 0x1p-134f)) {
+        const float e = expf(-g);
+        const float sig = 1.0f / (1.0f + e);
+        const float t = g * (e * sig);
+        const float s1 = 1.0f + t;
+        const float v = (sig * s1) * f;
+        const float rel = fabsf(t) * 0x1p-20f / fabsf(s1) + 0x1p-19f;
+        if (rel < 0x1p-10f && midpoint_distance(v) > 2.0f * rel * 0x1p24f + 16.0f)
+            return f32_to_bf16_rne(v) & 0xFFFFu;
+    }
+    return dsilu_times_f64(g, d, u);
+}
+
+__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// RN codes of four values times inv (the quantizers' cast).
+__device__ __forceinline__ uint32_t codes4(const float* v, float inv) {
+    return e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Forward.  A block of 256 threads covers 64 rows and one 128-column tile b of
+// H (G tile b, U tile F/128 + b); 16 lanes per row, 8 columns per lane, so a
+// row's three 1x128 tiles (G, U, H) each reduce with one DPP max over 16 lanes.
+// ---------------------------------------------------------------------------
+constexpr int kSwRows = 64;
+
+__global__ __launch_bounds__(256) void k_swiglu_fwd(
+    const uint16_t* __restrict__ gu, int64_t R, int64_t F, int64_t ldgu, float amax_floor,
+    uint8_t* __restrict__ q_gu, int64_t ldq_gu, float* __restrict__ s_gu, int64_t lds_gu,
+    uint8_t* __restrict__ q_h, int64_t ldq_h, float* __restrict__ s_h, int64_t lds_h,
+    uint16_t* __restrict__ h_out, int64_t ldh)
+{
+    const int lane16 = threadIdx.x & 15;
+    const int grp = threadIdx.x >> 4;
+    const int64_t b = blockIdx.y;
+    const int64_t c = b * kTile + lane16 * 8;          // column in H and G; U at F + c
+    const int64_t nb = F / kTile;
+    for (int it = 0; it < 4; ++it) {
+        const int64_t r = (int64_t)blockIdx.x * kSwRows + grp + 16 * it;
+        const bool ok = r < R;
+        const uint4 wg = ok ? ld16(gu + r * ldgu + c) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 wu = ok ? ld16(gu + r * ldgu + F + c) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t g2[4] = {wg.x, wg.y, wg.z, wg.w}, u2[4] = {wu.x, wu.y, wu.z, wu.w};
+        float g[8], u[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            g[2 * k] = bf16_lo(g2[k]); g[2 * k + 1] = bf16_hi(g2[k]);
+            u[2 * k] = bf16_lo(u2[k]); u[2 * k + 1] = bf16_hi(u2[k]);
+        }
+        // the stash: 1x128 tiles b (G) and nb + b (U) of [G | U]
+        if (q_gu != nullptr) {
+            uint32_t mg = 0, mu = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                mg = max(mg, __float_as_uint(g[k]) & 0x7FFFFFFFu);
+                mu = max(mu, __float_as_uint(u[k]) & 0x7FFFFFFFu);
+            }
+            mg = max16(mg);
+            mu = max16(mu);
+            float sg, ig, su, iu;
+            tile_scale(fmaxf(__uint_as_float(mg), amax_floor), sg, ig);
+            tile_scale(fmaxf(__uint_as_float(mu), amax_floor), su, iu);
+            if (ok) {
+                st8(q_gu + r * ldq_gu + c, make_uint2(codes4(g, ig), codes4(g + 4, ig)));
+                st8(q_gu + r * ldq_gu + F + c, make_uint2(codes4(u, iu), codes4(u + 4, iu)));
+                if (lane16 == 0) {
+                    s_gu[b * lds_gu + r] = sg;
+                    s_gu[(nb + b) * lds_gu + r] = su;
+                }
+            }
+        }
+        // H = bf16(silu(G) U), then its 1x128 tile b
+        uint32_t hb[8];
+        float hv[8];
+        uint32_t mh = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            hb[k] = silu_times(g[k], u[k]);
+            hv[k] = bf16_value(hb[k]);
+            mh = max(mh, __float_as_uint(hv[k]) & 0x7FFFFFFFu);
+        }
+        mh = max16(mh);
+        float sh, ih;
+        tile_scale(fmaxf(__uint_as_float(mh), amax_floor), sh, ih);
+        if (ok) {
+            st8(q_h + r * ldq_h + c, make_uint2(codes4(hv, ih), codes4(hv + 4, ih)));
+            if (lane16 == 0) s_h[b * lds_h + r] = sh;
+            if (h_out != nullptr)
+                st16(h_out + r * ldh + c, make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
+                                                     hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward.  A block of 256 threads covers 128 rows and one 128-column gate
+// tile j and produces two output tiles, dG (columns 128j..) and dU
+// (F + 128j..), one after the other.  For each: phase 1 forms the tile's bf16
+// values row by row (thread t: rows r0 + 8*(t/16) + i, columns 8*(t%16) ..+8)
+// into a 128 x 128 bf16 tile in LDS; phase 2 reads back the thread's 8 x 8
+// patch and quantizes it both ways: 1x128 (row maxima: one DPP max per
+// 16-lane row group) and 128x1 (column maxima: lane swizzles plus LDS; codes
+// transposed through LDS so every qT store is a 16-byte piece of a 128-byte
+// row).  Phase 1 keeps only one row of inputs live, so the fp64 fallback can
+// be a call.
+// ---------------------------------------------------------------------------
+constexpr int kSwTr = 136;   // bytes per staged qT row
+
+__global__ __launch_bounds__(256) void k_swiglu_bwd(
+    const uint8_t* __restrict__ q_gu, int64_t R, int64_t F, int64_t ldq_gu,
+    const float* __restrict__ s_gu, int64_t lds_gu,
+    const uint16_t* __restrict__ dh, int64_t lddh, float amax_floor,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ sT, int64_t ldsT,
+    uint16_t* __restrict__ dgu, int64_t lddgu)
+{
+    __shared__ uint32_t red[4][kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kSwTr];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[kTile * kTile];   // the tile's bf16 values
+
+    const int t = threadIdx.x;
+    const int cg = t & 15, rg = t >> 4, wave = t >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * kTile;
+    const int64_t j = blockIdx.y;
+    const int64_t nb = F / kTile;
+    const int64_t cc = j * kTile + cg * 8;             // gate column; up column F + cc
+
+    for (int half = 0; half < 2; ++half) {
+        const int64_t oc0 = (half == 0 ? 0 : F) + j * kTile;      // first output column of the tile
+        const int64_t tile = (half == 0 ? 0 : nb) + j;            // its 1x128 block index
+
+        // phase 1: G~ = bf16(fl32(dec(q) s)), U~ likewise, dH; the tile's values
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + rg * 8 + i;
+            const bool ok = r < R;
+            const uint2 cgw = ok ? ld8(q_gu + r * ldq_gu + cc) : make_uint2(0u, 0u);
+            const float sg = ok ? s_gu[j * lds_gu + r] : 0.0f;
+            const uint4 dw = ok ? ld16(dh + r * lddh + cc) : make_uint4(0u, 0u, 0u, 0u);
+            const float2 g0 = e4m3x2_decode<false>(cgw.x), g1 = e4m3x2_decode<true>(cgw.x);
+            const float2 g2 = e4m3x2_decode<false>(cgw.y), g3 = e4m3x2_decode<true>(cgw.y);
+            const float gd[8] = {g0.x, g0.y, g1.x, g1.y, g2.x, g2.y, g3.x, g3.y};
+            const uint32_t dd[4] = {dw.x, dw.y, dw.z, dw.w};
+            uint32_t w[4];
+            if (half == 0) {
+                const uint2 cuw = ok ? ld8(q_gu + r * ldq_gu + F + cc) : make_uint2(0u, 0u);
+                const float su = ok ? s_gu[(nb + j) * lds_gu + r] : 0.0f;
+                const float2 u0 = e4m3x2_decode<false>(cuw.x), u1 = e4m3x2_decode<true>(cuw.x);
+                const float2 u2 = e4m3x2_decode<false>(cuw.y), u3 = e4m3x2_decode<true>(cuw.y);
+                const float ud[8] = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint32_t a = dsilu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk] * sg)), bf16_lo(dd[kk]),
+                                                   bf16_value(f32_to_bf16_rne(ud[2 * kk] * su)));
+                    const uint32_t b = dsilu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk + 1] * sg)), bf16_hi(dd[kk]),
+                                                   bf16_value(f32_to_bf16_rne(ud[2 * kk + 1] * su)));
+                    w[kk] = a | (b << 16);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint32_t a = silu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk] * sg)), bf16_lo(dd[kk]));
+                    const uint32_t b = silu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk + 1] * sg)), bf16_hi(dd[kk]));
+                    w[kk] = a | (b << 16);
+                }
+            }
+            *reinterpret_cast<uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (dgu != nullptr && ok) st16(dgu + r * lddgu + oc0 + cg * 8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        __syncthreads();
+
+        // phase 2: the thread's patch back from LDS, quantized both ways
+        float v[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
+            v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x); v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
+            v[i][4] = bf16_lo(w.z); v[i][5] = bf16_hi(w.z); v[i][6] = bf16_lo(w.w); v[i][7] = bf16_hi(w.w);
+        }
+        // 128x1: column maxima over the block's 128 rows
+        uint32_t mc[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+            m = max(m, shfl_xor_u32(m, 16));
+            m = max(m, shfl_xor_u32(m, 32));
+            mc[k] = m;
+        }
+        if ((t & 63) < 16) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) red[wave][cg * 8 + k] = mc[k];
+        }
+        __syncthreads();
+        float inv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int col = cg * 8 + k;
+            const uint32_t m = max(max(red[0][col], red[1][col]), max(red[2][col], red[3][col]));
+            float sc;
+            tile_scale(fmaxf(__uint_as_float(m), amax_floor), sc, inv[k]);
+            if (rg == 0) sT[(int64_t)blockIdx.x * ldsT + oc0 + cg * 8 + k] = sc;
+        }
+        // 1x128: each row's tile is the block's 128 columns of that row
+        float s_own = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+            m = max16(m);
+            float sc, iv;
+            tile_scale(fmaxf(__uint_as_float(m), amax_floor), sc, iv);
+            if (cg == i) s_own = sc;
+            const int64_t r = r0 + rg * 8 + i;
+            if (r < R) st8(q + r * ldq + oc0 + cg * 8, make_uint2(codes4(v[i], iv), codes4(v[i] + 4, iv)));
+        }
+        {
+            const int64_t rr = r0 + rg * 8 + cg;
+            if (cg < 8 && rr < R) s[tile * lds + rr] = s_own;
+        }
+        // transposed codes through LDS: column k of the patch -> 8 row bytes
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
+            const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
+            *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = p * 32 + (t >> 3);
+            const int seg = t & 7;
+            const uint2 a = *reinterpret_cast<const uint2*>(&tr[row * kSwTr + seg * 16]);
+            const uint2 bq = *reinterpret_cast<const uint2*>(&tr[row * kSwTr + seg * 16 + 8]);
+            st16(qT + (oc0 + row) * ldqT + r0 + seg * 16, make_uint4(a.x, a.y, bq.x, bq.y));
+        }
+        __syncthreads();                                   // red and tr are reused by the second tile
+    }
+}
+
+hipError_t launch_swiglu_fwd(const uint16_t* gu, int64_t R, int64_t F, int64_t ldgu, float amax_floor,
+                             uint8_t* q_gu, int64_t ldq_gu, float* s_gu, int64_t lds_gu,
+                             uint8_t* q_h, int64_t ldq_h, float* s_h, int64_t lds_h,
+                             uint16_t* h, int64_t ldh, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((R + kSwRows - 1) / kSwRows), (unsigned)(F / kTile));
+    hipLaunchKernelGGL(k_swiglu_fwd, grid, dim3(256), 0, stream, gu, R, F, ldgu, amax_floor,
+                       q_gu, ldq_gu, s_gu, lds_gu, q_h, ldq_h, s_h, lds_h, h, ldh);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const uint8_t* q_gu, int64_t R, int64_t F, int64_t ldq_gu,
+                             const float* s_gu, int64_t lds_gu, const uint16_t* dh, int64_t lddh,
+                             float amax_floor, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                             uint16_t* dgu, int64_t lddgu, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)(F / kTile));
+    hipLaunchKernelGGL(k_swiglu_bwd, grid, dim3(256), 0, stream, q_gu, R, F, ldq_gu, s_gu, lds_gu,
+                       dh, lddh, amax_floor, q, ldq, s, lds, qT, ldqT, sT, ldsT, dgu, lddgu);
+    return hipGetLastError();
+}
+
+}  // namespace fgb

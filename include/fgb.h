@@ -182,6 +182,48 @@ int fgb_quantize_128x128_sr(const uint16_t* w, int64_t K, int64_t N, int64_t ldw
                             float* s, uint64_t seed, uint32_t salt, void* stream);
 
 /* ------------------------------------------------------------------------
+ * SwiGLU with its casts fused ([scratch], section "What is asserted, and
+ * from where": the SwiGLU input is saved as E4M3; a cast rides the nearest
+ * vector kernel -- the SwiGLU forward emits the down projection's E4M3
+ * operand, the SwiGLU backward emits the gate/up projection's dgrad and
+ * wgrad operands in both tile orientations -- and the backward computes in
+ * BF16 from the dequantized E4M3 input).
+ *
+ * The gate/up output is ONE bf16 tensor gu [R][2F] (ldgu >= 2F): G is
+ * columns 0..F-1, U columns F..2F-1; F % 128 == 0 so no tile straddles the
+ * two halves.  silu(g) = g / (1 + exp(-g)).  Every bf16 result below is the
+ * exact real value rounded ONCE to bf16 (to nearest, ties to even); the
+ * quantizations are exactly fgb_quantize_1x128 / fgb_quantize_128x1 of the
+ * bf16 tensors named.  Inputs and results must be finite.
+ * ---------------------------------------------------------------------- */
+
+/* Forward: H = bf16(silu(G) * U) [R][F].  Writes the 1x128 stash of gu
+ * (q_gu [R][2F], s_gu [2F/128][lds_gu >= R]; both NULL to skip), the 1x128
+ * codes and scales of H (q_h [R][F] with ldq_h >= F, s_h [F/128][lds_h >= R])
+ * and H itself (h [R][ldh >= F], 16-byte aligned; NULL to skip). */
+int fgb_swiglu_fwd_quant(const uint16_t* gu, int64_t R, int64_t F, int64_t ldgu,
+                         float amax_floor,
+                         uint8_t* q_gu, int64_t ldq_gu, float* s_gu, int64_t lds_gu,
+                         uint8_t* q_h, int64_t ldq_h, float* s_h, int64_t lds_h,
+                         uint16_t* h, int64_t ldh, void* stream);
+
+/* Backward, from the stash (q_gu [R][2F], s_gu [2F/128][lds_gu >= R], as
+ * written by the forward) and dH [R][F] (bf16, 16-byte aligned):
+ *   G~ = bf16(fl32(dec(q_gu[r][c]) * s_gu)), U~ likewise (columns F + c);
+ *   dG = bf16(dH * U~ * silu'(G~)), dU = bf16(dH * silu(G~)),
+ *   silu'(g) = sigma(g) (1 + g (1 - sigma(g))), sigma(g) = 1 / (1 + exp(-g)).
+ * Writes [dG | dU] [R][2F] quantized both ways: 1x128 (q [R][ldq >= 2F],
+ * s [2F/128][lds >= R]) and 128x1 (qT [2F][ldqT >= roundup(R,128)] zero
+ * padded, sT [ceil(R/128)][ldsT >= 2F]), and optionally [dG | dU] itself
+ * (dgu [R][lddgu >= 2F], 16-byte aligned; NULL to skip). */
+int fgb_swiglu_bwd_quant(const uint8_t* q_gu, int64_t R, int64_t F, int64_t ldq_gu,
+                         const float* s_gu, int64_t lds_gu,
+                         const uint16_t* dh, int64_t lddh, float amax_floor,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                         uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                         uint16_t* dgu, int64_t lddgu, void* stream);
+
+/* ------------------------------------------------------------------------
  * Power-of-two scales ([po2]).  Each quantizer above has a _ue8m0 twin with
  * the same arguments and layouts whose scales are powers of two:
  *     e = the smallest integer with 448 * 2^e >= a, clamped to [-127, 127]

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = fgb.lib()
     names = header_functions()
-    assert len(names) == 28
+    assert len(names) == 30
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fgb.SIGNATURES)
@@ -200,3 +200,36 @@ def test_stochastic_rounding_validation():
     assert L.fgb_quantize_128x128_sr(A, 256, 256, 256, 0.0, P(0), 256, P(0), 256, D, seed, salt, None) == E_NULL
     with pytest.raises(fgb.FgbError):
         fgb._quant_call("fgb_quantize_1x128", True, (1, 2), (A, 1, 8, 8, 0.0, B, 8, C_, 1, None))
+
+
+def test_swiglu_validation():
+    L = fgb.lib()
+
+    def fwd(R=256, F=256, gu=A, ldgu=512, fl=0.0, qg=B, ldqg=512, sg=C_, ldsg=256, qh=D, ldqh=256, sh=C_, ldsh=256,
+            h=P(0), ldh=0):
+        return L.fgb_swiglu_fwd_quant(gu, R, F, ldgu, fl, qg, ldqg, sg, ldsg, qh, ldqh, sh, ldsh, h, ldh, None)
+
+    assert fwd(F=200) == E_SHAPE
+    assert fwd(R=-1) == E_SHAPE
+    assert fwd(ldgu=256) == E_LD
+    assert fwd(gu=MIS) == E_ALIGN
+    assert fwd(qg=P(0)) == E_NULL                        # stash codes without scales
+    assert fwd(qh=P(0)) == E_NULL
+    assert fwd(ldqh=128) == E_LD
+    assert fwd(h=MIS, ldh=256) == E_ALIGN
+    assert fwd(fl=-1.0) == E_ARG
+    assert fwd(R=0, gu=P(0), qh=P(0), sh=P(0)) == OK
+
+    def bwd(R=256, F=256, qg=A, ldqg=512, sg=B, ldsg=256, dh=C_, lddh=256, fl=0.0, q=D, ldq=512, s=B, lds=256,
+            qT=A, ldqT=256, sT=B, ldsT=512, dgu=P(0), lddgu=0):
+        return L.fgb_swiglu_bwd_quant(qg, R, F, ldqg, sg, ldsg, dh, lddh, fl, q, ldq, s, lds, qT, ldqT, sT, ldsT,
+                                      dgu, lddgu, None)
+
+    assert bwd(F=100) == E_SHAPE
+    assert bwd(qg=P(0)) == E_NULL
+    assert bwd(lddh=128) == E_LD
+    assert bwd(ldqT=200) == E_LD
+    assert bwd(ldsT=256) == E_LD
+    assert bwd(qT=P(0x10008)) == E_ALIGN
+    assert bwd(dgu=MIS, lddgu=512) == E_ALIGN
+    assert bwd(F=0, qg=P(0)) == OK

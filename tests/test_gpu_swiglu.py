@@ -1,0 +1,138 @@
+"""GPU SwiGLU with fused casts against the CPU oracle: H, [dG | dU], every code
+and every scale bit pattern identical (padding included).  Every finite bf16
+gate value is covered in both directions (which exercises the fp32 fast path,
+the fp64 fallback near bf16 rounding midpoints, tiny gates whose g*u/2 ties are
+broken by the tanh correction, and gates beyond |g| = 80), then ragged shapes
+and one GPU's share of the MoE expert tensors."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_amd as fgb
+from fine_grained_block_amd import workloads as wl
+
+from parity import assert_codes_equal, assert_scales_equal, bf16_dev, f32_dev, host, u8_dev
+
+pytestmark = pytest.mark.gpu
+T = 128
+
+
+def finite_bf16():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return b[(b & 0x7F80) != 0x7F80]
+
+
+def bits(t):
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def check_fwd(orc, gu, name):
+    q_gu, s_gu, q_h, s_h, h = fgb.swiglu_fwd_quant(bf16_dev(gu), want_h=True)
+    oq_gu, os_gu, oq_h, os_h, oh = orc.swiglu_fwd_quant(gu)
+    hb = bits(h)
+    if not np.array_equal(hb, oh):
+        bad = np.argwhere(hb != oh)
+        i = tuple(bad[0])
+        raise AssertionError(f"{name}: {len(bad)} H values differ; first at {i}: gpu {hb[i]:#06x} oracle {oh[i]:#06x}")
+    assert_codes_equal(q_h, oq_h, f"{name} q_h")
+    assert_scales_equal(s_h, os_h, f"{name} s_h")
+    assert_codes_equal(q_gu, oq_gu, f"{name} q_gu")
+    assert_scales_equal(s_gu, os_gu, f"{name} s_gu")
+    return q_gu, s_gu
+
+
+def check_bwd(orc, q_gu, s_gu, dh, name):
+    q, s, qT, sT, dgu = fgb.swiglu_bwd_quant(u8_dev(q_gu), f32_dev(s_gu), bf16_dev(dh), want_dgu=True)
+    odgu, oq, os_, oqT, osT = orc.swiglu_bwd_quant(q_gu, s_gu, dh)
+    db = bits(dgu)
+    if not np.array_equal(db, odgu):
+        bad = np.argwhere(db != odgu)
+        i = tuple(bad[0])
+        raise AssertionError(f"{name}: {len(bad)} dG/dU values differ; first at {i}: "
+                             f"gpu {db[i]:#06x} oracle {odgu[i]:#06x}")
+    assert_codes_equal(q, oq, f"{name} q")
+    assert_scales_equal(s, os_, f"{name} s")
+    assert_codes_equal(qT, oqT, f"{name} qT")
+    assert_scales_equal(sT, osT, f"{name} sT")
+
+
+def test_forward_every_finite_gate(orc):
+    g = finite_bf16()                                   # 65280 values = 255 rows of 256
+    F = 256
+    G = g.reshape(-1, F)
+    rng = np.random.default_rng(1)
+    for name, U in [("u=1", np.full_like(G, 0x3F80)),
+                    ("u random", wl.bf16_bits((rng.standard_normal(G.shape) *
+                                               np.exp(rng.uniform(-8, 8, G.shape))).astype(np.float32)))]:
+        gu = np.concatenate([G, U], axis=1)
+        # keep H finite: drop rows whose |g*u| could overflow bf16
+        gf = torch.from_numpy(G.view(np.int16)).view(torch.bfloat16).float().numpy()
+        uf = torch.from_numpy(U.view(np.int16)).view(torch.bfloat16).float().numpy()
+        ok = np.all(np.abs(gf.astype(np.float64) * uf) < 1e38, axis=1)
+        check_fwd(orc, np.ascontiguousarray(gu[ok]), f"fwd every gate {name}")
+
+
+def test_backward_every_finite_gate(orc):
+    """Stash codes 1.0 with per-row scales equal to every finite bf16 value make G~
+    take each of them; U~ = 1 or 37, dH = 1 or random."""
+    g = finite_bf16()
+    gf = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).float().numpy()
+    R, F = g.size, 128
+    q = np.zeros((R, 2 * F), np.uint8)
+    q[:, :] = 0x38
+    s = np.zeros((2, R), np.float32)
+    s[0] = gf
+    s[1] = 37.0
+    rng = np.random.default_rng(2)
+    dh = wl.bf16_bits((rng.standard_normal((R, F)) * 1e-3).astype(np.float32))
+    dh[:, 0] = 0x3F80
+    check_bwd(orc, q, s, dh, "bwd every gate")
+
+
+def test_backward_zero_gate_ties():
+    """silu'(0) = 1/2: dH*U~/2 = 130.5 -> 130 and 133.5 -> 134 (ties to even)."""
+    R, F = 2, 128
+    q = np.zeros((R, 2 * F), np.uint8)
+    q[:, F] = 0x38
+    s = np.zeros((2, R), np.float32)
+    s[0] = 1.0
+    s[1] = [29.0, 89.0]
+    dh = np.zeros((R, F), np.uint16)
+    dh[:, 0] = [0x4110, 0x4040]
+    *_, dgu = fgb.swiglu_bwd_quant(u8_dev(q), f32_dev(s), bf16_dev(dh), want_dgu=True)
+    assert list(bits(dgu)[:, 0]) == [0x4302, 0x4306]
+
+
+@pytest.mark.parametrize("R,F", [(1, 128), (3, 256), (130, 128), (257, 384), (64, 1024)])
+def test_ragged_round_trip(orc, R, F):
+    rng = np.random.default_rng(R * 7 + F)
+    gu = wl.bf16_bits((rng.standard_normal((R, 2 * F)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32))
+    gu[:, :3] = 0
+    gu[0, 5] = 0x8000                                   # -0 gate
+    q_gu, s_gu = check_fwd(orc, gu, f"fwd {R}x{F}")
+    dh = wl.bf16_bits((rng.standard_normal((R, F)) * 1e-3).astype(np.float32))
+    check_bwd(orc, host(q_gu), host(s_gu), dh, f"bwd {R}x{F}")
+
+
+def test_stash_optional_and_strided(orc):
+    rng = np.random.default_rng(9)
+    R, F = 200, 256
+    big = wl.bf16_bits(rng.standard_normal((R, 2 * F + 64)).astype(np.float32))
+    gu = big[:, :2 * F]
+    gud = bf16_dev(big)[:, :2 * F]
+    q_gu, s_gu, q_h, s_h, h = fgb.swiglu_fwd_quant(gud, stash=False)
+    assert q_gu is None and s_gu is None and h is None
+    _, _, oq_h, os_h, _ = orc.swiglu_fwd_quant(gu)
+    assert_codes_equal(q_h, oq_h, "strided q_h")
+    assert_scales_equal(s_h, os_h, "strided s_h")
+
+
+def test_moe_share(orc):
+    """One GPU's MoE gate/up output, 8192 routed rows x [2048 | 2048], heavy-tailed
+    gates; forward then backward with dH ~ N(0, 1e-3)."""
+    rng = np.random.default_rng(4)
+    R, F = 8192, 2048
+    gu = wl.bf16_bits((rng.standard_t(3, (R, 2 * F)) * 2.0).astype(np.float32))
+    q_gu, s_gu = check_fwd(orc, gu, "moe fwd")
+    dh = wl.bf16_bits((rng.standard_normal((R, F)) * 1e-3).astype(np.float32))
+    check_bwd(orc, host(q_gu), host(s_gu), dh, "moe bwd")
