@@ -21,9 +21,10 @@ matrix core applies itself (no vector-ALU rescale).
 `--rounding sr` quantizes X, W and dY with stochastic rounding (one Philox
 word per element); the requant of the saved X stays round-to-nearest.
 
-`--workload moe_grouped` times the grouped expert GEMMs of one GPU's MoE share
-instead (32 experts, 8192 tokens routed top-8, gate/up and down projections,
-forward and backward); `value` then counts the routed rows' GEMM FLOP.
+`--workload moe_grouped` times one GPU's MoE expert share as a SwiGLU FFN
+instead (32 experts, 8192 tokens routed top-8; gate/up and down projections,
+forward and backward, with the SwiGLU casts fused into the SwiGLU kernels);
+`value` then counts the routed rows' GEMM FLOP.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload W] [--no-cpu-baseline]
 """
@@ -84,7 +85,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", choices=["linear_dsv3_attn", "moe_grouped"], default="linear_dsv3_attn",
                    help="linear_dsv3_attn (default): the DeepSeek-V3 attention projection's linear; "
-                        "moe_grouped: the grouped expert GEMMs of one GPU's MoE share (no CPU baseline)")
+                        "moe_grouped: one GPU's MoE expert share as a SwiGLU FFN, fwd+bwd (no CPU baseline)")
     p.add_argument("--recipe", choices=["fp32", "ue8m0"], default="fp32",
                    help="fp32: scales absmax/448 (default); ue8m0: power-of-two scales, applied by the matrix core")
     p.add_argument("--rounding", choices=["rn", "sr"], default="rn",
@@ -177,13 +178,17 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False):
 
 
 def moe_step(fgb, torch, dev, d):
-    """The grouped expert GEMMs of one GPU's MoE share, both projections (gate/up
-    d_model -> 2*d_ff, down d_ff -> d_model), forward and backward.  GEMM work
-    counts the routed rows only (padding rows are computed but not counted);
+    """One GPU's MoE expert share as a full SwiGLU FFN step, forward and backward:
+    quantize X and the expert weights, gate/up Fprop -> [G | U], SwiGLU forward
+    (emits the E4M3 stash of [G | U] and H's 1x128 codes), down Fprop; quantize dY
+    both ways, down Dgrad -> dH, requant H, down Wgrad, SwiGLU backward (emits
+    [dG | dU] in both tile orientations), gate/up Dgrad, requant X, gate/up Wgrad.
+    GEMM work counts the routed rows only (padding rows are computed, not counted);
     weight quantization is one launch per expert."""
     import numpy as np
     E, R = d["E"], d["R_pad"]
     rows = int(np.sum(d["loads"]))
+    Dm, F2, F = d["d_model"], d["d_ff2"], d["d_ff"]
     od = torch.from_numpy(np.asarray(d["offsets"], np.int32)).to(dev)
 
     def to_dev(bits):
@@ -191,46 +196,72 @@ def moe_step(fgb, torch, dev, d):
 
     u8 = dict(dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = []
-    for tag, xin, wts, dyin, K, N in [("up", "x", "w_up", "dy_up", d["d_model"], d["d_ff2"]),
-                                       ("down", "h", "w_down", "dy_down", d["d_ff"], d["d_model"])]:
-        x, dy = to_dev(d[xin]), to_dev(d[dyin])
-        w = to_dev(d[wts])                                   # [E, K, N]
-        b = {
-            "qx": torch.empty((R, K), **u8), "sx": torch.empty((K // T, R), **f32),
-            "qw": torch.empty((E, K, N), **u8), "qwT": torch.empty((E, N, K), **u8),
-            "sw": torch.empty((E, K // T, N // T), **f32),
-            "y": torch.empty((R, N), dtype=torch.bfloat16, device=dev),
-            "qdy": torch.empty((R, N), **u8), "sdy": torch.empty((N // T, R), **f32),
-            "dx": torch.empty((R, K), dtype=torch.bfloat16, device=dev),
-            "qdyT": torch.empty((N, R), **u8), "sdyT": torch.empty((R // T, N), **f32),
-            "qxT": torch.empty((K, R), **u8), "sxT": torch.empty((R // T, K), **f32),
-            "dw": torch.empty((E, K, N), **f32),
-        }
-        ab = algorithmic_bytes(R, K, N)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    x, dy = to_dev(d["x"]), to_dev(d["dy_down"])
+    w_up, w_down = to_dev(d["w_up"]), to_dev(d["w_down"])
+    Rt = R // T
+    b = {
+        "qx": torch.empty((R, Dm), **u8), "sx": torch.empty((Dm // T, R), **f32),
+        "qxT": torch.empty((Dm, R), **u8), "sxT": torch.empty((Rt, Dm), **f32),
+        "qwu": torch.empty((E, Dm, F2), **u8), "qwuT": torch.empty((E, F2, Dm), **u8),
+        "swu": torch.empty((E, Dm // T, F2 // T), **f32),
+        "qwd": torch.empty((E, F, Dm), **u8), "qwdT": torch.empty((E, Dm, F), **u8),
+        "swd": torch.empty((E, F // T, Dm // T), **f32),
+        # padding rows of a GEMM output stay zero (the grouped GEMMs compute them as 0)
+        "gu": torch.zeros((R, F2), **bf),
+        "q_gu": torch.empty((R, F2), **u8), "s_gu": torch.empty((F2 // T, R), **f32),
+        "q_h": torch.empty((R, F), **u8), "s_h": torch.empty((F // T, R), **f32),
+        "q_hT": torch.empty((F, R), **u8), "s_hT": torch.empty((Rt, F), **f32),
+        "y": torch.empty((R, Dm), **bf),
+        "qdy": torch.empty((R, Dm), **u8), "sdy": torch.empty((Dm // T, R), **f32),
+        "qdyT": torch.empty((Dm, R), **u8), "sdyT": torch.empty((Rt, Dm), **f32),
+        "dh": torch.zeros((R, F), **bf),
+        "q_dgu": torch.empty((R, F2), **u8), "s_dgu": torch.empty((F2 // T, R), **f32),
+        "q_dguT": torch.empty((F2, R), **u8), "s_dguT": torch.empty((Rt, F2), **f32),
+        "dx": torch.empty((R, Dm), **bf),
+        "dw_up": torch.empty((E, Dm, F2), **f32), "dw_down": torch.empty((E, F, Dm), **f32),
+    }
 
-        def quant_w(w=w, b=b):
-            for e in range(E):
-                fgb.quantize_128x128(w[e], q=b["qw"][e], qT=b["qwT"][e], s=b["sw"][e])
+    def quant_w(w, q, qT, s):
+        for e in range(E):
+            fgb.quantize_128x128(w[e], q=q[e], qT=qT[e], s=s[e])
 
-        flop = {"flop": 2.0 * rows * K * N}
-        out += [
-            (f"{tag}.quantize_1x128_x", lambda x=x, b=b: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]),
-             {"bytes": ab["quantize_1x128_x"]}),
-            (f"{tag}.quantize_128x128_w", quant_w, {"bytes": E * ab["quantize_128x128_w"]}),
-            (f"{tag}.gemm_fprop_grouped",
-             lambda b=b: fgb.gemm_fprop_grouped(od, b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"]), flop),
-            (f"{tag}.quantize_dual_dy",
-             lambda dy=dy, b=b: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
-             {"bytes": ab["quantize_dual_dy"]}),
-            (f"{tag}.gemm_dgrad_grouped",
-             lambda b=b: fgb.gemm_dgrad_grouped(od, b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"]), flop),
-            (f"{tag}.requant_128x1_x", lambda b=b: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
-             {"bytes": ab["requant_128x1_x"]}),
-            (f"{tag}.gemm_wgrad_grouped",
-             lambda b=b: fgb.gemm_wgrad_grouped(od, b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], dw=b["dw"]), flop),
-        ]
-    return out
+    up = {"flop": 2.0 * rows * Dm * F2}
+    down = {"flop": 2.0 * rows * F * Dm}
+    nb2, nb1 = F2 // T, F // T
+    swf_bytes = R * F2 * 2 + R * F2 + 4 * R * nb2 + R * F + 4 * R * nb1
+    swb_bytes = R * F2 + 4 * R * nb2 + R * F * 2 + R * F2 + 4 * R * nb2 + F2 * R + 4 * Rt * F2
+    ab_x = algorithmic_bytes(R, Dm, F2)
+    ab_h = algorithmic_bytes(R, F, Dm)
+    return [
+        ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]), {"bytes": ab_x["quantize_1x128_x"]}),
+        ("quantize_128x128_w_up", lambda: quant_w(w_up, b["qwu"], b["qwuT"], b["swu"]),
+         {"bytes": E * algorithmic_bytes(R, Dm, F2)["quantize_128x128_w"]}),
+        ("gemm_fprop_grouped_up", lambda: fgb.gemm_fprop_grouped(od, b["qx"], b["sx"], b["qwuT"], b["swu"], y=b["gu"]),
+         up),
+        ("swiglu_fwd_quant", lambda: fgb.swiglu_fwd_quant(b["gu"], q_gu=b["q_gu"], s_gu=b["s_gu"], q_h=b["q_h"],
+                                                          s_h=b["s_h"]), {"bytes": swf_bytes}),
+        ("quantize_128x128_w_down", lambda: quant_w(w_down, b["qwd"], b["qwdT"], b["swd"]),
+         {"bytes": E * algorithmic_bytes(R, F, Dm)["quantize_128x128_w"]}),
+        ("gemm_fprop_grouped_down", lambda: fgb.gemm_fprop_grouped(od, b["q_h"], b["s_h"], b["qwdT"], b["swd"],
+                                                                   y=b["y"]), down),
+        ("quantize_dual_dy", lambda: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
+         {"bytes": ab_h["quantize_dual_dy"]}),
+        ("gemm_dgrad_grouped_down", lambda: fgb.gemm_dgrad_grouped(od, b["qdy"], b["sdy"], b["qwd"], b["swd"],
+                                                                   dx=b["dh"]), down),
+        ("requant_128x1_h", lambda: fgb.requant_128x1(b["q_h"], b["s_h"], qT=b["q_hT"], sT=b["s_hT"]),
+         {"bytes": algorithmic_bytes(R, F, Dm)["requant_128x1_x"]}),
+        ("gemm_wgrad_grouped_down", lambda: fgb.gemm_wgrad_grouped(od, b["q_hT"], b["s_hT"], b["qdyT"], b["sdyT"],
+                                                                   dw=b["dw_down"]), down),
+        ("swiglu_bwd_quant", lambda: fgb.swiglu_bwd_quant(b["q_gu"], b["s_gu"], b["dh"], q=b["q_dgu"], s=b["s_dgu"],
+                                                          qT=b["q_dguT"], sT=b["s_dguT"]), {"bytes": swb_bytes}),
+        ("gemm_dgrad_grouped_up", lambda: fgb.gemm_dgrad_grouped(od, b["q_dgu"], b["s_dgu"], b["qwu"], b["swu"],
+                                                                 dx=b["dx"]), up),
+        ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
+         {"bytes": ab_x["requant_128x1_x"]}),
+        ("gemm_wgrad_grouped_up", lambda: fgb.gemm_wgrad_grouped(od, b["qxT"], b["sxT"], b["q_dguT"], b["s_dguT"],
+                                                                 dw=b["dw_up"]), up),
+    ]
 
 
 def main():
@@ -263,10 +294,11 @@ def main():
     else:
         d = wl.moe_grouped()
         kernels = moe_step(fgb, torch, dev, d)
-        config = {"workload": "moe_grouped fwd+bwd, one GPU's expert share: 32 experts, 8192 tokens top-8 "
-                              "(Zipf 1.1 loads, 3 empty), W_up [7168,4096], W_down [2048,7168] per expert",
+        config = {"workload": "moe_grouped SwiGLU FFN fwd+bwd, one GPU's expert share: 32 experts, 8192 tokens "
+                              "top-8 (Zipf 1.1 loads, 3 empty), W_gate/up [7168,2x2048], W_down [2048,7168] per "
+                              "expert, SwiGLU casts fused",
                   "experts": d["E"], "routed_rows": int(np.sum(d["loads"])), "R_pad": d["R_pad"]}
-        data = "synthetic (seeded N(0,1) X and H, N(0,0.02) W, N(0,1e-3) dY; bf16)"
+        data = "synthetic (seeded N(0,1) X, N(0,0.02) W, N(0,1e-3) dY; bf16)"
         del d
         args.no_cpu_baseline = True
 

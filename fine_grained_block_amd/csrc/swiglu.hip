@@ -114,41 +114,51 @@ __device__ __forceinline__ float midpoint_distance(float v) {
     return (float)(low > 0x8000u ? low - 0x8000u : 0x8000u - low);
 }
 
-// bf16(silu(g) * f).  fp32: e = expf(-g) (a few ulps), 1 + e, 1/(1+e), g*sigma,
-// *f: relative error < 2^-19, i.e. < 32 fp32 ulps of the result; accepted when
-// the result is more than 64 ulps from a midpoint.
-__device__ __forceinline__ uint32_t silu_times(float g, float f) {
-    if (fabsf(g) <= 80.0f) {
-        const float e = expf(-g);
-        const float sig = 1.0f / (1.0f + e);
-        const float v = (g * sig) * f;
-        if (midpoint_distance(v) > 64.0f) return f32_to_bf16_rne(v) & 0xFFFFu;
-    }
-    return silu_times_f64(g, f);
+// fp32 fast paths.  Errors in units of 2^-23 relative (one fp32 ulp at most):
+// expf <= 2 (its documented bound is 1), v_rcp_f32 <= 1, each IEEE add or
+// multiply <= 1/2.  A result is accepted when its distance to the nearest bf16
+// midpoint, in fp32 ulps of the result (at most 2^24 per unit relative error),
+// exceeds twice its error bound; otherwise the fp64 path decides.
+constexpr uint32_t kNeedF64 = 0xFFFFFFFFu;    // "not decided in fp32"
+
+// silu(g) * f: e (2) -> 1 + e (2.5) -> rcp (3.5) -> * g (4) -> * f (4.5 units
+// = 9 ulps of the result); accepted beyond 24 ulps.
+__device__ __forceinline__ uint32_t silu_times_fast(float g, float f) {
+    if (!(fabsf(g) <= 80.0f)) return kNeedF64;
+    const float e = expf(-g);
+    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
+    const float v = (g * sig) * f;
+    return midpoint_distance(v) > 24.0f ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
 }
 
-// bf16(silu'(g) * d * u), silu' = sigma (1 + t), t = g (1 - sigma), 1 - sigma = e sigma.
-// The fp32 error of 1 + t is < |t| 2^-20 + 2^-24 absolute (t carries the expf
-// and three roundings), so the relative error of the result is below
-// (|t| 2^-20) / |1 + t| + 2^-19; accepted when the distance to a midpoint
-// exceeds twice that bound in fp32 ulps.  f = d * u (two bf16 values, 16
-// significant bits) is exact in fp32 unless it falls below 2^-134.
-__device__ __forceinline__ uint32_t dsilu_times(float g, float d, float u) {
+// silu'(g) * d * u = sigma (1 + t) f, t = g e sigma, f = d u (exact in fp32 for
+// |f| >= 2^-134: 16 significant bits).  t carries <= 5 units, so 1 + t has an
+// absolute error <= 5 |t| + 1/2 units and the result a relative error
+// <= 8 (1 + |t| / |1 + t|) units (<= 2^-20 (1 + |t|/|1+t|)); accepted beyond
+// twice that in ulps, plus 8.
+__device__ __forceinline__ uint32_t dsilu_times_fast(float g, float d, float u) {
     const float f = d * u;
-    if (fabsf(g) <= 80.0f && (f == 0.0f || fabsf(f) >= 0x1p-134f)) {
-        const float e = expf(-g);
-        const float sig = 1.0f / (1.0f + e);
-        const float t = g * (e * sig);
-        const float s1 = 1.0f + t;
-        const float v = (sig * s1) * f;
-        const float rel = fabsf(t) * 0x1p-20f / fabsf(s1) + 0x1p-19f;
-        if (rel < 0x1p-10f && midpoint_distance(v) > 2.0f * rel * 0x1p24f + 16.0f)
-            return f32_to_bf16_rne(v) & 0xFFFFu;
-    }
-    return dsilu_times_f64(g, d, u);
+    if (!(fabsf(g) <= 80.0f) || !(f == 0.0f || fabsf(f) >= 0x1p-134f)) return kNeedF64;
+    const float e = expf(-g);
+    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
+    const float t = g * (e * sig);
+    const float s1 = 1.0f + t;
+    const float v = (sig * s1) * f;
+    const float ratio = fabsf(t) * __builtin_amdgcn_rcpf(fabsf(s1)) * 1.0001f;
+    if (!(ratio < 1024.0f)) return kNeedF64;
+    const float margin = 2.0f * 0x1p-20f * (1.0f + ratio) * 0x1p24f + 8.0f;
+    return midpoint_distance(v) > margin ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
+}
+
+__device__ __forceinline__ uint32_t silu_times(float g, float f) {
+    const uint32_t r = silu_times_fast(g, f);
+    return r != kNeedF64 ? r : silu_times_f64(g, f);
 }
 
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// E4M3 code -> its value (exact).
+__device__ __forceinline__ float e4m3_decode1(uint8_t code) { return e4m3x2_decode<false>((uint32_t)code).x; }
 
 // RN codes of four values times inv (the quantizers' cast).
 __device__ __forceinline__ uint32_t codes4(const float* v, float inv) {
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
 // ---------------------------------------------------------------------------
 constexpr int kSwTr = 136;   // bytes per staged qT row
 
-__global__ __launch_bounds__(256) void k_swiglu_bwd(
+__global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
     const uint8_t* __restrict__ q_gu, int64_t R, int64_t F, int64_t ldq_gu,
     const float* __restrict__ s_gu, int64_t lds_gu,
     const uint16_t* __restrict__ dh, int64_t lddh, float amax_floor,
@@ -269,45 +279,80 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(
         const int64_t oc0 = (half == 0 ? 0 : F) + j * kTile;      // first output column of the tile
         const int64_t tile = (half == 0 ? 0 : nb) + j;            // its 1x128 block index
 
-        // phase 1: G~ = bf16(fl32(dec(q) s)), U~ likewise, dH; the tile's values
+        // phase 1: G~ = bf16(fl32(dec(q) s)), U~ likewise, dH; the tile's values.
+        // 1a: four rows at a time, their raw inputs first, then every value whose
+        // fp32 form decides its bf16 rounding; `need` marks the others (bit 8 i + k).
+        uint64_t need = 0;
 #pragma unroll 1
-        for (int i = 0; i < 8; ++i) {
-            const int64_t r = r0 + rg * 8 + i;
-            const bool ok = r < R;
-            const uint2 cgw = ok ? ld8(q_gu + r * ldq_gu + cc) : make_uint2(0u, 0u);
-            const float sg = ok ? s_gu[j * lds_gu + r] : 0.0f;
-            const uint4 dw = ok ? ld16(dh + r * lddh + cc) : make_uint4(0u, 0u, 0u, 0u);
-            const float2 g0 = e4m3x2_decode<false>(cgw.x), g1 = e4m3x2_decode<true>(cgw.x);
-            const float2 g2 = e4m3x2_decode<false>(cgw.y), g3 = e4m3x2_decode<true>(cgw.y);
-            const float gd[8] = {g0.x, g0.y, g1.x, g1.y, g2.x, g2.y, g3.x, g3.y};
-            const uint32_t dd[4] = {dw.x, dw.y, dw.z, dw.w};
-            uint32_t w[4];
-            if (half == 0) {
-                const uint2 cuw = ok ? ld8(q_gu + r * ldq_gu + F + cc) : make_uint2(0u, 0u);
-                const float su = ok ? s_gu[(nb + j) * lds_gu + r] : 0.0f;
-                const float2 u0 = e4m3x2_decode<false>(cuw.x), u1 = e4m3x2_decode<true>(cuw.x);
-                const float2 u2 = e4m3x2_decode<false>(cuw.y), u3 = e4m3x2_decode<true>(cuw.y);
-                const float ud[8] = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
+        for (int i0 = 0; i0 < 8; i0 += 4) {
+            uint2 cgw[4], cuw[4];
+            uint4 dw[4];
+            float sg[4], su[4];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const uint32_t a = dsilu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk] * sg)), bf16_lo(dd[kk]),
-                                                   bf16_value(f32_to_bf16_rne(ud[2 * kk] * su)));
-                    const uint32_t b = dsilu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk + 1] * sg)), bf16_hi(dd[kk]),
-                                                   bf16_value(f32_to_bf16_rne(ud[2 * kk + 1] * su)));
-                    w[kk] = a | (b << 16);
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const uint32_t a = silu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk] * sg)), bf16_lo(dd[kk]));
-                    const uint32_t b = silu_times(bf16_value(f32_to_bf16_rne(gd[2 * kk + 1] * sg)), bf16_hi(dd[kk]));
-                    w[kk] = a | (b << 16);
-                }
+            for (int ii = 0; ii < 4; ++ii) {
+                const int64_t r = r0 + rg * 8 + i0 + ii;
+                const bool ok = r < R;
+                cgw[ii] = ok ? ld8(q_gu + r * ldq_gu + cc) : make_uint2(0u, 0u);
+                dw[ii] = ok ? ld16(dh + r * lddh + cc) : make_uint4(0u, 0u, 0u, 0u);
+                sg[ii] = ok ? s_gu[j * lds_gu + r] : 0.0f;
+                cuw[ii] = (half == 0 && ok) ? ld8(q_gu + r * ldq_gu + F + cc) : make_uint2(0u, 0u);
+                su[ii] = (half == 0 && ok) ? s_gu[(nb + j) * lds_gu + r] : 0.0f;
             }
-            *reinterpret_cast<uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]) = make_uint4(w[0], w[1], w[2], w[3]);
-            if (dgu != nullptr && ok) st16(dgu + r * lddgu + oc0 + cg * 8, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = i0 + ii;
+                const float2 g0 = e4m3x2_decode<false>(cgw[ii].x), g1 = e4m3x2_decode<true>(cgw[ii].x);
+                const float2 g2 = e4m3x2_decode<false>(cgw[ii].y), g3 = e4m3x2_decode<true>(cgw[ii].y);
+                const float gd[8] = {g0.x, g0.y, g1.x, g1.y, g2.x, g2.y, g3.x, g3.y};
+                const float2 u0 = e4m3x2_decode<false>(cuw[ii].x), u1 = e4m3x2_decode<true>(cuw[ii].x);
+                const float2 u2 = e4m3x2_decode<false>(cuw[ii].y), u3 = e4m3x2_decode<true>(cuw[ii].y);
+                const float ud[8] = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
+                const uint32_t dd[4] = {dw[ii].x, dw[ii].y, dw[ii].z, dw[ii].w};
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float g = bf16_value(f32_to_bf16_rne(gd[k] * sg[ii]));
+                    const float d = (k & 1) ? bf16_hi(dd[k >> 1]) : bf16_lo(dd[k >> 1]);
+                    uint32_t r;
+                    if (half == 0) r = dsilu_times_fast(g, d, bf16_value(f32_to_bf16_rne(ud[k] * su[ii])));
+                    else r = silu_times_fast(g, d);
+                    if (r == kNeedF64) {
+                        need |= 1ull << (8 * i + k);
+                        r = 0;
+                    }
+                    if (k & 1) w[k >> 1] |= r << 16;
+                    else w[k >> 1] = r;
+                }
+                *reinterpret_cast<uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        // 1b: the marked values in fp64, one at a time
+        while (need != 0) {
+            const int idx = __builtin_ctzll(need);
+            need &= need - 1;
+            const int i = idx >> 3, k = idx & 7;
+            const int64_t r = r0 + rg * 8 + i;          // marked values lie in valid rows
+            const float g = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + cc + k]) * s_gu[j * lds_gu + r]));
+            const float d = bf16_value(dh[r * lddh + cc + k]);
+            uint32_t v;
+            if (half == 0) {
+                const float u = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + F + cc + k]) *
+                                                           s_gu[(nb + j) * lds_gu + r]));
+                v = dsilu_times_f64(g, d, u);
+            } else {
+                v = silu_times_f64(g, d);
+            }
+            vt[(rg * 8 + i) * kTile + cg * 8 + k] = (uint16_t)v;
         }
         __syncthreads();
+        if (dgu != nullptr) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t r = r0 + rg * 8 + i;
+                const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
+                if (r < R) st16(dgu + r * lddgu + oc0 + cg * 8, w);
+            }
+        }
 
         // phase 2: the thread's patch back from LDS, quantized both ways
         float v[8][8];
