@@ -5,6 +5,7 @@ Usage: ``python -m fine_grained_block_amd.build`` or ``build_library()``.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -30,12 +31,38 @@ COMMON_FLAGS = [
 ]
 
 
+# Sources whose kernels must not use scratch memory: a spilled register in the
+# GEMM main loop is reloaded with a vector-memory load whose wait also drains
+# the in-flight direct-to-LDS prefetch, so a spill is a build error there.
+NO_SCRATCH = {"gemm.hip"}
+
+
+def _scratch_users(remarks: str) -> list:
+    """Kernels with a non-zero ScratchSize in hipcc's resource-usage remarks."""
+    users, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
+
+
 def _compile(src: str, build_dir: str) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SCRATCH else []
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if src in NO_SCRATCH:
+        bad = _scratch_users(r.stderr)
+        if bad:
+            os.remove(obj)
+            raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {bad}")
     return obj
 
 

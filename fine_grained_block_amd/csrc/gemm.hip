@@ -11,6 +11,9 @@
 // chain never spans more than one 128-block, and dequantization plus the
 // running sum happen in FP32 on the vector ALUs.
 
+#include <type_traits>
+#include <utility>
+
 #include "device_common.hpp"
 #include "fgb_internal.hpp"
 
@@ -21,7 +24,8 @@ namespace fgb {
 // accumulator VGPRs of a wave fit beside its fragments).  Per 128-block the A
 // and B slices (32 KB each) and the block's scales are brought into LDS by
 // direct-to-LDS 16-byte loads, double buffered: the loads of block kb+1 are in
-// flight while block kb is computed.
+// flight while block kb is computed, and on the vector-rescale path they are
+// issued one every other MFMA step of block kb's computation.
 // ===========================================================================
 constexpr int kTM = 256;                           // output rows per block tile
 constexpr int kStageA = kTM * kTile;               // 32 KB
@@ -32,24 +36,52 @@ constexpr int kV1Threads = 512;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // Direct-to-LDS loads (global_load_lds): 64 lanes x 16 B (or x 4 B) land at
-// consecutive addresses from the wave-uniform LDS byte address `lds`.  Issued
-// from inline assembly so that the compiler's wait insertion does not treat the
-// in-flight loads as pending writes to every LDS location (which would make
-// every LDS read wait for the prefetch); the kernel waits for each stage itself
-// with vmcnt.  M0 carries the LDS address and is restored afterwards.
-__device__ __forceinline__ void dma16(const void* g, const uint8_t* lds) {
-    const uint32_t a = (uint32_t)(uintptr_t)((const lds_u8*)lds);
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(g), "s"(a) : "memory");
+// consecutive addresses from the wave-uniform LDS byte address `lds`; the
+// global address is the wave-uniform `base` (an SGPR pair) plus the lane's
+// 32-bit byte offset.  Issued from inline assembly so that the compiler's wait
+// insertion does not treat the in-flight loads as pending writes to every LDS
+// location (which would make every LDS read wait for the prefetch); the kernel
+// waits for each stage itself with vmcnt.  M0 carries the LDS address and is
+// restored afterwards.  The "memory" clobber keeps LDS accesses from moving
+// across the issue; the _nc forms, used inside the computation for the stage
+// that it does not read, leave the compiler free to schedule around them (the
+// next barrier orders them).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* lds) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_u8*)lds));
 }
-__device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
-    const uint32_t a = (uint32_t)(uintptr_t)((const lds_u8*)lds);
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, const uint8_t* lds) {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(g), "s"(a) : "memory");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, const uint8_t* lds) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ void dma16_nc(const void* base, uint32_t off, const uint8_t* lds) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)));
+}
+__device__ __forceinline__ void dma4_nc(const void* base, uint32_t off, const uint8_t* lds) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)));
+}
+
+// Calls f(integral_constant<int, t>) for t = 0 .. N-1, so that every index
+// derived from t is a compile-time constant.
+template <int... ts, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, ts...>, F&& f) {
+    (f(std::integral_constant<int, ts>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
 // Staged row r keeps its eight 16-byte chunks at slots c ^ swz(r), swz(r) =
@@ -64,14 +96,13 @@ __device__ __forceinline__ void dma4(const void* g, const uint8_t* lds) {
 // serves every fragment.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ v8i frag_swz(const uint8_t* stage_rows, int row, int g) {
-    // 32 bytes = chunks 2g and 2g+1 of staged row `row`
-    const int sw = swz(row);
-    const uint4 lo = *reinterpret_cast<const uint4*>(stage_rows + row * kTile + (((2 * g) ^ sw) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(stage_rows + row * kTile + (((2 * g + 1) ^ sw) << 4));
+// A fragment from its two 16-byte chunks at lo + off and hi + off.
+__device__ __forceinline__ v8i frag_at(const uint8_t* lo, const uint8_t* hi, int off) {
+    const uint4 l = *reinterpret_cast<const uint4*>(lo + off);
+    const uint4 h = *reinterpret_cast<const uint4*>(hi + off);
     v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    r[0] = (int)l.x; r[1] = (int)l.y; r[2] = (int)l.z; r[3] = (int)l.w;
+    r[4] = (int)h.x; r[5] = (int)h.y; r[6] = (int)h.z; r[7] = (int)h.w;
     return r;
 }
 
@@ -270,29 +301,33 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     // ---- load plan: A rows in 32 groups of 8, B rows in TN/8 groups; group q is
     // loaded by wave q % 8 with one direct-to-LDS instruction.  Lane -> staged
     // row r = 8*q + lane/8 at slot lane&7, which holds source chunk
-    // (lane&7) ^ swz(r); 32-bit byte offsets from the operand base.
+    // (lane&7) ^ swz(r); 32-bit byte offsets from the operand base (operands are
+    // cut below 4 GiB on the host).
     constexpr int NB = (TN / 8 + 7) / 8;            // B groups per wave (upper bound)
+    constexpr int NL = 4 + NB + 1;                  // load instructions per wave and block
     uint32_t a_off[4], b_off[NB];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = (wave + 8 * i) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(r);
         int64_t ar = m0 + r; ar = ar < mend ? ar : mend - 1;
-        a_off[i] = (uint32_t)(ar * g.lda) + chunk * 16;
+        a_off[i] = (uint32_t)ar * (uint32_t)g.lda + (uint32_t)(chunk * 16);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int r = (wave + 8 * i) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(r);
         int64_t br = n0 + r; br = br < g.N ? br : g.N - 1;
-        b_off[i] = (uint32_t)(br * g.ldb) + chunk * 16;
+        b_off[i] = (uint32_t)br * (uint32_t)g.ldb + (uint32_t)(chunk * 16);
     }
     // Scales.  Waves 0..3 stage SA, permuted so that a lane fetches the scales of
     // its row in all MI row pieces with MI/4 16-byte reads: float p of the SA
     // area holds row WTM*h + 16*i + q for p = WTM*h + 64*(i>>2) + 4*q + (i&3).
-    // Waves 4..7 stage SB: the column scales (Wgrad), or (Fprop/Dgrad) in floats
-    // 0..3 the scales of the weight tiles floor(n0/128) + 0..3 that the block's
-    // columns can touch.
+    // Waves 4..7 stage SB: the column scales (Wgrad), or (Fprop/Dgrad) in word
+    // SBW*c + j the weight-tile scale of piece j of wave column c, so that a wave
+    // reads the scales of its NJ pieces from consecutive words.
+    constexpr int SBW = NJ <= 4 ? 4 : 8;            // SB words per wave column
+    static_assert(S::WAVES_N * SBW <= 16, "per-piece weight scales fit 16 words");
     const float* s_base;
     int64_t s_kb;
     uint32_t s_off;
@@ -307,22 +342,39 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             int64_t c = n0 + sidx; c = c < g.N ? c : g.N - 1;
             s_base = sbp; s_kb = g.sb_kb; s_off = (uint32_t)c;
         } else {
-            int64_t t = n0 / kTile + (lane & 3);
+            const int w = lane & 15;
+            const int pc = w / SBW, pj = w % SBW < NJ ? w % SBW : NJ - 1;
+            int64_t t = (n0 + 16 * (pc * NJ + pj)) / kTile;
             const int64_t tmax = (g.N + kTile - 1) / kTile - 1;
             t = t < tmax ? t : tmax;
-            s_base = sbp; s_kb = g.sb_kb; s_off = (uint32_t)(t * g.sb_n);
+            s_base = sbp; s_kb = g.sb_kb; s_off = (uint32_t)t * (uint32_t)g.sb_n;
         }
     }
 
-    auto issue = [&](int64_t kb, uint8_t* sbase) {
-        const uint8_t* A = g.A + kb * kTile;
-        const uint8_t* B = Bp + kb * kTile;
+    // Load k (0 <= k < NL) of block kb into the stage at sbase.  SPREAD: issued
+    // from inside the computation; B groups past b_rows are then loaded anyway
+    // (from clamped, valid rows into staged rows no fragment read touches), so
+    // that no branch splits the computation.
+    auto issue_one = [&](int k, int64_t kb, uint8_t* sbase, auto spread) __attribute__((always_inline)) {
+        constexpr bool SP = decltype(spread)::value;
+        if (k < 4) {
+            const uint8_t* A = g.A + kb * kTile;
+            if constexpr (SP) dma16_nc(A, a_off[k], sbase + (wave + 8 * k) * 8 * kTile);
+            else dma16(A, a_off[k], sbase + (wave + 8 * k) * 8 * kTile);
+        } else if (k < 4 + NB) {
+            const int i = k - 4;
+            const uint8_t* B = Bp + kb * kTile;
+            if constexpr (SP) dma16_nc(B, b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
+            else if ((wave + 8 * i) * 8 < b_rows) dma16(B, b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
+        } else {
+            const float* sp = s_base + kb * s_kb;
+            if constexpr (SP) dma4_nc(sp, s_off * 4u, sbase + kStageA + kStageB + wave * 256);
+            else dma4(sp, s_off * 4u, sbase + kStageA + kStageB + wave * 256);
+        }
+    };
+    auto issue = [&](int64_t kb, uint8_t* sbase) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(A + a_off[i], sbase + (wave + 8 * i) * 8 * kTile);
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-            if ((wave + 8 * i) * 8 < b_rows) dma16(B + b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
-        dma4(s_base + kb * s_kb + s_off, sbase + kStageA + kStageB + wave * 256);
+        for (int k = 0; k < NL; ++k) issue_one(k, kb, sbase, std::false_type{});
     };
 
     v4f acc[MI][NJ];
@@ -332,23 +384,37 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int frow = lane & 15, fg = lane >> 4;
-    const int tile0 = (int)(n0 / kTile);
+    // Byte offsets, from a stage's start, of a lane's two 16-byte chunks in its
+    // first A and first B fragment row; later fragments are 16 rows (2 KB) on,
+    // and the second chunk sits in slot (first ^ 1), i.e. at offset ^ 16.
+    const uint32_t fo_lo = (uint32_t)(((2 * fg) ^ swz(frow)) << 4);
+    const uint32_t a_lo = (uint32_t)((wm * WTM + frow) * kTile) + fo_lo, a_hi = a_lo ^ 16u;
+    const uint32_t b_lo = (uint32_t)(kStageA + (wn * WTN + frow) * kTile) + fo_lo, b_hi = b_lo ^ 16u;
 
     // One 128-block: MI*NJ MFMAs in a flat schedule where step t issues MFMA t
     // and folds the partial of MFMA t-2 (a ring of four partials), so no fold
     // waits on a result still in the matrix pipeline.  The operands of the first
     // MFMA are requested first.  The shorter side's fragments (B for TN = 256,
     // A for TN = 224) stay in registers for the whole block; the other side's
-    // stream two pieces ahead through a ring of three.
+    // stream two pieces ahead through a ring of three.  With a next block
+    // (NEXT), its load k is issued at step 1 + 2k.
     constexpr bool ROW_MAJOR = MI >= NJ;           // steps walk columns inside a row piece
     constexpr int NH = ROW_MAJOR ? NJ : MI;        // held fragments
     constexpr int NS = ROW_MAJOR ? MI : NJ;        // streamed fragments
-    auto compute = [&](const uint8_t* sA) {
-        const uint8_t* sB = sA + kStageA;
-        const float* sSA = reinterpret_cast<const float*>(sB + kStageB);
+    constexpr int T = MI * NJ;
+    constexpr int PER = ROW_MAJOR ? NJ : MI;       // steps per streamed fragment
+    // (Wgrad without the half-tile split: loads at steps 0 .. NL-1, which keeps
+    // that instantiation within 256 VGPRs without spilling)
+    constexpr bool kDense1 = OUTER && !SPLIT;
+    constexpr int kSpreadFirst = kDense1 ? 0 : 1, kSpreadEvery = kDense1 ? 1 : 2;
+    static_assert(kSpreadFirst + kSpreadEvery * (NL - 1) < T, "every spread load falls on a step");
+    auto compute = [&](const uint8_t* sA, uint8_t* nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next)::value;
+        const float* sSA = reinterpret_cast<const float*>(sA + kStageA + kStageB);
         const float* sSB = sSA + 4 * 64;           // region of wave 4 onwards
-        auto afrag = [&](int i) { return frag_swz(sA, wm * WTM + i * 16 + frow, fg); };
-        auto bfrag = [&](int j) { return frag_swz(sB, wn * WTN + j * 16 + frow, fg); };
+        const uint8_t *pal = sA + a_lo, *pah = sA + a_hi, *pbl = sA + b_lo, *pbh = sA + b_hi;
+        auto afrag = [&](int i) { return frag_at(pal, pah, i * 16 * kTile); };
+        auto bfrag = [&](int j) { return frag_at(pbl, pbh, j * 16 * kTile); };
         auto held = [&](int h) { return ROW_MAJOR ? bfrag(h) : afrag(h); };
         auto streamed = [&](int q) { return ROW_MAJOR ? afrag(q) : bfrag(q); };
 
@@ -371,8 +437,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
                 const float4 t = *reinterpret_cast<const float4*>(sSB + wn * WTN + j * 16 + fg * 4);
                 c[0] = t.x; c[1] = t.y; c[2] = t.z; c[3] = t.w;
             } else {
-                // weight tile of this 16-column piece (pieces never straddle 128)
-                c[0] = sSB[(int)((n0 + wn * WTN + j * 16) / kTile) - tile0];
+                c[0] = sSB[wn * SBW + j];
             }
         };
         float cs[ROW_MAJOR ? NJ : 1][4];
@@ -402,21 +467,22 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             if constexpr (ROW_MAJOR) return cs[t % NJ];
             else return cbuf[(t / MI) & 1];
         };
-        constexpr int T = MI * NJ;
-        constexpr int PER = ROW_MAJOR ? NJ : MI;       // steps per streamed fragment
         static_assert(ROW_MAJOR || MI >= 3, "column-major walk needs >= 3 row pieces");
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int q = t / PER, h = t % PER;        // streamed piece, held piece
-            if (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
+        static_for<T>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int q = t / PER, h = t % PER;        // streamed piece, held piece
+            if constexpr (NEXT && t >= kSpreadFirst && (t - kSpreadFirst) % kSpreadEvery == 0 &&
+                          (t - kSpreadFirst) / kSpreadEvery < NL)
+                issue_one((t - kSpreadFirst) / kSpreadEvery, kbn, nxt, std::true_type{});
+            if constexpr (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
             // piece q-1's last fold runs at step q*PER + 1, so its scale slot is
             // free from step q*PER + 2 on: load piece q+1's scales there
-            if (!ROW_MAJOR && h == 2 && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
+            if constexpr (!ROW_MAJOR && h == 2 && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
             P[t & 3] = ROW_MAJOR
                 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], zero, 0, 0, 0, 0, 0, 0)
                 : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], zero, 0, 0, 0, 0, 0, 0);
-            if (t >= 2) fold(t - 2, scales_of_step(t - 2));
-        }
+            if constexpr (t >= 2) fold(t - 2, scales_of_step(t - 2));
+        });
         fold(T - 2, scales_of_step(T - 2));
         fold(T - 1, scales_of_step(T - 1));
     };
@@ -424,13 +490,14 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     // Power-of-two scales: one MFMA per 16x16 piece and block, accumulating
     // through C; the scale operand of a lane is the exponent field (the E8M0
     // byte) of its fragment row's scale: B rows are output columns 16j + frow,
-    // A rows are output rows 16i + frow.
-    auto compute_po2 = [&](const uint8_t* sA) {
-        const uint8_t* sB = sA + kStageA;
-        const float* sSA = reinterpret_cast<const float*>(sB + kStageB);
+    // A rows are output rows 16i + frow.  Loads of the next block as above.
+    auto compute_po2 = [&](const uint8_t* sA, uint8_t* nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next)::value;
+        const float* sSA = reinterpret_cast<const float*>(sA + kStageA + kStageB);
         const float* sSB = sSA + 4 * 64;
-        auto afrag = [&](int i) { return frag_swz(sA, wm * WTM + i * 16 + frow, fg); };
-        auto bfrag = [&](int j) { return frag_swz(sB, wn * WTN + j * 16 + frow, fg); };
+        const uint8_t *pal = sA + a_lo, *pah = sA + a_hi, *pbl = sA + b_lo, *pbh = sA + b_hi;
+        auto afrag = [&](int i) { return frag_at(pal, pah, i * 16 * kTile); };
+        auto bfrag = [&](int j) { return frag_at(pbl, pbh, j * 16 * kTile); };
         auto held = [&](int h) { return ROW_MAJOR ? bfrag(h) : afrag(h); };
         auto streamed = [&](int q) { return ROW_MAJOR ? afrag(q) : bfrag(q); };
         v8i hf[NH];
@@ -451,36 +518,45 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             if constexpr (OUTER)
                 eb[j] = (int)(__float_as_uint(sSB[wn * WTN + j * 16 + frow]) >> 23);
             else
-                eb[j] = (int)(__float_as_uint(sSB[(int)((n0 + wn * WTN + j * 16) / kTile) - tile0]) >> 23);
+                eb[j] = (int)(__float_as_uint(sSB[wn * SBW + j]) >> 23);
         }
-        constexpr int T = MI * NJ;
-        constexpr int PER = ROW_MAJOR ? NJ : MI;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int q = t / PER, h = t % PER;
-            if (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
-            const int i = ROW_MAJOR ? q : h, j = ROW_MAJOR ? h : q;
+        static_for<T>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int q = t / PER, h = t % PER;
+            if constexpr (NEXT && t >= kSpreadFirst && (t - kSpreadFirst) % kSpreadEvery == 0 &&
+                          (t - kSpreadFirst) / kSpreadEvery < NL)
+                issue_one((t - kSpreadFirst) / kSpreadEvery, kbn, nxt, std::true_type{});
+            if constexpr (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
+            constexpr int i = ROW_MAJOR ? q : h, j = ROW_MAJOR ? h : q;
             acc[i][j] = ROW_MAJOR
                 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], acc[i][j], 0, 0, 0, eb[j], 0, ea[i])
                 : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], acc[i][j], 0, 0, 0, eb[j], 0, ea[i]);
-        }
+        });
     };
 
     // K loop, one barrier per block: wait for this wave's loads of block kb, then
     // the barrier (all waves' loads of kb have landed, and all waves are done
-    // with block kb-1, so its stage can be refilled), then start the loads of
-    // kb+1 into that stage and compute kb while they fly.
-    if (kb1 > kb0) issue(kb0, smem);
-    for (int64_t kb = kb0; kb < kb1; ++kb) {
+    // with block kb-1, so its stage can be refilled).  Waves that compute issue
+    // the loads of kb+1 into that stage from inside the computation of kb; waves
+    // of a half-tile block that do not compute issue them at once.  The last
+    // block (no kb+1) is a separate instantiation without loads.
+    auto kstep = [&](int64_t kb, auto next) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next)::value;
         const int st = (int)((kb - kb0) & 1);
+        uint8_t* nxt = smem + (st ^ 1) * kStageBytes;
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of block kb
         lds_barrier();
-        if (kb + 1 < kb1) issue(kb + 1, smem + (st ^ 1) * kStageBytes);
         if (!SPLIT || active) {
-            if constexpr (PO2) compute_po2(smem + st * kStageBytes);
-            else compute(smem + st * kStageBytes);
+            if constexpr (PO2) compute_po2(smem + st * kStageBytes, nxt, kb + 1, next);
+            else compute(smem + st * kStageBytes, nxt, kb + 1, next);
+        } else if constexpr (NEXT) {
+            issue(kb + 1, nxt);
         }
-    }
+    };
+    if (kb1 > kb0) issue(kb0, smem);
+    int64_t kb = kb0;
+    for (; kb + 1 < kb1; ++kb) kstep(kb, std::true_type{});
+    if (kb < kb1) kstep(kb, std::false_type{});
     if (SPLIT && !active) return;
 
     // epilogue: row m0 + wm*WTM + 16*i + frow, columns n0 + wn*WTN + 16*j + 4*fg .. +3
