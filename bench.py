@@ -21,6 +21,15 @@ matrix core applies itself (no vector-ALU rescale).
 `--rounding sr` quantizes X, W and dY with stochastic rounding (one Philox
 word per element); the requant of the saved X stays round-to-nearest.
 
+`--schedule overlap` runs the casts that no GEMM waits for on a second HIP
+stream beside the GEMMs (quantize X beside quantize W; the dY casts and the X
+requant beside Fprop; in the MoE step the down weights' cast, the dY casts and
+both requants).  Every GEMM waits for the casts it reads, and a step's second
+stream waits for the previous step's GEMMs, so steps never overlap.  The
+default, `serial`, runs every kernel on one stream in the order above: beside
+a GEMM's blocks the casts get few CUs, and the cross-stream waits cost more
+than the overlap saves in the linear step.
+
 `--workload moe_grouped` times one GPU's MoE expert share as a SwiGLU FFN
 instead (32 experts, 8192 tokens routed top-8; gate/up and down projections,
 forward and backward, with the SwiGLU casts fused into the SwiGLU kernels);
@@ -97,6 +106,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, run a plain streaming kernel (1 GiB read, 1 GiB "
                         "written) three times: it scales rocprofv3's FETCH_SIZE/WRITE_SIZE to bytes")
+    p.add_argument("--schedule", choices=["serial", "overlap"], default="serial",
+                   help="serial (default): every kernel on one stream, in step order; "
+                        "overlap: casts that no GEMM waits for run on a second stream")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="Fprop/Dgrad output rows in the CPU-baseline sample (0 = auto, ~15 s of GEMM work)")
     return p.parse_args()
@@ -116,9 +128,11 @@ def algorithmic_bytes(M, K, N):
     }
 
 
-def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False):
-    """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work)
-    per kernel, work = {"flop": ...} or {"bytes": ...} (algorithmic)."""
+def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bufs=None):
+    """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work,
+    lane, deps) per kernel in issue order, work = {"flop": ...} or {"bytes": ...}
+    (algorithmic); lane 1 = the second stream, deps = kernels it reads the
+    output of (only waits across streams matter)."""
     import numpy as np
     M, K, N = d["M"], d["K"], d["N"]
 
@@ -139,6 +153,8 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False):
         "qxT": torch.empty((K, Mp), **u8), "sxT": torch.empty((Mp // T, K), **f32),
         "dw": torch.empty((K, N), **f32),
     }
+    if bufs is not None:
+        bufs.update(b)
     ab = algorithmic_bytes(M, K, N)
     flop = {"flop": 2.0 * M * N * K}
     # stochastic rounding: one (seed, salt) per step, a salt per tensor
@@ -170,14 +186,27 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False):
         ("gemm_wgrad", lambda: fgb.gemm_wgrad(b["qxT"], b["sxT"], b["qdyT"], b["sdyT"], M, dw=b["dw"], ue8m0=ue8m0),
          flop),
     ]
-    if ue8m0:
-        steps = [(name + "_ue8m0", fn, work) for name, fn, work in steps]
-    if sr:
-        steps = [(name + ("_sr" if name.startswith("quantize") else ""), fn, work) for name, fn, work in steps]
-    return steps
+    dy_names = [n for n, _, _ in dy_casts]
+    lanes = {"quantize_1x128_x": (1, []), "quantize_128x128_w": (0, []),
+             "gemm_fprop": (0, ["quantize_1x128_x", "quantize_128x128_w"]),
+             "gemm_dgrad": (0, dy_names + ["quantize_128x128_w"]),
+             "requant_128x1_x": (1, ["quantize_1x128_x"]),
+             "gemm_wgrad": (0, dy_names + ["requant_128x1_x"])}
+    for n in dy_names:
+        lanes[n] = (1, [])
+    # issue order: the casts ahead of the GEMM they hide behind
+    order = ["quantize_1x128_x", "quantize_128x128_w", "gemm_fprop"] + dy_names + \
+            ["requant_128x1_x", "gemm_dgrad", "gemm_wgrad"]
+    by = {name: (name, fn, work) for name, fn, work in steps}
+    steps = [by[n] + lanes[n] for n in order]
+
+    def rename(n):
+        n = n + "_ue8m0" if ue8m0 else n
+        return n + "_sr" if sr and n.startswith("quantize") else n
+    return [(rename(n), fn, work, lane, [rename(x) for x in deps]) for n, fn, work, lane, deps in steps]
 
 
-def moe_step(fgb, torch, dev, d):
+def moe_step(fgb, torch, dev, d, bufs=None):
     """One GPU's MoE expert share as a full SwiGLU FFN step, forward and backward:
     quantize X and the expert weights, gate/up Fprop -> [G | U], SwiGLU forward
     (emits the E4M3 stash of [G | U] and H's 1x128 codes), down Fprop; quantize dY
@@ -221,6 +250,8 @@ def moe_step(fgb, torch, dev, d):
         "dx": torch.empty((R, Dm), **bf),
         "dw_up": torch.empty((E, Dm, F2), **f32), "dw_down": torch.empty((E, F, Dm), **f32),
     }
+    if bufs is not None:
+        bufs.update(b)
 
     def quant_w(w, q, qT, s):
         for e in range(E):
@@ -233,7 +264,7 @@ def moe_step(fgb, torch, dev, d):
     swb_bytes = R * F2 + 4 * R * nb2 + R * F * 2 + R * F2 + 4 * R * nb2 + F2 * R + 4 * Rt * F2
     ab_x = algorithmic_bytes(R, Dm, F2)
     ab_h = algorithmic_bytes(R, F, Dm)
-    return [
+    steps = [
         ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"]), {"bytes": ab_x["quantize_1x128_x"]}),
         ("quantize_128x128_w_up", lambda: quant_w(w_up, b["qwu"], b["qwuT"], b["swu"]),
          {"bytes": E * algorithmic_bytes(R, Dm, F2)["quantize_128x128_w"]}),
@@ -262,6 +293,54 @@ def moe_step(fgb, torch, dev, d):
         ("gemm_wgrad_grouped_up", lambda: fgb.gemm_wgrad_grouped(od, b["qxT"], b["sxT"], b["q_dguT"], b["s_dguT"],
                                                                  dw=b["dw_up"]), up),
     ]
+    # second stream: the down weights' cast, the dY casts and the two requants
+    lanes = {"quantize_128x128_w_down": (1, []), "quantize_dual_dy": (1, []),
+             "requant_128x1_x": (1, ["quantize_1x128_x"]), "requant_128x1_h": (1, ["swiglu_fwd_quant"]),
+             "gemm_fprop_grouped_down": (0, ["quantize_128x128_w_down"]),
+             "gemm_dgrad_grouped_down": (0, ["quantize_dual_dy", "quantize_128x128_w_down"]),
+             "gemm_wgrad_grouped_down": (0, ["requant_128x1_h", "quantize_dual_dy"]),
+             "gemm_wgrad_grouped_up": (0, ["requant_128x1_x"])}
+    order = ["quantize_1x128_x", "quantize_128x128_w_up", "quantize_128x128_w_down", "gemm_fprop_grouped_up",
+             "swiglu_fwd_quant", "quantize_dual_dy", "requant_128x1_h", "requant_128x1_x",
+             "gemm_fprop_grouped_down", "gemm_dgrad_grouped_down", "gemm_wgrad_grouped_down", "swiglu_bwd_quant",
+             "gemm_dgrad_grouped_up", "gemm_wgrad_grouped_up"]
+    by = {name: (name, fn, work) for name, fn, work in steps}
+    assert sorted(order) == sorted(by)
+    return [by[n] + lanes.get(n, (0, [])) for n in order]
+
+
+def make_runner(torch, dev, kernels, overlap):
+    """step(events=None) launching `kernels` (name, fn, work, lane, deps) once.
+    overlap: lane-1 kernels go to a second stream (default priority); a kernel
+    waits for the events of its deps on the other stream; the second stream
+    first waits for everything the main stream has queued (the previous step),
+    and the main stream finally waits for the second.  events[i] = (start, end)
+    timing events recorded on kernel i's stream."""
+    main_s = torch.cuda.current_stream(dev)
+    side_s = torch.cuda.Stream(dev) if overlap else main_s
+    lane_of = {name: lane for name, _, _, lane, _ in kernels}
+    done = {name: torch.cuda.Event() for name, _, _, _, _ in kernels}
+
+    def step(events=None):
+        if overlap:
+            side_s.wait_stream(main_s)
+        for i, (name, fn, _, lane, deps) in enumerate(kernels):
+            s = side_s if overlap and lane == 1 else main_s
+            with torch.cuda.stream(s):
+                if overlap:
+                    for dname in deps:
+                        if lane_of[dname] != lane:
+                            s.wait_event(done[dname])
+                if events is not None:
+                    events[i][0].record(s)
+                fn()
+                if events is not None:
+                    events[i][1].record(s)
+                if overlap:
+                    done[name].record(s)
+        if overlap:
+            main_s.wait_stream(side_s)
+    return step
 
 
 def main():
@@ -302,19 +381,14 @@ def main():
         del d
         args.no_cpu_baseline = True
 
-    def step(events=None):
-        for i, (_, fn, _) in enumerate(kernels):
-            if events is not None:
-                events[i][0].record()
-            fn()
-            if events is not None:
-                events[i][1].record()
+    overlap = args.schedule == "overlap"
+    step = make_runner(torch, dev, kernels, overlap)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: per-kernel HIP events on the kernels' stream (torch's current stream)
+    # timed region: per-kernel HIP events on the stream each kernel runs on
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in kernels] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -327,8 +401,8 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
     per_kernel_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
-                     for i, (name, _, _) in enumerate(kernels)}
-    work = {name: w for name, _, w in kernels}
+                     for i, (name, _, _, _, _) in enumerate(kernels)}
+    work = {name: w for name, _, w, _, _ in kernels}
 
     step_flop = sum(w.get("flop", 0.0) for w in work.values())
     quant_bytes = sum(w.get("bytes", 0) for w in work.values())
@@ -350,7 +424,9 @@ def main():
                 "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(dom_rate / FP8_PEAK, 4),
                 "traffic": traffic_record(dom)}
     quant_ms = sum(v for k, v in per_kernel_ms.items() if "bytes" in work[k])
-    config.update({"gemm_flop_per_step": step_flop, "quant_bytes_per_step": quant_bytes})
+    config.update({"gemm_flop_per_step": step_flop, "quant_bytes_per_step": quant_bytes,
+                   "schedule": ("overlap: casts " + ", ".join(n for n, _, _, lane, _ in kernels if lane == 1)
+                                + " on a second stream") if overlap else "serial: one stream"})
 
     out = {
         "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak) + quant GB/s (% HBM) at 1 GPU",
