@@ -194,9 +194,8 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bu
              "gemm_wgrad": (0, dy_names + ["requant_128x1_x"])}
     for n in dy_names:
         lanes[n] = (1, [])
-    # issue order: the casts ahead of the GEMM they hide behind
     order = ["quantize_1x128_x", "quantize_128x128_w", "gemm_fprop"] + dy_names + \
-            ["requant_128x1_x", "gemm_dgrad", "gemm_wgrad"]
+            ["gemm_dgrad", "requant_128x1_x", "gemm_wgrad"]
     by = {name: (name, fn, work) for name, fn, work in steps}
     steps = [by[n] + lanes[n] for n in order]
 
