@@ -106,6 +106,7 @@ def _load():
     lib.orc_quantize_128x1_ue8m0.argtypes = [P, I64, I64, I64, F, P, I64, P, I64]
     lib.orc_quantize_128x128_ue8m0.argtypes = [P, I64, I64, I64, F, P, I64, P, I64, P]
     lib.orc_requant_128x1_ue8m0.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64]
+    lib.orc_requant_128x128_ue8m0.argtypes = [P, I64, I64, I64, P, F, P, I64, P, I64, P]
     lib.orc_gemm_block_scaled.argtypes = [I64, P, I64, P, I64, I64, I64,
                                           P, I64, P, I64, I64, I64,
                                           P, I64, P, I64, P, P]
@@ -295,6 +296,22 @@ def requant_128x1_ue8m0(q, e):
     eT = np.empty((_cdiv(R, TILE), C), np.uint8)
     _load().orc_requant_128x1_ue8m0(_ptr(q), R, C, C, _ptr(e), R, _ptr(qT), Rp, _ptr(eT), C)
     return qT, eT
+
+
+def requant_128x128_ue8m0(q, s, amax_floor: float = 0.0):
+    """Second stage of the two-stage weight cast: 128x128 E4M3 codes q [K, N]
+    with fp32 tile scales s [ceil(K/128), ceil(N/128)] (as quantize_128x128
+    returns them) -> (q2 [K, N], q2T [N, K], e [ceil(K/128), ceil(N/128)]):
+    v = fl32(dec(q) * s), then the UE8M0 128x128 rule on v."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    K, N = q.shape
+    assert s.shape == (_cdiv(K, TILE), _cdiv(N, TILE))
+    q2 = np.empty((K, N), np.uint8)
+    q2T = np.empty((N, K), np.uint8)
+    e = np.empty((_cdiv(K, TILE), _cdiv(N, TILE)), np.uint8)
+    _load().orc_requant_128x128_ue8m0(_ptr(q), K, N, N, _ptr(s), amax_floor, _ptr(q2), N, _ptr(q2T), K, _ptr(e))
+    return q2, q2T, e
 
 
 # --------------------------------------------------------------------------

@@ -416,6 +416,40 @@ void orc_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq
     free(v);
 }
 
+/* Second stage of the two-stage weight cast (prime-rl PR #4073 conventions
+ * table, row "Two-stage weights": the online FP8 cast of a weight, then its
+ * decoded values requantized to power-of-two scales).  Input: a 128x128-tiled
+ * E4M3 weight, codes q [K][N] and fp32 tile scales s[i*ceil(N/128) + j] as
+ * orc_quantize_128x128 writes them.  Each element is dequantized
+ * v = fl32(dec(q) * s) (one rounding of the exact product) and the tiles of v
+ * are requantized with the UE8M0 rule (same 128x128 tiles), writing q2 and/or
+ * its transpose q2T and the bytes e[i*ceil(N/128) + j]. */
+void orc_requant_128x128_ue8m0(const uint8_t* q, int64_t K, int64_t N, int64_t ldq,
+                               const float* s, float amax_floor,
+                               uint8_t* q2, int64_t ldq2, uint8_t* q2T, int64_t ldq2T, uint8_t* e)
+{
+    int64_t kb = ceil_div(K, ORC_TILE), nb = ceil_div(N, ORC_TILE);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < kb * nb; ++t) {
+        int64_t i = t / nb, j = t % nb;
+        int64_t k0 = i * ORC_TILE, n0 = j * ORC_TILE;
+        int64_t kn = (K - k0 < ORC_TILE) ? K - k0 : ORC_TILE;
+        int64_t nn = (N - n0 < ORC_TILE) ? N - n0 : ORC_TILE;
+        float v[ORC_TILE * ORC_TILE];
+        uint8_t code[ORC_TILE * ORC_TILE];
+        const double sc = (double)s[i * nb + j];
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b)
+                v[a * nn + b] = (float)(orc_e4m3_decode(q[(k0 + a) * ldq + n0 + b]) * sc);
+        quantize_tile_ue8m0(v, kn * nn, amax_floor, &e[i * nb + j], code);
+        for (int64_t a = 0; a < kn; ++a)
+            for (int64_t b = 0; b < nn; ++b) {
+                if (q2) q2[(k0 + a) * ldq2 + n0 + b] = code[a * nn + b];
+                if (q2T) q2T[(n0 + b) * ldq2T + k0 + a] = code[a * nn + b];
+            }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Block-scaled GEMM                                                   */
 /* ------------------------------------------------------------------ */

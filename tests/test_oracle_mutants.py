@@ -54,6 +54,12 @@ MUTANTS = {
     "ue8m0_clamp_at_minus_126": ("    int e = -127;\n", "    int e = -126;\n"),
     "e8m0_decode_bias_126": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)"),
     "requant_ue8m0_first_block_byte": ("orc_e8m0_decode(e[(c / ORC_TILE) * lde + r])", "orc_e8m0_decode(e[r])"),
+    "two_stage_tile_scale_transposed": ("const double sc = (double)s[i * nb + j];",
+                                        "const double sc = (double)s[j * kb + i];"),
+    "two_stage_scale_unapplied": ("(float)(orc_e4m3_decode(q[(k0 + a) * ldq + n0 + b]) * sc);",
+                                  "(float)(orc_e4m3_decode(q[(k0 + a) * ldq + n0 + b]));"),
+    "two_stage_transpose_not_transposed": ("if (q2T) q2T[(n0 + b) * ldq2T + k0 + a] = code[a * nn + b];",
+                                           "if (q2T) q2T[(n0 + a) * ldq2T + k0 + b] = code[a * nn + b];"),
     "philox_multiplier_typo": ("(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F57u * c0"),
     "philox_nine_rounds": ("for (int round = 0; round < 10; ++round)", "for (int round = 0; round < 9; ++round)"),
     "philox_weyl_constants_swapped": ("k0 += 0x9E3779B9u;\n        k1 += 0xBB67AE85u;",

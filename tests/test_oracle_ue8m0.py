@@ -140,3 +140,54 @@ def test_e8m0_decode_table(orc):
     assert d[127] == 1.0 and d[128] == 2.0 and d[0] == 2.0 ** -127 and d[254] == 2.0 ** 127
     assert np.isnan(d[255])
     assert np.all(np.diff(d[:255]) > 0)
+
+
+def test_two_stage_weight_requant_is_ue8m0_rule_on_dequantized(orc):
+    """Second stage of the two-stage weight cast: v = fl32(dec(q) * s) with the
+    first stage's fp32 tile scales (torch's decode; the float32 product of two
+    float32 values is the exact product rounded once), then the UE8M0 rule per
+    128x128 tile of v, checked by its two inequalities and torch's cast."""
+    K, N = 256, 384
+    w = stress_bits(K, N, 11)
+    q, _, s = orc.quantize_128x128(w)
+    q2, q2T, e = orc.requant_128x128_ue8m0(q, s)
+    assert np.array_equal(q2.T, q2T)
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    v = dec * np.repeat(np.repeat(s, T, axis=0), T, axis=1)          # float32 * float32
+    for i in range(K // T):
+        for j in range(N // T):
+            tile = v[i * T:(i + 1) * T, j * T:(j + 1) * T]
+            check_exponents(e[i:i + 1, j], np.array([np.abs(tile).max()]))
+            ex = int(e[i, j]) - 127
+            scaled = (tile.astype(np.float64) * 2.0 ** -ex).astype(np.float32)
+            assert np.abs(scaled).max() <= 448.0
+            assert np.array_equal(q2[i * T:(i + 1) * T, j * T:(j + 1) * T], torch_cast(scaled))
+
+
+def test_two_stage_requant_of_power_of_two_weights_is_identity(orc):
+    """A first stage that already has power-of-two scales comes back unchanged:
+    the decoded tile's absmax is a code times 2^e, so the rule picks e again and
+    every scaled value is an E4M3 value."""
+    w = stress_bits(384, 256, 12)
+    q, _, e = orc.quantize_128x128_ue8m0(w)
+    s = np.exp2(e.astype(np.float64) - 127.0).astype(np.float32)
+    q2, _, e2 = orc.requant_128x128_ue8m0(q, s)
+    assert np.array_equal(e2, e)
+    assert np.array_equal(q2, q)
+
+
+def test_two_stage_requant_floors(orc):
+    """The pages' minimum power-of-two scales (conventions row "Activation
+    floors"): an amax floor of 1e-10 gives 2^-42 (1e-10 / 448 lies in
+    (2^-43, 2^-42]); flooring the scale itself at 1e-10 gives 2^-33, the same
+    exponent as an amax floor of 448 * 2^-33.  A tile whose values are tiny
+    but non-zero takes the floor when the floor is larger."""
+    q = np.zeros((128, 256), np.uint8)
+    q[0, 130] = 0x01                                   # dec = 2^-9 in tile (0, 1)
+    s = np.array([[1.0, 2.0 ** -40]], np.float32)      # tile (0, 1) holds 2^-49
+    for floor, want in [(1e-10, -42), (448.0 * 2.0 ** -33, -33)]:
+        _, _, e = orc.requant_128x128_ue8m0(q, s, amax_floor=floor)
+        assert int(e[0, 0]) - 127 == want and int(e[0, 1]) - 127 == want
+    _, _, e = orc.requant_128x128_ue8m0(q, s)
+    assert int(e[0, 0]) == 0                            # all-zero tile, no floor: -127
+    assert int(e[0, 1]) - 127 == -57                    # 448 * 2^-58 < 2^-49 <= 448 * 2^-57
