@@ -61,6 +61,7 @@ SIGNATURES = {
     "fgb_quantize_dual_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _I, _P, _I, _P],
     "fgb_quantize_128x128_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _P],
     "fgb_requant_128x1_ue8m0": [_P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P],
+    "fgb_requant_128x128_ue8m0": [_P, _I, _I, _I, _P, _F, _P, _I, _P, _I, _P, _P],
     "fgb_gemm_fprop_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
     "fgb_gemm_dgrad_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
     "fgb_gemm_wgrad_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _N, _P],
@@ -228,6 +229,28 @@ def requant_128x1(q: torch.Tensor, s: torch.Tensor, qT=None, sT=None, ue8m0: boo
                                    _ptr(qT), _rows(qT, torch.uint8, "qT"), _ptr(sT),
                                    _rows(sT, torch.float32, "sT"), _stream(q)), "requant_128x1")
     return qT, sT
+
+
+def requant_128x128_ue8m0(q: torch.Tensor, s: torch.Tensor, amax_floor: float = 0.0, want_q: bool = True,
+                          want_qT: bool = True, q2=None, q2T=None, s2=None):
+    """Second stage of the two-stage weight cast: a 128x128 E4M3 weight (codes q
+    [K, N], fp32 tile scales s [K/128, N/128] as quantize_128x128 returns them)
+    requantized to power-of-two tiles -> (q2 [K, N], q2T [N, K], s2 [K/128, N/128])."""
+    K, N = q.shape
+    ldq = _rows(q, torch.uint8, "q")
+    if s.dtype != torch.float32 or tuple(s.shape) != (_cdiv(K, TILE), _cdiv(N, TILE)) or not s.is_contiguous():
+        raise FgbError(f"requant_128x128_ue8m0: s must be contiguous float32 [{_cdiv(K, TILE)}, {_cdiv(N, TILE)}]")
+    if want_q and q2 is None:
+        q2 = torch.empty((K, N), dtype=torch.uint8, device=q.device)
+    if want_qT and q2T is None:
+        q2T = torch.empty((N, K), dtype=torch.uint8, device=q.device)
+    if s2 is None:
+        s2 = torch.empty((_cdiv(K, TILE), _cdiv(N, TILE)), dtype=torch.float32, device=q.device)
+    ldq2 = _rows(q2, torch.uint8, "q2") if q2 is not None else 0
+    ldq2T = _rows(q2T, torch.uint8, "q2T") if q2T is not None else 0
+    _check(_fn("fgb_requant_128x128", True)(_ptr(q), K, N, ldq, _ptr(s), amax_floor, _ptr(q2), ldq2, _ptr(q2T),
+                                            ldq2T, _ptr(s2), _stream(q)), "requant_128x128_ue8m0")
+    return q2, q2T, s2
 
 
 # ---------------------------------------------------------------------------

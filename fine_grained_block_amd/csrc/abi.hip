@@ -216,6 +216,23 @@ int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
     return requant_128x1(q, R, C, ldq, s, lds, qT, ldqT, sT, ldsT, true, stream);
 }
 
+int fgb_requant_128x128_ue8m0(const uint8_t* q, int64_t K, int64_t N, int64_t ldq, const float* s,
+                              float amax_floor, uint8_t* q2, int64_t ldq2, uint8_t* q2T, int64_t ldq2T,
+                              float* s2, void* stream)
+{
+    if (K < 0 || N < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
+    if (bad_floor(amax_floor)) return FGB_E_ARG;
+    if (K == 0 || N == 0) return FGB_OK;
+    FGB_TRY(check_codes(q, ldq, N, 8));
+    FGB_TRY(check_sc(s, N / T, N / T, false));
+    if (!q2 && !q2T) return FGB_E_NULL;
+    if (q2) FGB_TRY(check_codes(q2, ldq2, N, 8));
+    if (q2T) FGB_TRY(check_codes(q2T, ldq2T, K, 16));
+    FGB_TRY(check_sc(s2, N / T, N / T, true));
+    return hip_status(fgb::launch_tile128(fgb::kTileRequant128x128, q, K, N, ldq, s, N / T, amax_floor,
+                                          q2, ldq2, q2T, ldq2T, s2, N / T, true, as_stream(stream)));
+}
+
 // ------------------------------- SwiGLU ------------------------------------
 int fgb_swiglu_fwd_quant(const uint16_t* gu, int64_t R, int64_t F, int64_t ldgu, float amax_floor,
                          uint8_t* q_gu, int64_t ldq_gu, float* s_gu, int64_t lds_gu,

@@ -19,7 +19,7 @@ hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_
                                  float* s, int64_t lds, bool po2, hipStream_t stream,
                                  const SrParams* sr = nullptr);
 
-enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 3 };
+enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 3, kTileRequant128x128 = 4 };
 
 // 128x128 tile kernels over a [R][C] input:
 //   kTile128x1:   bf16 in, per-column 128-row scales, transposed codes out (qT, sT)
@@ -27,6 +27,8 @@ enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 
 //   kTileRequant: E4M3 + 1x128 scales in, then as kTile128x1
 //   kTileDual:    bf16 in, both the 1x128 codes and scales (q, s_row) and the
 //                 128x1 transposed codes and scales (qT, sT) from one read
+//   kTileRequant128x128: E4M3 + one fp32 scale per 128x128 tile in
+//                 (s_in[i * lds_in + j]), then as kTile128x128
 // po2 as above for every scale written (scales read by the requant are fp32 either way).
 // sr: stochastic rounding for kTile128x1, kTile128x128 and kTileDual (absmax/448).
 hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,

@@ -133,7 +133,10 @@ __global__ __launch_bounds__(256) void k_tile128(
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
     float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row, SrArgs sr)
 {
-    static_assert(!(SR && (PO2 || MODE == kTileRequant)), "stochastic rounding: absmax/448 scales, no requant");
+    static_assert(!(SR && (PO2 || MODE == kTileRequant || MODE == kTileRequant128x128)),
+                  "stochastic rounding: absmax/448 scales, no requant");
+    // one scale per 128x128 tile: the weight quantizer and its requant
+    constexpr bool TILE = MODE == kTile128x128 || MODE == kTileRequant128x128;
     // scale of absmax a: fp32 (s = a/448, mul = 448/a) or power of two (E8M0 byte, mul = 2^-e)
     auto scale_of = [&](float a, float& sc, uint32_t& eb, float& mul) {
         if constexpr (PO2) tile_scale_ue8m0(a, eb, mul);
@@ -157,10 +160,14 @@ __global__ __launch_bounds__(256) void k_tile128(
     for (int i = 0; i < 8; ++i) {
         const int64_t r = r0 + rg * 8 + i;
         const bool ok = cok && r < R;
-        if constexpr (MODE == kTileRequant) {
+        if constexpr (MODE == kTileRequant || MODE == kTileRequant128x128) {
+            // dequantize: v = fl32(dec(q) * s) with the row's 1x128 scale, or
+            // the tile's scale s_in[i * lds_in + j] for a 128x128 weight tile
             const uint8_t* p = static_cast<const uint8_t*>(in);
             const uint2 w = ok ? ld8(p + r * ldin + cc) : make_uint2(0u, 0u);
-            const float sr = ok ? s_in[(int64_t)blockIdx.y * lds_in + r] : 0.0f;
+            const float sr = !ok ? 0.0f
+                : MODE == kTileRequant ? s_in[(int64_t)blockIdx.y * lds_in + r]
+                                       : s_in[(int64_t)blockIdx.x * lds_in + blockIdx.y];
             const float2 d0 = e4m3x2_decode<false>(w.x), d1 = e4m3x2_decode<true>(w.x);
             const float2 d2 = e4m3x2_decode<false>(w.y), d3 = e4m3x2_decode<true>(w.y);
             v[i][0] = d0.x * sr; v[i][1] = d0.y * sr; v[i][2] = d1.x * sr; v[i][3] = d1.y * sr;
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(256) void k_tile128(
     }
 
     float inv[8];
-    if constexpr (MODE == kTile128x128) {
+    if constexpr (TILE) {
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(256) void k_tile128(
                                  u[0], u[1], u[2], u[3]);
             cr[i][1] = e4m3x4_sr(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7],
                                  u[4], u[5], u[6], u[7]);
-            if constexpr (MODE == kTile128x128) {
+            if constexpr (TILE) {
                 if (q != nullptr && cok && r < R) st8(q + r * ldq + cc, make_uint2(cr[i][0], cr[i][1]));
             }
         }
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(256) void k_tile128(
             const int64_t rr = r0 + rg * 8 + cg;
             if (cg < 8 && rr < R) s_row[(int64_t)blockIdx.y * lds_row + rr] = sr_own;
         }
-        if constexpr (MODE == kTile128x128) {
+        if constexpr (TILE) {
             if (qT == nullptr) return;
         }
         // column k of the patch: byte k & 3 of cr[i][k >> 2] for rows i = 0..7
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(256) void k_tile128(
     }
 
     // Row-major codes (128x128 weights, q != nullptr): 8 bytes per patch row.
-    if constexpr (MODE == kTile128x128) {
+    if constexpr (TILE) {
         if (q != nullptr) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -376,6 +383,11 @@ static void launch_tile128_t(TileMode mode, dim3 grid, const void* in, int64_t R
         hipLaunchKernelGGL((k_tile128<kTileDual, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
                            s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
         break;
+    case kTileRequant128x128:
+        if constexpr (!SR)
+            hipLaunchKernelGGL((k_tile128<kTileRequant128x128, PO2, false>), grid, dim3(256), 0, stream, in, R, C,
+                               ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
+        break;
     }
 }
 
@@ -385,7 +397,7 @@ hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, i
                           float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
                           float* s_row, int64_t lds_row, const SrParams* sr)
 {
-    if (sr && (po2 || mode == kTileRequant)) return hipErrorInvalidValue;
+    if (sr && (po2 || mode == kTileRequant || mode == kTileRequant128x128)) return hipErrorInvalidValue;
     dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
     const SrArgs a = sr_args(sr);
     if (po2)

@@ -255,6 +255,24 @@ int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                             void* stream);
 
+/* Second stage of the two-stage weight cast ([prime] conventions row
+ * "Two-stage weights": the weight's online FP8 cast, then its decoded values
+ * requantized to power-of-two scales).  Input: a 128x128-tiled E4M3 weight as
+ * fgb_quantize_128x128 writes it, codes q [K][N] (ldq >= N) and fp32 tile
+ * scales s [K/128][N/128] (dense).  Each element is dequantized
+ * v = fl32(dec(q) * s) and every 128x128 tile of v is requantized with the
+ * power-of-two rule above (a = max(absmax, amax_floor)), writing q2 [K][N]
+ * (ldq2 >= N) and/or its transpose q2T [N][K] (ldq2T >= K), either may be
+ * NULL but not both, and the power-of-two scales s2 [K/128][N/128].  An amax
+ * floor of 1e-10 gives the minimum scale 2^-42; flooring the scale itself at
+ * 1e-10 (minimum 2^-33) is the floor 448 * 2^-33 here ([prime] row
+ * "Activation floors").  K and N multiples of 128; outputs must not overlap
+ * the inputs. */
+int fgb_requant_128x128_ue8m0(const uint8_t* q, int64_t K, int64_t N, int64_t ldq,
+                              const float* s, float amax_floor,
+                              uint8_t* q2, int64_t ldq2, uint8_t* q2T, int64_t ldq2T,
+                              float* s2, void* stream);
+
 /* ------------------------------------------------------------------------
  * Block-scaled GEMMs ([drift] section 3 rows (a)/(b) and section 5: the
  * partial sum of every 128-long contraction segment is multiplied by

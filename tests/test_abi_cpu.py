@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = fgb.lib()
     names = header_functions()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fgb.SIGNATURES)
@@ -233,3 +233,24 @@ def test_swiglu_validation():
     assert bwd(qT=P(0x10008)) == E_ALIGN
     assert bwd(dgu=MIS, lddgu=512) == E_ALIGN
     assert bwd(F=0, qg=P(0)) == OK
+
+
+def rq2(q=A, K=128, N=256, ldq=256, s=C_, fl=0.0, q2=B, ldq2=256, q2T=D, ldq2T=128, s2=C_):
+    return fgb.lib().fgb_requant_128x128_ue8m0(q, K, N, ldq, s, fl, q2, ldq2, q2T, ldq2T, s2, None)
+
+
+def test_requant_128x128_ue8m0_validation():
+    assert rq2(K=100) == E_SHAPE
+    assert rq2(N=200) == E_SHAPE
+    assert rq2(K=-128) == E_SHAPE
+    assert rq2(fl=-1.0) == E_ARG
+    assert rq2(fl=float("nan")) == E_ARG
+    assert rq2(q=P(0)) == E_NULL
+    assert rq2(s=P(0)) == E_NULL
+    assert rq2(s2=P(0)) == E_NULL
+    assert rq2(q2=P(0), q2T=P(0)) == E_NULL
+    assert rq2(ldq=128) == E_LD
+    assert rq2(ldq2=128) == E_LD
+    assert rq2(ldq2T=64) == E_LD
+    assert rq2(q=MIS) == E_ALIGN
+    assert rq2(K=0) == OK and rq2(N=0) == OK          # empty: nothing to do
