@@ -16,7 +16,10 @@ against its own roofline (HBM for the quantizers).  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same step.
 
 `--recipe ue8m0` runs the same step with power-of-two (UE8M0) scales, which the
-matrix core applies itself (no vector-ALU rescale).
+matrix core applies itself (no vector-ALU rescale).  Its weight cast has two
+stages by default, as in the pages' conventions: the FP8 cast with fp32 tile
+scales, then the decoded weight requantized to power-of-two tiles
+(`--ue8m0-weights direct` casts the bf16 weight straight to power-of-two tiles).
 
 `--rounding sr` quantizes X, W and dY with stochastic rounding (one Philox
 word per element); the requant of the saved X stays round-to-nearest.
@@ -97,6 +100,9 @@ def parse():
                         "moe_grouped: one GPU's MoE expert share as a SwiGLU FFN, fwd+bwd (no CPU baseline)")
     p.add_argument("--recipe", choices=["fp32", "ue8m0"], default="fp32",
                    help="fp32: scales absmax/448 (default); ue8m0: power-of-two scales, applied by the matrix core")
+    p.add_argument("--ue8m0-weights", choices=["two-stage", "direct"], default="two-stage",
+                   help="with --recipe ue8m0: two-stage (default) = FP8 cast with fp32 tile scales, then "
+                        "requant of the decoded weight to power-of-two tiles; direct = one power-of-two cast")
     p.add_argument("--rounding", choices=["rn", "sr"], default="rn",
                    help="rn: round-to-nearest casts (default); sr: stochastic rounding of the X, W and dY "
                         "casts (Philox words; the requant of X stays round-to-nearest)")
@@ -125,10 +131,13 @@ def algorithmic_bytes(M, K, N):
         "quantize_128x1_dy": M * N * 2 + N * Mp + nbM * N * 4,
         "requant_128x1_x": M * K + nbK * M * 4 + K * Mp + nbM * K * 4,
         "quantize_dual_dy": M * N * 2 + M * N + nbN * M * 4 + N * Mp + nbM * N * 4,
+        # two-stage weight cast: the first stage writes the row-major codes only
+        "quantize_128x128_w_stage1": K * N * 2 + K * N + nbK * nbN * 4,
+        "requant_128x128_w": K * N + nbK * nbN * 4 + 2 * K * N + nbK * nbN * 4,
     }
 
 
-def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bufs=None):
+def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bufs=None, two_stage=False):
     """The linear layer's step at X [M,K], W [K,N], dY [M,N]: (name, launch, work,
     lane, deps) per kernel in issue order, work = {"flop": ...} or {"bytes": ...}
     (algorithmic); lane 1 = the second stream, deps = kernels it reads the
@@ -153,6 +162,10 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bu
         "qxT": torch.empty((K, Mp), **u8), "sxT": torch.empty((Mp // T, K), **f32),
         "dw": torch.empty((K, N), **f32),
     }
+    two_stage = two_stage and ue8m0
+    if two_stage:
+        b["qw1"] = torch.empty((K, N), **u8)
+        b["sw1"] = torch.empty((K // T, N // T), **f32)
     if bufs is not None:
         bufs.update(b)
     ab = algorithmic_bytes(M, K, N)
@@ -172,12 +185,26 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bu
                                                           ue8m0=ue8m0, sr=srk(3)),
              {"bytes": ab["quantize_dual_dy"]}),
         ]
+    if two_stage:
+        w_casts = [
+            # first stage with the pages' weight amax floor 1e-4 (conventions row "Weight floors")
+            ("quantize_128x128_w_stage1", lambda: fgb.quantize_128x128(w, 1e-4, q=b["qw1"], s=b["sw1"],
+                                                                       want_qT=False),
+             {"bytes": ab["quantize_128x128_w_stage1"]}),
+            ("requant_128x128_w", lambda: fgb.requant_128x128_ue8m0(b["qw1"], b["sw1"], q2=b["qw"], q2T=b["qwT"],
+                                                                    s2=b["sw"]),
+             {"bytes": ab["requant_128x128_w"]}),
+        ]
+    else:
+        w_casts = [
+            ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"], ue8m0=ue8m0,
+                                                                sr=srk(2)),
+             {"bytes": ab["quantize_128x128_w"]}),
+        ]
     steps = [
         ("quantize_1x128_x", lambda: fgb.quantize_1x128(x, q=b["qx"], s=b["sx"], ue8m0=ue8m0, sr=srk(1)),
          {"bytes": ab["quantize_1x128_x"]}),
-        ("quantize_128x128_w", lambda: fgb.quantize_128x128(w, q=b["qw"], qT=b["qwT"], s=b["sw"], ue8m0=ue8m0,
-                                                            sr=srk(2)),
-         {"bytes": ab["quantize_128x128_w"]}),
+    ] + w_casts + [
         ("gemm_fprop", lambda: fgb.gemm_fprop(b["qx"], b["sx"], b["qwT"], b["sw"], y=b["y"], ue8m0=ue8m0), flop),
     ] + dy_casts + [
         ("gemm_dgrad", lambda: fgb.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], dx=b["dx"], ue8m0=ue8m0), flop),
@@ -187,19 +214,24 @@ def linear_step(fgb, torch, dev, d, separate_dy=False, ue8m0=False, sr=False, bu
          flop),
     ]
     dy_names = [n for n, _, _ in dy_casts]
-    lanes = {"quantize_1x128_x": (1, []), "quantize_128x128_w": (0, []),
-             "gemm_fprop": (0, ["quantize_1x128_x", "quantize_128x128_w"]),
-             "gemm_dgrad": (0, dy_names + ["quantize_128x128_w"]),
+    w_names = [n for n, _, _ in w_casts]
+    lanes = {"quantize_1x128_x": (1, []),
+             "gemm_fprop": (0, ["quantize_1x128_x", w_names[-1]]),
+             "gemm_dgrad": (0, dy_names + [w_names[-1]]),
              "requant_128x1_x": (1, ["quantize_1x128_x"]),
              "gemm_wgrad": (0, dy_names + ["requant_128x1_x"])}
     for n in dy_names:
         lanes[n] = (1, [])
-    order = ["quantize_1x128_x", "quantize_128x128_w", "gemm_fprop"] + dy_names + \
+    for n in w_names:
+        lanes[n] = (0, [])
+    order = ["quantize_1x128_x"] + w_names + ["gemm_fprop"] + dy_names + \
             ["gemm_dgrad", "requant_128x1_x", "gemm_wgrad"]
     by = {name: (name, fn, work) for name, fn, work in steps}
     steps = [by[n] + lanes[n] for n in order]
 
     def rename(n):
+        if n == "quantize_128x128_w_stage1":
+            return n
         n = n + "_ue8m0" if ue8m0 else n
         return n + "_sr" if sr and n.startswith("quantize") else n
     return [(rename(n), fn, work, lane, [rename(x) for x in deps]) for n, fn, work, lane, deps in steps]
@@ -363,9 +395,12 @@ def main():
         if ue8m0 and sr:
             print("bench.py: stochastic rounding uses absmax/448 scales (--recipe fp32)", file=sys.stderr)
             sys.exit(2)
-        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts, ue8m0=ue8m0, sr=sr)
+        two_stage = ue8m0 and args.ue8m0_weights == "two-stage"
+        kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts, ue8m0=ue8m0, sr=sr,
+                              two_stage=two_stage)
         config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]"
                               + (", power-of-two (UE8M0) scales" if ue8m0 else "")
+                              + (" with the two-stage weight cast" if two_stage else "")
                               + (", stochastic rounding of the X, W and dY casts" if sr else ""),
                   "M": d["M"], "K": d["K"], "N": d["N"], "scales": args.recipe, "rounding": args.rounding}
         data = "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)"

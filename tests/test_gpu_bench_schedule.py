@@ -17,8 +17,8 @@ def _outputs(bufs):
     return {k: v.clone() for k, v in bufs.items()}
 
 
-@pytest.mark.parametrize("ue8m0", [False, True])
-def test_linear_overlap_matches_serial(ue8m0):
+@pytest.mark.parametrize("ue8m0,two_stage", [(False, False), (True, False), (True, True)])
+def test_linear_overlap_matches_serial(ue8m0, two_stage):
     dev = torch.device("cuda:0")
     M, K, N = 640, 1024, 896
     d = {"M": M, "K": K, "N": N,
@@ -27,7 +27,7 @@ def test_linear_overlap_matches_serial(ue8m0):
     res = {}
     for overlap in (False, True):
         bufs = {}
-        kernels = bench.linear_step(fgb, torch, dev, d, ue8m0=ue8m0, bufs=bufs)
+        kernels = bench.linear_step(fgb, torch, dev, d, ue8m0=ue8m0, bufs=bufs, two_stage=two_stage)
         for b in bufs.values():
             b.zero_()
         step = bench.make_runner(torch, dev, kernels, overlap)
