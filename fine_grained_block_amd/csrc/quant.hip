@@ -45,9 +45,12 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
         const int64_t r = rb + grp + 16 * it;
         v[it] = (cok && r < R) ? ld16(x + r * ldx + c) : make_uint4(0u, 0u, 0u, 0u);
     }
+    // the 4 row maxima; lane it of the 16-lane row group then computes row it's
+    // scale (one pair of divisions per wave) and every lane fetches the
+    // multiplier of row it from that lane
+    float a_own = 0.0f;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const int64_t r = rb + grp + 16 * it;
         const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
         u16x2 m2 = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
 #pragma unroll
@@ -55,11 +58,18 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
             m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
         uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
         m = max16(m);
-        const float a = fmaxf(__uint_as_float(m << 16), amax_floor);
-        float sc, inv;
-        uint32_t eb = 0;
-        if constexpr (PO2) tile_scale_ue8m0(a, eb, inv);
-        else tile_scale(a, sc, inv);
+        if (lane16 == it) a_own = fmaxf(__uint_as_float(m << 16), amax_floor);
+    }
+    float sc_own = 0.0f, inv_own;
+    uint32_t eb_own = 0;
+    if constexpr (PO2) tile_scale_ue8m0(a_own, eb_own, inv_own);
+    else tile_scale(a_own, sc_own, inv_own);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int64_t r = rb + grp + 16 * it;
+        const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+        const float inv = __shfl(inv_own, (lane & 48) | it, 64);
         uint32_t o0, o1;
         if constexpr (SR) {
             uint32_t u[8];
@@ -72,10 +82,11 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
             o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
             o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
         }
-        if (cok && r < R) {
-            st8(q + r * ldq + c, make_uint2(o0, o1));
-            if (lane16 == 0) s[j * lds + r] = PO2 ? e8m0_to_f32(eb) : sc;
-        }
+        if (cok && r < R) st8(q + r * ldq + c, make_uint2(o0, o1));
+    }
+    if (lane16 < 4) {          // the block's segment j exists (grid = ceil(C/128)): only rows can be past the end
+        const int64_t r = rb + grp + 16 * lane16;
+        if (r < R) s[j * lds + r] = PO2 ? e8m0_to_f32(eb_own) : sc_own;
     }
 }
 
@@ -146,6 +157,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         base[idx] = PO2 ? e8m0_to_f32(eb) : sc;
     };
     __shared__ uint32_t red[4][kTile];
+    __shared__ float col_mul[kTile];
     __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kTrStride];
 
     const int t = threadIdx.x;
@@ -216,21 +228,20 @@ __global__ __launch_bounds__(256) void k_tile128(
             for (int k = 0; k < 8; ++k) red[wave][cg * 8 + k] = mc[k];
         }
         __syncthreads();
-        float sc[8];
-        uint32_t eb[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int col = cg * 8 + k;
-            const uint32_t m = max(max(red[0][col], red[1][col]), max(red[2][col], red[3][col]));
+        // thread c < 128 computes column c's scale (two IEEE divisions) once for
+        // the block and shares its multiplier through LDS
+        if (t < kTile) {
+            const uint32_t m = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
             const float a = fmaxf(__uint_as_float(m), amax_floor);
-            sc[k] = 0.0f;
-            eb[k] = 0;
-            scale_of(a, sc[k], eb[k], inv[k]);
+            float sc = 0.0f, iv;
+            uint32_t eb = 0;
+            scale_of(a, sc, eb, iv);
+            col_mul[t] = iv;
+            if (c0 + t < C) put_scale(s_out, (int64_t)blockIdx.x * lds_out + c0 + t, sc, eb);
         }
-        if (rg == 0 && cok) {
+        __syncthreads();
 #pragma unroll
-            for (int k = 0; k < 8; ++k) put_scale(s_out, (int64_t)blockIdx.x * lds_out + cc + k, sc[k], eb[k]);
-        }
+        for (int k = 0; k < 8; ++k) inv[k] = col_mul[cg * 8 + k];
     }
 
     if constexpr (SR) {
@@ -301,19 +312,25 @@ __global__ __launch_bounds__(256) void k_tile128(
     // Dual mode, 1x128 part: row r's tile is the block's 128 columns of row r,
     // held by the 16 lanes that share rg; their absmax is one DPP reduction.
     if constexpr (MODE == kTileDual) {
-        float sr_own = 0.0f;
-        uint32_t er_own = 0;
+        // the 8 row maxima of the patch rows; lane cg = i of the 16-lane row
+        // group then computes row i's scale (one pair of divisions per wave) and
+        // every lane fetches the multiplier of row i from that lane
+        float a_own = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t m = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
             m = max16(m);
-            const float a = fmaxf(__uint_as_float(m), amax_floor);
-            float sc = 0.0f, iv;
-            uint32_t eb = 0;
-            scale_of(a, sc, eb, iv);
-            if (cg == i) { sr_own = sc; er_own = eb; }
+            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+        }
+        float sr_own = 0.0f, iv_own;
+        uint32_t er_own = 0;
+        scale_of(a_own, sr_own, er_own, iv_own);
+        const int lane = t & 63;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
             const int64_t r = r0 + rg * 8 + i;
             const uint32_t o0 = e4m3x4(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
             const uint32_t o1 = e4m3x4(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
