@@ -265,6 +265,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
     uint16_t* __restrict__ dgu, int64_t lddgu)
 {
     __shared__ uint32_t red[4][kTile];
+    __shared__ float col_mul[kTile];
     __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kSwTr];
     __shared__ __attribute__((aligned(16))) uint16_t vt[kTile * kTile];   // the tile's bf16 values
 
@@ -378,29 +379,39 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             for (int k = 0; k < 8; ++k) red[wave][cg * 8 + k] = mc[k];
         }
         __syncthreads();
-        float inv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int col = cg * 8 + k;
-            const uint32_t m = max(max(red[0][col], red[1][col]), max(red[2][col], red[3][col]));
-            float sc;
-            tile_scale(fmaxf(__uint_as_float(m), amax_floor), sc, inv[k]);
-            if (rg == 0) sT[(int64_t)blockIdx.x * ldsT + oc0 + cg * 8 + k] = sc;
+        // thread c < 128 computes column c's scale once and shares its multiplier
+        if (t < kTile) {
+            const uint32_t m = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
+            float sc, iv;
+            tile_scale(fmaxf(__uint_as_float(m), amax_floor), sc, iv);
+            col_mul[t] = iv;
+            sT[(int64_t)blockIdx.x * ldsT + oc0 + t] = sc;
         }
-        // 1x128: each row's tile is the block's 128 columns of that row
-        float s_own = 0.0f;
+        // 1x128: each row's tile is the block's 128 columns of that row; lane
+        // cg = i of the 16-lane row group computes row i's scale, the others
+        // fetch its multiplier with a lane shuffle
+        float a_own = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t m = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
             m = max16(m);
-            float sc, iv;
-            tile_scale(fmaxf(__uint_as_float(m), amax_floor), sc, iv);
-            if (cg == i) s_own = sc;
+            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+        }
+        float s_own, iv_own;
+        tile_scale(a_own, s_own, iv_own);
+        const int lane = t & 63;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
             const int64_t r = r0 + rg * 8 + i;
             if (r < R) st8(q + r * ldq + oc0 + cg * 8, make_uint2(codes4(v[i], iv), codes4(v[i] + 4, iv)));
         }
+        __syncthreads();                                   // col_mul written
+        float inv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) inv[k] = col_mul[cg * 8 + k];
         {
             const int64_t rr = r0 + rg * 8 + cg;
             if (cg < 8 && rr < R) s[tile * lds + rr] = s_own;
