@@ -71,8 +71,9 @@ struct GemmArgs {
     const float* sb = nullptr;  int64_t sb_kb = 0, sb_n = 0;
     void* out = nullptr;        int64_t ldo = 0;
     int accumulate = 0;         // Wgrad: out += result
-    // dense only: blocks from split_from on each take one column half of one of
-    // the tiles that do not fill a whole round of CUs (set by launch_gemm)
+    // dense only: the tiles from split_from on (those that do not fill a whole
+    // round of CUs) are computed as column halves by two blocks each (set by
+    // launch_gemm)
     int64_t split_from = -1;
     // grouped forms
     const int32_t* offsets = nullptr;  // device, E+1 entries
