@@ -189,6 +189,13 @@ __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) {
 // Vector global memory access
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Non-temporal 16-byte load, for an input read once: its lines are not kept in
+// L2 / the MALL, which stay with the outputs that the next kernel reads.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    return make_uint4(__builtin_nontemporal_load(&q->x), __builtin_nontemporal_load(&q->y),
+                      __builtin_nontemporal_load(&q->z), __builtin_nontemporal_load(&q->w));
+}
 __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }

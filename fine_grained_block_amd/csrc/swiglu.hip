@@ -188,8 +188,9 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
     for (int it = 0; it < 4; ++it) {
         const int64_t r = (int64_t)blockIdx.x * kSwRows + grp + 16 * it;
         const bool ok = r < R;
-        const uint4 wg = ok ? ld16(gu + r * ldgu + c) : make_uint4(0u, 0u, 0u, 0u);
-        const uint4 wu = ok ? ld16(gu + r * ldgu + F + c) : make_uint4(0u, 0u, 0u, 0u);
+        // [G | U] is read once: non-temporal loads (see ld16_stream)
+        const uint4 wg = ok ? ld16_stream(gu + r * ldgu + c) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 wu = ok ? ld16_stream(gu + r * ldgu + F + c) : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t g2[4] = {wg.x, wg.y, wg.z, wg.w}, u2[4] = {wu.x, wu.y, wu.z, wu.w};
         float g[8], u[8];
 #pragma unroll
