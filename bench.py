@@ -244,7 +244,7 @@ def moe_step(fgb, torch, dev, d, bufs=None):
     both ways, down Dgrad -> dH, requant H, down Wgrad, SwiGLU backward (emits
     [dG | dU] in both tile orientations), gate/up Dgrad, requant X, gate/up Wgrad.
     GEMM work counts the routed rows only (padding rows are computed, not counted);
-    weight quantization is one launch per expert."""
+    each projection's expert weights are quantized in one launch."""
     import numpy as np
     E, R = d["E"], d["R_pad"]
     rows = int(np.sum(d["loads"]))
@@ -284,9 +284,8 @@ def moe_step(fgb, torch, dev, d, bufs=None):
     if bufs is not None:
         bufs.update(b)
 
-    def quant_w(w, q, qT, s):
-        for e in range(E):
-            fgb.quantize_128x128(w[e], q=q[e], qT=qT[e], s=s[e])
+    def quant_w(w, q, qT, s):                 # all experts' weights in one launch
+        fgb.quantize_128x128_batched(w, q=q, qT=qT, s=s)
 
     up = {"flop": 2.0 * rows * Dm * F2}
     down = {"flop": 2.0 * rows * F * Dm}

@@ -62,6 +62,8 @@ SIGNATURES = {
     "fgb_quantize_128x128_ue8m0": [_P, _I, _I, _I, _F, _P, _I, _P, _I, _P, _P],
     "fgb_requant_128x1_ue8m0": [_P, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P],
     "fgb_requant_128x128_ue8m0": [_P, _I, _I, _I, _P, _F, _P, _I, _P, _I, _P, _P],
+    "fgb_quantize_128x128_batched": [_I, _P, _I, _I, _F, _P, _P, _P, _P],
+    "fgb_quantize_128x128_batched_ue8m0": [_I, _P, _I, _I, _F, _P, _P, _P, _P],
     "fgb_gemm_fprop_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
     "fgb_gemm_dgrad_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P],
     "fgb_gemm_wgrad_ue8m0": [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _N, _P],
@@ -215,6 +217,29 @@ def quantize_128x128(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = Tr
     ldqT = _rows(qT, torch.uint8, "qT") if qT is not None else 0
     _check(_quant_call("fgb_quantize_128x128", ue8m0, sr, (_ptr(w), K, N, ldw, amax_floor, _ptr(q), ldq, _ptr(qT),
                        ldqT, _ptr(s), _stream(w))), "quantize_128x128")
+    return q, qT, s
+
+
+def quantize_128x128_batched(w: torch.Tensor, amax_floor: float = 0.0, want_q: bool = True, want_qT: bool = True,
+                             q=None, qT=None, s=None, ue8m0: bool = False):
+    """E stacked weights w [E, K, N] (contiguous bf16) in one launch -> (q [E, K, N],
+    qT [E, N, K], s [E, K/128, N/128]), each matrix as quantize_128x128 alone."""
+    if w.dim() != 3:
+        raise FgbError("quantize_128x128_batched: w must be [E, K, N]")
+    E, K, N = w.shape
+    dev = w.device
+    if want_q and q is None:
+        q = torch.empty((E, K, N), dtype=torch.uint8, device=dev)
+    if want_qT and qT is None:
+        qT = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = torch.empty((E, _cdiv(K, TILE), _cdiv(N, TILE)), dtype=torch.float32, device=dev)
+    for t, dt, shape in ((w, torch.bfloat16, (E, K, N)), (q, torch.uint8, (E, K, N)), (qT, torch.uint8, (E, N, K)),
+                         (s, torch.float32, (E, _cdiv(K, TILE), _cdiv(N, TILE)))):
+        if t is not None and (t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise FgbError(f"quantize_128x128_batched: expected contiguous {dt} {shape}")
+    _check(_fn("fgb_quantize_128x128_batched", ue8m0)(E, _ptr(w), K, N, amax_floor, _ptr(q), _ptr(qT), _ptr(s),
+                                                      _stream(w)), "quantize_128x128_batched")
     return q, qT, s
 
 

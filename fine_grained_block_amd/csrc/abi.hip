@@ -141,6 +141,37 @@ static int quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw
                                           q, ldq, qT, ldqT, s, N / T, po2, as_stream(stream), nullptr, 0, sr));
 }
 
+// E stacked weights w [E][K][N] -> q [E][K][N], qT [E][N][K], s [E][K/128][N/128].
+static int quantize_128x128_batched(int64_t E, const uint16_t* w, int64_t K, int64_t N, float amax_floor,
+                                    uint8_t* q, uint8_t* qT, float* s, bool po2, void* stream)
+{
+    if (E < 0 || E > 65535 || K < 0 || N < 0 || K % T != 0 || N % T != 0) return FGB_E_SHAPE;
+    if (bad_floor(amax_floor)) return FGB_E_ARG;
+    if (E == 0 || K == 0 || N == 0) return FGB_OK;
+    FGB_TRY(check_bf16(w, N, N));
+    if (!q && !qT) return FGB_E_NULL;
+    if (q) FGB_TRY(check_codes(q, N, N, 8));
+    if (qT) FGB_TRY(check_codes(qT, K, K, 16));
+    FGB_TRY(check_sc(s, N / T, N / T, po2));
+    fgb::TileBatch bt;
+    bt.in = K * N * 2; bt.q = K * N; bt.qT = N * K; bt.s = (K / T) * (N / T);
+    return hip_status(fgb::launch_tile128(fgb::kTile128x128, w, K, N, N, nullptr, 0, amax_floor,
+                                          q, N, qT, K, s, N / T, po2, as_stream(stream), nullptr, 0, nullptr,
+                                          E, bt));
+}
+
+int fgb_quantize_128x128_batched(int64_t E, const uint16_t* w, int64_t K, int64_t N, float amax_floor,
+                                 uint8_t* q, uint8_t* qT, float* s, void* stream)
+{
+    return quantize_128x128_batched(E, w, K, N, amax_floor, q, qT, s, false, stream);
+}
+
+int fgb_quantize_128x128_batched_ue8m0(int64_t E, const uint16_t* w, int64_t K, int64_t N, float amax_floor,
+                                       uint8_t* q, uint8_t* qT, float* s, void* stream)
+{
+    return quantize_128x128_batched(E, w, K, N, amax_floor, q, qT, s, true, stream);
+}
+
 static int requant_128x1(const uint8_t* q, int64_t R, int64_t C, int64_t ldq, const float* s, int64_t lds,
                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, bool po2, void* stream)
 {

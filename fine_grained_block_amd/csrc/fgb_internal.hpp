@@ -31,11 +31,15 @@ enum TileMode { kTile128x1 = 0, kTile128x128 = 1, kTileRequant = 2, kTileDual = 
 //                 (s_in[i * lds_in + j]), then as kTile128x128
 // po2 as above for every scale written (scales read by the requant are fp32 either way).
 // sr: stochastic rounding for kTile128x1, kTile128x128 and kTileDual (absmax/448).
+// A stack of `batch` matrices of the same shape, matrix z at z * (byte strides
+// in, q, qT; float stride s) from the first (grid z; the 128x128 quantizer).
+struct TileBatch { int64_t in = 0, q = 0, qT = 0, s = 0; };
 hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, int64_t ldin,
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                           float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
-                          float* s_row = nullptr, int64_t lds_row = 0, const SrParams* sr = nullptr);
+                          float* s_row = nullptr, int64_t lds_row = 0, const SrParams* sr = nullptr,
+                          int64_t batch = 1, TileBatch bt = TileBatch{});
 
 // ------------------------------- SwiGLU ------------------------------------
 // [G | U] is one [R][2F] bf16 tensor, F % 128 == 0.  Forward: the 1x128 stash

@@ -145,10 +145,19 @@ __global__ __launch_bounds__(256) void k_tile128(
     const void* __restrict__ in, int64_t R, int64_t C, int64_t ldin,
     const float* __restrict__ s_in, int64_t lds_in, float amax_floor,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
-    float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row, SrArgs sr)
+    float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row, SrArgs sr,
+    TileBatch bt)
 {
     static_assert(!(SR && (PO2 || MODE == kTileRequant || MODE == kTileRequant128x128)),
                   "stochastic rounding: absmax/448 scales, no requant");
+    // batched launches: matrix blockIdx.z of a stack (byte strides; scales in floats)
+    if (blockIdx.z > 0) {
+        const int64_t z = blockIdx.z;
+        in = static_cast<const uint8_t*>(in) + z * bt.in;
+        if (q != nullptr) q += z * bt.q;
+        if (qT != nullptr) qT += z * bt.qT;
+        s_out += z * bt.s;
+    }
     // one scale per 128x128 tile: the weight quantizer and its requant
     constexpr bool TILE = MODE == kTile128x128 || MODE == kTileRequant128x128;
     // scale of absmax a: fp32 (s = a/448, mul = 448/a) or power of two (E8M0 byte, mul = 2^-e)
@@ -383,30 +392,30 @@ static void launch_tile128_t(TileMode mode, dim3 grid, const void* in, int64_t R
                              const float* s_in, int64_t lds_in, float amax_floor,
                              uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                              float* s_out, int64_t lds_out, hipStream_t stream, float* s_row, int64_t lds_row,
-                             SrArgs a)
+                             SrArgs a, TileBatch bt)
 {
     switch (mode) {
     case kTile128x1:
         hipLaunchKernelGGL((k_tile128<kTile128x1, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
         break;
     case kTile128x128:
         hipLaunchKernelGGL((k_tile128<kTile128x128, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
         break;
     case kTileRequant:
         if constexpr (!SR)
             hipLaunchKernelGGL((k_tile128<kTileRequant, PO2, false>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                               s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
+                               s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
         break;
     case kTileDual:
         hipLaunchKernelGGL((k_tile128<kTileDual, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
         break;
     case kTileRequant128x128:
         if constexpr (!SR)
             hipLaunchKernelGGL((k_tile128<kTileRequant128x128, PO2, false>), grid, dim3(256), 0, stream, in, R, C,
-                               ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a);
+                               ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
         break;
     }
 }
@@ -415,20 +424,21 @@ hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, i
                           const float* s_in, int64_t lds_in, float amax_floor,
                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                           float* s_out, int64_t lds_out, bool po2, hipStream_t stream,
-                          float* s_row, int64_t lds_row, const SrParams* sr)
+                          float* s_row, int64_t lds_row, const SrParams* sr, int64_t batch, TileBatch bt)
 {
     if (sr && (po2 || mode == kTileRequant || mode == kTileRequant128x128)) return hipErrorInvalidValue;
-    dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile));
+    if (batch < 1 || batch > 65535) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile), (unsigned)batch);
     const SrArgs a = sr_args(sr);
     if (po2)
         launch_tile128_t<true, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                      s_out, lds_out, stream, s_row, lds_row, a);
+                                      s_out, lds_out, stream, s_row, lds_row, a, bt);
     else if (sr)
         launch_tile128_t<false, true>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                      s_out, lds_out, stream, s_row, lds_row, a);
+                                      s_out, lds_out, stream, s_row, lds_row, a, bt);
     else
         launch_tile128_t<false, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                       s_out, lds_out, stream, s_row, lds_row, a);
+                                       s_out, lds_out, stream, s_row, lds_row, a, bt);
     return hipGetLastError();
 }
 

@@ -132,6 +132,14 @@ int fgb_quantize_128x128(const uint16_t* w, int64_t K, int64_t N, int64_t ldw,
                          uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                          float* s, void* stream);
 
+/* E weights at once (the experts of a MoE layer): w [E][K][N] (dense, bf16)
+ * -> q [E][K][N] and/or qT [E][N][K] (either may be NULL but not both) and
+ * s [E][K/128][N/128], each matrix exactly as fgb_quantize_128x128 quantizes
+ * it alone, in one launch.  K and N multiples of 128, 0 <= E <= 65535. */
+int fgb_quantize_128x128_batched(int64_t E, const uint16_t* w, int64_t K, int64_t N,
+                                 float amax_floor, uint8_t* q, uint8_t* qT, float* s,
+                                 void* stream);
+
 /* Re-tile a 1x128-quantized tensor to 128x1 ([scratch]: the Wgrad operand
  * is re-quantized 128x1 from the saved tensor by a small requant box).
  * Input codes q [R][C] (ldq >= C) with scales s [ceil(C/128)][lds],
@@ -250,6 +258,9 @@ int fgb_quantize_128x128_ue8m0(const uint16_t* w, int64_t K, int64_t N, int64_t 
                                float amax_floor,
                                uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                                float* s, void* stream);
+int fgb_quantize_128x128_batched_ue8m0(int64_t E, const uint16_t* w, int64_t K, int64_t N,
+                                       float amax_floor, uint8_t* q, uint8_t* qT, float* s,
+                                       void* stream);
 int fgb_requant_128x1_ue8m0(const uint8_t* q, int64_t R, int64_t C, int64_t ldq,
                             const float* s, int64_t lds,
                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,

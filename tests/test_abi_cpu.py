@@ -30,7 +30,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = fgb.lib()
     names = header_functions()
-    assert len(names) == 31
+    assert len(names) == 33
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fgb.SIGNATURES)
@@ -254,3 +254,20 @@ def test_requant_128x128_ue8m0_validation():
     assert rq2(ldq2T=64) == E_LD
     assert rq2(q=MIS) == E_ALIGN
     assert rq2(K=0) == OK and rq2(N=0) == OK          # empty: nothing to do
+
+
+def qb(E=2, w=A, K=128, N=256, fl=0.0, q=B, qT=D, s=C_):
+    return fgb.lib().fgb_quantize_128x128_batched(E, w, K, N, fl, q, qT, s, None)
+
+
+def test_quantize_128x128_batched_validation():
+    assert qb(K=100) == E_SHAPE
+    assert qb(N=200) == E_SHAPE
+    assert qb(E=-1) == E_SHAPE
+    assert qb(E=65536) == E_SHAPE
+    assert qb(fl=-2.0) == E_ARG
+    assert qb(w=P(0)) == E_NULL
+    assert qb(q=P(0), qT=P(0)) == E_NULL
+    assert qb(s=P(0)) == E_NULL
+    assert qb(w=MIS) == E_ALIGN
+    assert qb(E=0) == OK and qb(K=0) == OK

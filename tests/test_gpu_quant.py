@@ -220,3 +220,22 @@ def test_linear_workload_quantizers_full(orc):
     assert_codes_equal(q, oq, "w q")
     assert_codes_equal(qT, oqT, "w qT")
     assert_scales_equal(s, os_, "w s")
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_128x128_batched_equals_single(orc, ue8m0):
+    """A stack of E weights in one launch: every matrix bit-exact against the
+    oracle's single-matrix quantization (fp32 scales, or E8M0 bytes)."""
+    E, K, N = 3, 256, 384
+    ws = [stress(K, N, 9600 + e) for e in range(E)]
+    w = torch.stack([bf16_dev(x) for x in ws])
+    q, qT, s = fgb.quantize_128x128_batched(w, ue8m0=ue8m0)
+    for e in range(E):
+        if ue8m0:
+            oq, oqT, oe = orc.quantize_128x128_ue8m0(ws[e])
+            os_ = orc.e8m0_decode(oe).astype(np.float32)
+        else:
+            oq, oqT, os_ = orc.quantize_128x128(ws[e])
+        assert_codes_equal(q[e], oq, f"batched q[{e}]")
+        assert_codes_equal(qT[e], oqT, f"batched qT[{e}]")
+        assert_scales_equal(s[e], os_, f"batched s[{e}]")
