@@ -136,6 +136,7 @@ constexpr int kTrStride = 136;   // bytes per staged qT row (128 + 8 to spread b
 
 __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
 
+
 // PO2: the scales written are powers of two (the UE8M0 values, held in fp32).
 // SR: stochastic rounding of every cast with the words of `sr` (element (r, c)
 // of the input draws word (r, c), so q, qT and the dual outputs of one element
@@ -179,12 +180,17 @@ __global__ __launch_bounds__(256) void k_tile128(
     const int64_t cc = c0 + cg * 8;
     const bool cok = cc < C;
 
-    float v[8][8];  // [row i][column k]
+    // The thread's 8x8 patch, V(i, k) = row i, column k: bf16 inputs stay
+    // packed two to a word and are widened where used (exact); requant inputs
+    // are dequantized once into fp32.
+    constexpr bool REQ = MODE == kTileRequant || MODE == kTileRequant128x128;
+    uint32_t vw[REQ ? 1 : 8][4];
+    float vf[REQ ? 8 : 1][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t r = r0 + rg * 8 + i;
         const bool ok = cok && r < R;
-        if constexpr (MODE == kTileRequant || MODE == kTileRequant128x128) {
+        if constexpr (REQ) {
             // dequantize: v = fl32(dec(q) * s) with the row's 1x128 scale, or
             // the tile's scale s_in[i * lds_in + j] for a 128x128 weight tile
             const uint8_t* p = static_cast<const uint8_t*>(in);
@@ -194,14 +200,50 @@ __global__ __launch_bounds__(256) void k_tile128(
                                        : s_in[(int64_t)blockIdx.x * lds_in + blockIdx.y];
             const float2 d0 = e4m3x2_decode<false>(w.x), d1 = e4m3x2_decode<true>(w.x);
             const float2 d2 = e4m3x2_decode<false>(w.y), d3 = e4m3x2_decode<true>(w.y);
-            v[i][0] = d0.x * sr; v[i][1] = d0.y * sr; v[i][2] = d1.x * sr; v[i][3] = d1.y * sr;
-            v[i][4] = d2.x * sr; v[i][5] = d2.y * sr; v[i][6] = d3.x * sr; v[i][7] = d3.y * sr;
+            vf[i][0] = d0.x * sr; vf[i][1] = d0.y * sr; vf[i][2] = d1.x * sr; vf[i][3] = d1.y * sr;
+            vf[i][4] = d2.x * sr; vf[i][5] = d2.y * sr; vf[i][6] = d3.x * sr; vf[i][7] = d3.y * sr;
         } else {
             const uint16_t* p = static_cast<const uint16_t*>(in);
             const uint4 w = ok ? ld16_stream(p + r * ldin + cc) : make_uint4(0u, 0u, 0u, 0u);
-            v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x); v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
-            v[i][4] = bf16_lo(w.z); v[i][5] = bf16_hi(w.z); v[i][6] = bf16_lo(w.w); v[i][7] = bf16_hi(w.w);
+            vw[i][0] = w.x; vw[i][1] = w.y; vw[i][2] = w.z; vw[i][3] = w.w;
         }
+    }
+    auto V = [&](int i, int k) __attribute__((always_inline)) -> float {
+        if constexpr (REQ) return vf[i][k];
+        else return (k & 1) ? bf16_hi(vw[i][k >> 1]) : bf16_lo(vw[i][k >> 1]);
+    };
+
+    // Dual mode, 1x128 part (first: it needs no other thread's values): row r's
+    // tile is the block's 128 columns of row r, held by the 16 lanes that share
+    // rg; their absmax is one DPP reduction.
+    if constexpr (MODE == kTileDual && !SR) {
+        // the 8 row maxima of the patch rows; lane cg = i of the 16-lane row
+        // group then computes row i's scale (one pair of divisions per wave) and
+        // every lane fetches the multiplier of row i from that lane
+        float a_own = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, abs_bits(V(i, k)));
+            m = max16(m);
+            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+        }
+        float sr_own = 0.0f, iv_own;
+        uint32_t er_own = 0;
+        scale_of(a_own, sr_own, er_own, iv_own);
+        const int lane = t & 63;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
+            const int64_t r = r0 + rg * 8 + i;
+            const uint32_t o0 = e4m3x4(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
+            const uint32_t o1 = e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
+            if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
+        }
+        // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
+        const int64_t rr = r0 + rg * 8 + cg;
+        if (cg < 8 && rr < R) put_scale(s_row, (int64_t)blockIdx.y * lds_row + rr, sr_own, er_own);
     }
 
     float inv[8];
@@ -210,7 +252,7 @@ __global__ __launch_bounds__(256) void k_tile128(
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
+            for (int k = 0; k < 8; ++k) m = max(m, abs_bits(V(i, k)));
         m = max16(m);
         m = max(m, shfl_xor_u32(m, 16));
         m = max(m, shfl_xor_u32(m, 32));
@@ -230,7 +272,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         for (int k = 0; k < 8; ++k) {
             uint32_t m = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i][k]));
+            for (int i = 0; i < 8; ++i) m = max(m, abs_bits(V(i, k)));
             m = max(m, shfl_xor_u32(m, 16));
             m = max(m, shfl_xor_u32(m, 32));
             mc[k] = m;
@@ -271,21 +313,21 @@ __global__ __launch_bounds__(256) void k_tile128(
             if constexpr (MODE == kTileDual) {
                 uint32_t m = 0;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
+                for (int k = 0; k < 8; ++k) m = max(m, abs_bits(V(i, k)));
                 m = max16(m);
                 const float a = fmaxf(__uint_as_float(m), amax_floor);
                 float sc, iv;
                 tile_scale(a, sc, iv);
                 if (cg == i) sr_own = sc;
-                const uint32_t o0 = e4m3x4_sr(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv,
+                const uint32_t o0 = e4m3x4_sr(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv,
                                               u[0], u[1], u[2], u[3]);
-                const uint32_t o1 = e4m3x4_sr(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv,
+                const uint32_t o1 = e4m3x4_sr(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv,
                                               u[4], u[5], u[6], u[7]);
                 if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
             }
-            cr[i][0] = e4m3x4_sr(v[i][0] * inv[0], v[i][1] * inv[1], v[i][2] * inv[2], v[i][3] * inv[3],
+            cr[i][0] = e4m3x4_sr(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3],
                                  u[0], u[1], u[2], u[3]);
-            cr[i][1] = e4m3x4_sr(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7],
+            cr[i][1] = e4m3x4_sr(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7],
                                  u[4], u[5], u[6], u[7]);
             if constexpr (TILE) {
                 if (q != nullptr && cok && r < R) st8(q + r * ldq + cc, make_uint2(cr[i][0], cr[i][1]));
@@ -321,46 +363,14 @@ __global__ __launch_bounds__(256) void k_tile128(
         return;
     }
 
-    // Dual mode, 1x128 part: row r's tile is the block's 128 columns of row r,
-    // held by the 16 lanes that share rg; their absmax is one DPP reduction.
-    if constexpr (MODE == kTileDual) {
-        // the 8 row maxima of the patch rows; lane cg = i of the 16-lane row
-        // group then computes row i's scale (one pair of divisions per wave) and
-        // every lane fetches the multiplier of row i from that lane
-        float a_own = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
-            m = max16(m);
-            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
-        }
-        float sr_own = 0.0f, iv_own;
-        uint32_t er_own = 0;
-        scale_of(a_own, sr_own, er_own, iv_own);
-        const int lane = t & 63;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
-            const int64_t r = r0 + rg * 8 + i;
-            const uint32_t o0 = e4m3x4(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
-            const uint32_t o1 = e4m3x4(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
-            if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
-        }
-        // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
-        const int64_t rr = r0 + rg * 8 + cg;
-        if (cg < 8 && rr < R) put_scale(s_row, (int64_t)blockIdx.y * lds_row + rr, sr_own, er_own);
-    }
-
     // Row-major codes (128x128 weights, q != nullptr): 8 bytes per patch row.
     if constexpr (TILE) {
         if (q != nullptr) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t r = r0 + rg * 8 + i;
-                const uint32_t o0 = e4m3x4(v[i][0] * inv[0], v[i][1] * inv[1], v[i][2] * inv[2], v[i][3] * inv[3]);
-                const uint32_t o1 = e4m3x4(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7]);
+                const uint32_t o0 = e4m3x4(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]);
+                const uint32_t o1 = e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
                 if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
             }
         }
@@ -370,8 +380,8 @@ __global__ __launch_bounds__(256) void k_tile128(
     // Transposed codes: column k of the patch -> 8 row bytes, staged in LDS.
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
-        const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
+        const uint32_t lo = e4m3x4(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]);
+        const uint32_t hi = e4m3x4(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]);
         *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
     }
     __syncthreads();
