@@ -38,6 +38,15 @@ instead (32 experts, 8192 tokens routed top-8; gate/up and down projections,
 forward and backward, with the SwiGLU casts fused into the SwiGLU kernels);
 `value` then counts the routed rows' GEMM FLOP.
 
+`--workload quant_stress` times the quantizers alone on the stress tensor
+X [16384, 7168] (per-row scales 10^U(-6,3), signed zeros, zero tiles, tiny and
+subnormal negatives): 1x128, 128x1, 128x128 (both layouts), the fused dual
+cast and the 128x1 requant of the 1x128 codes.  Every launch runs cold: a
+1 GiB read scrub before it (outside its events) evicts L2 and the Infinity
+Cache.  Per kernel the median over the timed steps; `value` is the summed
+algorithmic bytes over the summed medians in GB/s, and `roofline` prices the
+slowest kernel against 8 TB/s.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -95,9 +104,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["linear_dsv3_attn", "moe_grouped"], default="linear_dsv3_attn",
+    p.add_argument("--workload", choices=["linear_dsv3_attn", "moe_grouped", "quant_stress"],
+                   default="linear_dsv3_attn",
                    help="linear_dsv3_attn (default): the DeepSeek-V3 attention projection's linear; "
-                        "moe_grouped: one GPU's MoE expert share as a SwiGLU FFN, fwd+bwd (no CPU baseline)")
+                        "moe_grouped: one GPU's MoE expert share as a SwiGLU FFN, fwd+bwd (no CPU baseline); "
+                        "quant_stress: the quantizers alone on X [16384,7168], cold cache")
     p.add_argument("--recipe", choices=["fp32", "ue8m0"], default="fp32",
                    help="fp32: scales absmax/448 (default); ue8m0: power-of-two scales, applied by the matrix core")
     p.add_argument("--ue8m0-weights", choices=["two-stage", "direct"], default="two-stage",
@@ -339,6 +350,119 @@ def moe_step(fgb, torch, dev, d, bufs=None):
     return [by[n] + lanes.get(n, (0, [])) for n in order]
 
 
+def quant_stress_bytes(R, C):
+    """Algorithmic bytes of each quantizer on X [R, C] (bf16 in; codes, scales out)."""
+    nbR, nbC = -(-R // T), -(-C // T)
+    Rp = nbR * T
+    return {
+        "quantize_1x128": R * C * 2 + R * C + nbC * R * 4,
+        "quantize_128x1": R * C * 2 + C * Rp + nbR * C * 4,
+        "quantize_128x128": R * C * 2 + 2 * R * C + nbR * nbC * 4,
+        "quantize_dual": R * C * 2 + R * C + nbC * R * 4 + C * Rp + nbR * C * 4,
+        "requant_128x1": R * C + nbC * R * 4 + C * Rp + nbR * C * 4,
+    }
+
+
+def quant_stress_main(args, np, torch, fgb, wl):
+    """--workload quant_stress: each quantizer cold, median over the timed steps."""
+    dev = torch.device("cuda:0")
+    d = wl.quant_stress()
+    R, C = d["R"], d["C"]
+    x = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).to(dev).view(torch.bfloat16)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    nbR, nbC = -(-R // T), -(-C // T)
+    Rp = nbR * T
+    b = {"q": torch.empty((R, C), **u8), "s": torch.empty((nbC, R), **f32),
+         "qT": torch.empty((C, Rp), **u8), "sT": torch.empty((nbR, C), **f32),
+         "qw": torch.empty((R, C), **u8), "qwT": torch.empty((C, R), **u8), "sw": torch.empty((nbR, nbC), **f32),
+         "q2": torch.empty((R, C), **u8), "s2": torch.empty((nbC, R), **f32),
+         "qT2": torch.empty((C, Rp), **u8), "sT2": torch.empty((nbR, C), **f32),
+         "rqT": torch.empty((C, Rp), **u8), "rsT": torch.empty((nbR, C), **f32)}
+    ab = quant_stress_bytes(R, C)
+    kernels = [
+        ("quantize_1x128", lambda: fgb.quantize_1x128(x, q=b["q"], s=b["s"])),
+        ("quantize_128x1", lambda: fgb.quantize_128x1(x, qT=b["qT"], sT=b["sT"])),
+        ("quantize_128x128", lambda: fgb.quantize_128x128(x, q=b["qw"], qT=b["qwT"], s=b["sw"])),
+        ("quantize_dual", lambda: fgb.quantize_dual(x, q=b["q2"], s=b["s2"], qT=b["qT2"], sT=b["sT2"])),
+        ("requant_128x1", lambda: fgb.requant_128x1(b["q"], b["s"], qT=b["rqT"], sT=b["rsT"])),
+    ]
+    scrub = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        for _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    times = {name: [] for name, _ in kernels}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name, fn in kernels:
+            torch.sum(scrub, dim=(0,), out=sink)      # 1 GiB read: L2 and Infinity Cache cold
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            times[name].append(a.elapsed_time(e))
+    wall = time.perf_counter() - t0
+    med = {n: float(np.median(v)) for n, v in times.items()}
+    kinfo = {}
+    for n, ms in med.items():
+        rate = ab[n] / (ms * 1e-3)
+        kinfo[n] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
+                    "frac_hbm_peak": round(rate / HBM_PEAK, 4), "bytes": ab[n]}
+    total_ms = sum(med.values())
+    total_b = sum(ab.values())
+    dom = max(med, key=med.get)
+    dom_rate = ab[dom] / (med[dom] * 1e-3)
+    out = {
+        "metric": "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak) + quant GB/s (% HBM) at 1 GPU",
+        "value": round(total_b / (total_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 -> e4m3 codes (u8) + fp32 scales",
+        "data": "synthetic quantization stress tensor (seeded; per-row scales 10^U(-6,3), signed zeros, "
+                "zero tiles, tiny and subnormal negatives; bf16)",
+        "config": {"workload": "quant_stress: X[16384,7168] bf16 through the five quantizers, each launch cold "
+                               "(1 GiB read scrub before it, outside its events); per-kernel median",
+                   "R": R, "C": C, "quant_bytes_per_step": total_b,
+                   "wall_s_incl_scrubs": round(wall, 2)},
+        "quant_frac_hbm_peak": round(total_b / (total_ms * 1e-3) / HBM_PEAK, 4),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_rate / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(dom_rate / HBM_PEAK, 4),
+                     "traffic": traffic_record("stress_" + dom)},
+        "kernels": kinfo,
+    }
+    if args.copy_calibration:
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        c = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=c)
+        torch.cuda.synchronize()
+        del a, c
+    if not args.no_cpu_baseline:
+        import oracle
+        t1 = time.perf_counter()
+        oq, os_ = oracle.quantize_1x128(d["x"])
+        oracle.quantize_128x1(d["x"])
+        oracle.quantize_128x128(d["x"])
+        oracle.quantize_1x128(d["x"])          # the dual cast's two outputs, as two oracle calls
+        oracle.quantize_128x1(d["x"])
+        oracle.requant_128x1(oq, os_)
+        tq = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": round(total_b / tq / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+                               "kind": "oracle",
+                               "sample": f"the whole workload: the five quantizers on the full tensor ({tq:.1f} s; "
+                                         "the dual cast as the 1x128 and 128x1 oracle calls)"}
+    print(json.dumps(out), flush=True)
+
+
 def make_runner(torch, dev, kernels, overlap):
     """step(events=None) launching `kernels` (name, fn, work, lane, deps) once.
     overlap: lane-1 kernels go to a second stream (default priority); a kernel
@@ -386,6 +510,9 @@ def main():
     import fine_grained_block_amd as fgb
     from fine_grained_block_amd import workloads as wl
 
+    if args.workload == "quant_stress":
+        quant_stress_main(args, np, torch, fgb, wl)
+        return
     dev = torch.device("cuda:0")
     if args.workload == "linear_dsv3_attn":
         d = wl.linear_dsv3_attn()
