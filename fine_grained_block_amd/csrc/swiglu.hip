@@ -290,15 +290,20 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             uint2 cgw[4], cuw[4];
             uint4 dw[4];
             float sg[4], su[4];
+            // the thread's first patch row; rows are whole leading dimensions apart
+            const int64_t rp = r0 + rg * 8;
+            const uint8_t* pq = q_gu + rp * ldq_gu + cc;
+            const uint16_t* pd = dh + rp * lddh + cc;
+            const float* ps = s_gu + j * lds_gu + rp;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const int64_t r = r0 + rg * 8 + i0 + ii;
-                const bool ok = r < R;
-                cgw[ii] = ok ? ld8(q_gu + r * ldq_gu + cc) : make_uint2(0u, 0u);
-                dw[ii] = ok ? ld16(dh + r * lddh + cc) : make_uint4(0u, 0u, 0u, 0u);
-                sg[ii] = ok ? s_gu[j * lds_gu + r] : 0.0f;
-                cuw[ii] = (half == 0 && ok) ? ld8(q_gu + r * ldq_gu + F + cc) : make_uint2(0u, 0u);
-                su[ii] = (half == 0 && ok) ? s_gu[(nb + j) * lds_gu + r] : 0.0f;
+                const int i = i0 + ii;
+                const bool ok = rp + i < R;
+                cgw[ii] = ok ? ld8(pq + i * ldq_gu) : make_uint2(0u, 0u);
+                dw[ii] = ok ? ld16(pd + i * lddh) : make_uint4(0u, 0u, 0u, 0u);
+                sg[ii] = ok ? ps[i] : 0.0f;
+                cuw[ii] = (half == 0 && ok) ? ld8(pq + i * ldq_gu + F) : make_uint2(0u, 0u);
+                su[ii] = (half == 0 && ok) ? ps[nb * lds_gu + i] : 0.0f;
             }
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
@@ -348,24 +353,58 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
         }
         __syncthreads();
         if (dgu != nullptr) {
+            uint16_t* po = dgu + (r0 + rg * 8) * lddgu + oc0 + cg * 8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t r = r0 + rg * 8 + i;
                 const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
-                if (r < R) st16(dgu + r * lddgu + oc0 + cg * 8, w);
+                if (r < R) st16(po + i * lddgu, w);
             }
         }
 
-        // phase 2: the thread's patch back from LDS, quantized both ways
+        // phase 2: the thread's patch back from LDS, quantized both ways.  Each
+        // part reads the patch again rather than keeping it in registers across
+        // the barriers of the column scales.
+        auto patch = [&](float (&v)[8][8]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
+                v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x); v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
+                v[i][4] = bf16_lo(w.z); v[i][5] = bf16_hi(w.z); v[i][6] = bf16_lo(w.w); v[i][7] = bf16_hi(w.w);
+            }
+        };
+        float s_own;
+        {
         float v[8][8];
+        patch(v);
+        // 1x128 first (it needs no other thread's values): each row's tile is the
+        // block's 128 columns of that row; lane
+        // cg = i of the 16-lane row group computes row i's scale, the others
+        // fetch its multiplier with a lane shuffle
+        float a_own = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
-            v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x); v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
-            v[i][4] = bf16_lo(w.z); v[i][5] = bf16_hi(w.z); v[i][6] = bf16_lo(w.w); v[i][7] = bf16_hi(w.w);
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+            m = max16(m);
+            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+        }
+        float iv_own;
+        tile_scale(a_own, s_own, iv_own);
+        const int lane = t & 63;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
+            const int64_t r = r0 + rg * 8 + i;
+            if (r < R) st8(q + (r0 + rg * 8) * ldq + oc0 + cg * 8 + i * ldq, make_uint2(codes4(v[i], iv), codes4(v[i] + 4, iv)));
+        }
         }
         // 128x1: column maxima over the block's 128 rows
         uint32_t mc[8];
+        {
+        float v[8][8];
+        patch(v);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             uint32_t m = 0;
@@ -374,6 +413,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             m = max(m, shfl_xor_u32(m, 16));
             m = max(m, shfl_xor_u32(m, 32));
             mc[k] = m;
+        }
         }
         if ((t & 63) < 16) {
 #pragma unroll
@@ -388,27 +428,6 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             col_mul[t] = iv;
             sT[(int64_t)blockIdx.x * ldsT + oc0 + t] = sc;
         }
-        // 1x128: each row's tile is the block's 128 columns of that row; lane
-        // cg = i of the 16-lane row group computes row i's scale, the others
-        // fetch its multiplier with a lane shuffle
-        float a_own = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
-            m = max16(m);
-            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
-        }
-        float s_own, iv_own;
-        tile_scale(a_own, s_own, iv_own);
-        const int lane = t & 63;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
-            const int64_t r = r0 + rg * 8 + i;
-            if (r < R) st8(q + r * ldq + oc0 + cg * 8, make_uint2(codes4(v[i], iv), codes4(v[i] + 4, iv)));
-        }
         __syncthreads();                                   // col_mul written
         float inv[8];
 #pragma unroll
@@ -418,11 +437,15 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             if (cg < 8 && rr < R) s[tile * lds + rr] = s_own;
         }
         // transposed codes through LDS: column k of the patch -> 8 row bytes
+        {
+        float v[8][8];
+        patch(v);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
             const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
             *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
+        }
         }
         __syncthreads();
 #pragma unroll
