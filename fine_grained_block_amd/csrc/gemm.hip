@@ -575,8 +575,8 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             const int64_t col = n0 + wn * WTN + j * 16 + fg * 4;
             if (col >= g.N) continue;
             if constexpr (BF16_OUT) {
-                const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-                const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+                const uint32_t lo = cvt_pk_bf16(acc[i][j][0], acc[i][j][1]);
+                const uint32_t hi = cvt_pk_bf16(acc[i][j][2], acc[i][j][3]);
                 st8(reinterpret_cast<uint16_t*>(outp) + row * g.ldo + col, make_uint2(lo, hi));
             } else {
                 float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(outp) + row * g.ldo + col);
