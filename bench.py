@@ -45,7 +45,9 @@ cast and the 128x1 requant of the 1x128 codes.  Every launch runs cold: a
 1 GiB read scrub before it (outside its events) evicts L2 and the Infinity
 Cache.  Per kernel the median over the timed steps; `value` is the summed
 algorithmic bytes over the summed medians in GB/s, and `roofline` prices the
-slowest kernel against 8 TB/s.
+slowest kernel against 8 TB/s.  `copy_reference` times a plain streaming
+kernel with the 1x128 cast's traffic (2 bytes read, 1 written per element)
+the same way, and each kernel's `frac_of_copy` compares its rate with it.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload W] [--no-cpu-baseline]
 """
@@ -387,6 +389,13 @@ def quant_stress_main(args, np, torch, fgb, wl):
         ("quantize_dual", lambda: fgb.quantize_dual(x, q=b["q2"], s=b["s2"], qT=b["qT2"], sT=b["sT2"])),
         ("requant_128x1", lambda: fgb.requant_128x1(b["q"], b["s"], qT=b["rqT"], sT=b["rsT"])),
     ]
+    # reference: a plain streaming kernel that reads 2 bytes and writes 1 per element of X,
+    # the 1x128 cast's traffic without its arithmetic
+    n_ref = R * C // 4
+    ref_in = torch.ones(2 * n_ref, dtype=torch.float32, device=dev)
+    ref_out = torch.empty(n_ref, dtype=torch.float32, device=dev)
+    kernels.append(("copy_reference", lambda: torch.add(ref_in[:n_ref], ref_in[n_ref:], out=ref_out)))
+    ab["copy_reference"] = 3 * n_ref * 4
     scrub = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
@@ -406,11 +415,15 @@ def quant_stress_main(args, np, torch, fgb, wl):
             times[name].append(a.elapsed_time(e))
     wall = time.perf_counter() - t0
     med = {n: float(np.median(v)) for n, v in times.items()}
+    ref_ms = med.pop("copy_reference")
+    ref_b = ab.pop("copy_reference")
+    ref_rate = ref_b / (ref_ms * 1e-3)
     kinfo = {}
     for n, ms in med.items():
         rate = ab[n] / (ms * 1e-3)
         kinfo[n] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
-                    "frac_hbm_peak": round(rate / HBM_PEAK, 4), "bytes": ab[n]}
+                    "frac_hbm_peak": round(rate / HBM_PEAK, 4), "frac_of_copy": round(rate / ref_rate, 3),
+                    "bytes": ab[n]}
     total_ms = sum(med.values())
     total_b = sum(ab.values())
     dom = max(med, key=med.get)
@@ -438,6 +451,10 @@ def quant_stress_main(args, np, torch, fgb, wl):
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(dom_rate / HBM_PEAK, 4),
                      "traffic": traffic_record("stress_" + dom)},
         "kernels": kinfo,
+        "copy_reference": {"us": round(ref_ms * 1e3, 2), "GB/s": round(ref_rate / 1e9, 1),
+                           "frac_hbm_peak": round(ref_rate / HBM_PEAK, 4), "bytes": ref_b,
+                           "what": "torch add of two fp32 halves into a third: reads 2 and writes 1 byte per "
+                                   "byte of X's elements, cold like the casts"},
     }
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
