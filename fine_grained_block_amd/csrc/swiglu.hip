@@ -375,45 +375,46 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
         };
         float s_own;
         {
-        float v[8][8];
-        patch(v);
-        // 1x128 first (it needs no other thread's values): each row's tile is the
-        // block's 128 columns of that row; lane
-        // cg = i of the 16-lane row group computes row i's scale, the others
-        // fetch its multiplier with a lane shuffle
-        float a_own = 0.0f;
+            float v[8][8];
+            patch(v);
+            // 1x128 first (it needs no other thread's values): each row's tile is
+            // the block's 128 columns of that row; lane cg = i of the 16-lane row
+            // group computes row i's scale, the others fetch its multiplier with
+            // a lane shuffle
+            float a_own = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t m = 0;
+            for (int i = 0; i < 8; ++i) {
+                uint32_t m = 0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
-            m = max16(m);
-            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
-        }
-        float iv_own;
-        tile_scale(a_own, s_own, iv_own);
-        const int lane = t & 63;
+                for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+                m = max16(m);
+                if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+            }
+            float iv_own;
+            tile_scale(a_own, s_own, iv_own);
+            const int lane = t & 63;
+            uint8_t* pq8 = q + (r0 + rg * 8) * ldq + oc0 + cg * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
-            const int64_t r = r0 + rg * 8 + i;
-            if (r < R) st8(q + (r0 + rg * 8) * ldq + oc0 + cg * 8 + i * ldq, make_uint2(codes4(v[i], iv), codes4(v[i] + 4, iv)));
-        }
+            for (int i = 0; i < 8; ++i) {
+                const float iv = __shfl(iv_own, (lane & 48) | i, 64);
+                const int64_t r = r0 + rg * 8 + i;
+                if (r < R) st8(pq8 + i * ldq, make_uint2(codes4(v[i], iv), codes4(v[i] + 4, iv)));
+            }
         }
         // 128x1: column maxima over the block's 128 rows
         uint32_t mc[8];
         {
-        float v[8][8];
-        patch(v);
+            float v[8][8];
+            patch(v);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            uint32_t m = 0;
+            for (int k = 0; k < 8; ++k) {
+                uint32_t m = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
-            m = max(m, shfl_xor_u32(m, 16));
-            m = max(m, shfl_xor_u32(m, 32));
-            mc[k] = m;
-        }
+                for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+                m = max(m, shfl_xor_u32(m, 16));
+                m = max(m, shfl_xor_u32(m, 32));
+                mc[k] = m;
+            }
         }
         if ((t & 63) < 16) {
 #pragma unroll
@@ -438,14 +439,14 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
         }
         // transposed codes through LDS: column k of the patch -> 8 row bytes
         {
-        float v[8][8];
-        patch(v);
+            float v[8][8];
+            patch(v);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
-            const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
-            *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
-        }
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
+                const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
+                *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
+            }
         }
         __syncthreads();
 #pragma unroll
