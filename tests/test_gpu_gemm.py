@@ -288,3 +288,46 @@ def test_zero_gradient_patterns(orc):
     d["dy"] = np.zeros((M, N), np.uint16)
     out = run_linear(d)
     assert torch.all(out["dw"] == 0) and torch.all(out["sdyT"] == 0)
+
+
+# ---------------------------------------------------------------------------
+# operands beyond 4 GiB: the host cuts the output into pieces whose operand
+# slices fit the kernel's 32-bit offsets (rows of X, or columns of W)
+# ---------------------------------------------------------------------------
+
+def big_codes(g, rows, cols):
+    """Random E4M3 codes (no NaN), generated in row chunks to bound host memory."""
+    c = np.empty((rows, cols), np.uint8)
+    step = 1 << 16
+    for r0 in range(0, rows, step):
+        blk = g.integers(0, 256, (min(step, rows - r0), cols), dtype=np.uint8)
+        blk[(blk & 0x7F) == 0x7F] = 0x3C
+        c[r0:r0 + blk.shape[0]] = blk
+    return c
+
+
+@pytest.mark.parametrize("side", ["x_rows", "w_cols"])
+def test_fprop_operand_beyond_4gib(orc, side):
+    """Fprop with one operand of 4.43 GB: X [540672, 8192] (cut after row
+    524288) or W^T [540672, 8192] (cut after column 523264).  Sampled outputs
+    on both sides of the cut against the oracle."""
+    g = np.random.default_rng(4242)
+    K, big, small = 8192, 540672, 256
+    M, N = (big, small) if side == "x_rows" else (small, big)
+    print(f"[{side}] generating {max(M, N) * K / 1e9:.2f} GB of codes", flush=True)
+    qx = big_codes(g, M, K) if side == "x_rows" else rand_codes(g, (M, K))
+    qwT = rand_codes(g, (N, K)) if side == "x_rows" else big_codes(g, N, K)
+    sx, sw = rand_scales(g, (K // T, M)), rand_scales(g, (K // T, N // T))
+    assert max(M, N) * K > (1 << 32)
+    y = fgb.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qwT), f32_dev(sw))
+    torch.cuda.synchronize()
+    cut = 524288 if side == "x_rows" else 523264
+    near = np.array([0, 1, cut - 2, cut - 1, cut, cut + 1, big - 2, big - 1], np.int64)
+    wide = np.unique(np.concatenate([near, g.choice(big, 56, replace=False)]))
+    rows = wide if side == "x_rows" else np.arange(M, dtype=np.int64)[::8]
+    cols = np.arange(N, dtype=np.int64)[::8] if side == "x_rows" else wide
+    r, aabs = orc.gemm_fprop(qx, sx, qwT, sw, rows=rows, cols=cols)
+    ri, ci = torch.as_tensor(rows, device=y.device), torch.as_tensor(cols, device=y.device)
+    got = bf16_host_f64(y[ri][:, ci].contiguous())
+    check_gemm(got, r, aabs, True, f"fprop beyond 4 GiB ({side})",
+               hw_bound_fprop(qx, sx, qwT, sw, rows=rows, cols=cols), K // T)
