@@ -123,10 +123,11 @@ constexpr uint32_t kNeedF64 = 0xFFFFFFFFu;    // "not decided in fp32"
 
 // silu(g) * f: e (2) -> 1 + e (2.5) -> rcp (3.5) -> * g (4) -> * f (4.5 units
 // = 9 ulps of the result); accepted beyond 24 ulps.
-__device__ __forceinline__ uint32_t silu_times_fast(float g, float f) {
+// e = expf(-g) and sig = rcp(1 + e) are passed in, so that silu and silu' of
+// one gate share them (for |g| > 80 they are discarded unused).
+__device__ __forceinline__ uint32_t silu_times_fast(float g, float f, float e, float sig) {
     if (!(fabsf(g) <= 80.0f)) return kNeedF64;
-    const float e = expf(-g);
-    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
+    (void)e;
     const float v = (g * sig) * f;
     return midpoint_distance(v) > 24.0f ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
 }
@@ -136,11 +137,9 @@ __device__ __forceinline__ uint32_t silu_times_fast(float g, float f) {
 // absolute error <= 5 |t| + 1/2 units and the result a relative error
 // <= 8 (1 + |t| / |1 + t|) units (<= 2^-20 (1 + |t|/|1+t|)); accepted beyond
 // twice that in ulps, plus 8.
-__device__ __forceinline__ uint32_t dsilu_times_fast(float g, float d, float u) {
+__device__ __forceinline__ uint32_t dsilu_times_fast(float g, float d, float u, float e, float sig) {
     const float f = d * u;
     if (!(fabsf(g) <= 80.0f) || !(f == 0.0f || fabsf(f) >= 0x1p-134f)) return kNeedF64;
-    const float e = expf(-g);
-    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
     const float t = g * (e * sig);
     const float s1 = 1.0f + t;
     const float v = (sig * s1) * f;
@@ -150,8 +149,16 @@ __device__ __forceinline__ uint32_t dsilu_times_fast(float g, float d, float u) 
     return midpoint_distance(v) > margin ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
 }
 
+// the sigmoid pieces of the fast paths: e = expf(-g), sig = rcp(1 + e)
+__device__ __forceinline__ void sigmoid_pieces(float g, float& e, float& sig) {
+    e = expf(-g);
+    sig = __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ uint32_t silu_times(float g, float f) {
-    const uint32_t r = silu_times_fast(g, f);
+    float e, sig;
+    sigmoid_pieces(g, e, sig);
+    const uint32_t r = silu_times_fast(g, f, e, sig);
     return r != kNeedF64 ? r : silu_times_f64(g, f);
 }
 
@@ -246,14 +253,15 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
 // ---------------------------------------------------------------------------
 // Backward.  A block of 256 threads covers 128 rows and one 128-column gate
 // tile j and produces two output tiles, dG (columns 128j..) and dU
-// (F + 128j..), one after the other.  For each: phase 1 forms the tile's bf16
-// values row by row (thread t: rows r0 + 8*(t/16) + i, columns 8*(t%16) ..+8)
-// into a 128 x 128 bf16 tile in LDS; phase 2 reads back the thread's 8 x 8
-// patch and quantizes it both ways: 1x128 (row maxima: one DPP max per
-// 16-lane row group) and 128x1 (column maxima: lane swizzles plus LDS; codes
-// transposed through LDS so every qT store is a 16-byte piece of a 128-byte
-// row).  Phase 1 keeps only one row of inputs live, so the fp64 fallback can
-// be a call.
+// (F + 128j..).  Phase 1 forms both tiles' bf16 values row by row (thread t:
+// rows r0 + 8*(t/16) + i, columns 8*(t%16) ..+8; dG and dU of an element share
+// its sigmoid) into two 128 x 128 bf16 tiles in LDS.  Phase 2, once per tile,
+// reads back the thread's 8 x 8 patch and quantizes it both ways: 1x128 (row
+// maxima: one DPP max per 16-lane row group) and 128x1 (column maxima: lane
+// swizzles plus LDS; codes transposed through LDS, over the dG tile once it
+// has been read, so every qT store is a 16-byte piece of a 128-byte row).
+// Phase 1 keeps only four rows of inputs live, so the fp64 fallback can be a
+// call.
 // ---------------------------------------------------------------------------
 constexpr int kSwTr = 136;   // bytes per staged qT row
 
@@ -267,8 +275,11 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
 {
     __shared__ uint32_t red[4][kTile];
     __shared__ float col_mul[kTile];
-    __shared__ __attribute__((aligned(16))) uint8_t tr[kTile * kSwTr];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[kTile * kTile];   // the tile's bf16 values
+    // both output tiles' bf16 values (dG in vt[0], dU in vt[1]); the staged
+    // transposed codes reuse vt[0] once its values have been read
+    __shared__ __attribute__((aligned(16))) uint16_t vt[2][kTile * kTile];
+    uint8_t* const tr = reinterpret_cast<uint8_t*>(&vt[0][0]);
+    static_assert(kTile * kSwTr <= (int)sizeof(vt[0]), "staged codes fit one value tile");
 
     const int t = threadIdx.x;
     const int cg = t & 15, rg = t >> 4, wave = t >> 6;
@@ -277,87 +288,103 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
     const int64_t nb = F / kTile;
     const int64_t cc = j * kTile + cg * 8;             // gate column; up column F + cc
 
-    for (int half = 0; half < 2; ++half) {
-        const int64_t oc0 = (half == 0 ? 0 : F) + j * kTile;      // first output column of the tile
-        const int64_t tile = (half == 0 ? 0 : nb) + j;            // its 1x128 block index
-
-        // phase 1: G~ = bf16(fl32(dec(q) s)), U~ likewise, dH; the tile's values.
-        // 1a: four rows at a time, their raw inputs first, then every value whose
-        // fp32 form decides its bf16 rounding; `need` marks the others (bit 8 i + k).
-        uint64_t need = 0;
+    // phase 1: G~ = bf16(fl32(dec(q) s)), U~ likewise, dH; both tiles' values
+    // from one pass (dG and dU of an element share its sigmoid).  1a: four rows
+    // at a time, their raw inputs first, then every value whose fp32 form
+    // decides its bf16 rounding; need[h] marks the others (bit 8 i + k).
+    uint64_t need[2] = {0, 0};
 #pragma unroll 1
-        for (int i0 = 0; i0 < 8; i0 += 4) {
-            uint2 cgw[4], cuw[4];
-            uint4 dw[4];
-            float sg[4], su[4];
-            // the thread's first patch row; rows are whole leading dimensions apart
-            const int64_t rp = r0 + rg * 8;
-            const uint8_t* pq = q_gu + rp * ldq_gu + cc;
-            const uint16_t* pd = dh + rp * lddh + cc;
-            const float* ps = s_gu + j * lds_gu + rp;
+    for (int i0 = 0; i0 < 8; i0 += 4) {
+        uint2 cgw[4], cuw[4];
+        uint4 dw[4];
+        float sg[4], su[4];
+        // the thread's first patch row; rows are whole leading dimensions apart
+        const int64_t rp = r0 + rg * 8;
+        const uint8_t* pq = q_gu + rp * ldq_gu + cc;
+        const uint16_t* pd = dh + rp * lddh + cc;
+        const float* ps = s_gu + j * lds_gu + rp;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int i = i0 + ii;
-                const bool ok = rp + i < R;
-                cgw[ii] = ok ? ld8(pq + i * ldq_gu) : make_uint2(0u, 0u);
-                dw[ii] = ok ? ld16(pd + i * lddh) : make_uint4(0u, 0u, 0u, 0u);
-                sg[ii] = ok ? ps[i] : 0.0f;
-                cuw[ii] = (half == 0 && ok) ? ld8(pq + i * ldq_gu + F) : make_uint2(0u, 0u);
-                su[ii] = (half == 0 && ok) ? ps[nb * lds_gu + i] : 0.0f;
-            }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int i = i0 + ii;
-                const float2 g0 = e4m3x2_decode<false>(cgw[ii].x), g1 = e4m3x2_decode<true>(cgw[ii].x);
-                const float2 g2 = e4m3x2_decode<false>(cgw[ii].y), g3 = e4m3x2_decode<true>(cgw[ii].y);
-                const float gd[8] = {g0.x, g0.y, g1.x, g1.y, g2.x, g2.y, g3.x, g3.y};
-                const float2 u0 = e4m3x2_decode<false>(cuw[ii].x), u1 = e4m3x2_decode<true>(cuw[ii].x);
-                const float2 u2 = e4m3x2_decode<false>(cuw[ii].y), u3 = e4m3x2_decode<true>(cuw[ii].y);
-                const float ud[8] = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
-                const uint32_t dd[4] = {dw[ii].x, dw[ii].y, dw[ii].z, dw[ii].w};
-                uint32_t w[4];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float g = bf16_value(f32_to_bf16_rne(gd[k] * sg[ii]));
-                    const float d = (k & 1) ? bf16_hi(dd[k >> 1]) : bf16_lo(dd[k >> 1]);
-                    uint32_t r;
-                    if (half == 0) r = dsilu_times_fast(g, d, bf16_value(f32_to_bf16_rne(ud[k] * su[ii])));
-                    else r = silu_times_fast(g, d);
-                    if (r == kNeedF64) {
-                        need |= 1ull << (8 * i + k);
-                        r = 0;
-                    }
-                    if (k & 1) w[k >> 1] |= r << 16;
-                    else w[k >> 1] = r;
-                }
-                *reinterpret_cast<uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]) = make_uint4(w[0], w[1], w[2], w[3]);
-            }
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = i0 + ii;
+            const bool ok = rp + i < R;
+            cgw[ii] = ok ? ld8(pq + i * ldq_gu) : make_uint2(0u, 0u);
+            dw[ii] = ok ? ld16(pd + i * lddh) : make_uint4(0u, 0u, 0u, 0u);
+            sg[ii] = ok ? ps[i] : 0.0f;
+            cuw[ii] = ok ? ld8(pq + i * ldq_gu + F) : make_uint2(0u, 0u);
+            su[ii] = ok ? ps[nb * lds_gu + i] : 0.0f;
         }
-        // 1b: the marked values in fp64, one at a time
-        while (need != 0) {
-            const int idx = __builtin_ctzll(need);
-            need &= need - 1;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = i0 + ii;
+            const float2 g0 = e4m3x2_decode<false>(cgw[ii].x), g1 = e4m3x2_decode<true>(cgw[ii].x);
+            const float2 g2 = e4m3x2_decode<false>(cgw[ii].y), g3 = e4m3x2_decode<true>(cgw[ii].y);
+            const float gd[8] = {g0.x, g0.y, g1.x, g1.y, g2.x, g2.y, g3.x, g3.y};
+            const float2 u0 = e4m3x2_decode<false>(cuw[ii].x), u1 = e4m3x2_decode<true>(cuw[ii].x);
+            const float2 u2 = e4m3x2_decode<false>(cuw[ii].y), u3 = e4m3x2_decode<true>(cuw[ii].y);
+            const float ud[8] = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
+            const uint32_t dd[4] = {dw[ii].x, dw[ii].y, dw[ii].z, dw[ii].w};
+            uint32_t wg[4], wu[4];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float g = bf16_value(f32_to_bf16_rne(gd[k] * sg[ii]));
+                const float d = (k & 1) ? bf16_hi(dd[k >> 1]) : bf16_lo(dd[k >> 1]);
+                float e, sig;
+                sigmoid_pieces(g, e, sig);
+                uint32_t rg_ = dsilu_times_fast(g, d, bf16_value(f32_to_bf16_rne(ud[k] * su[ii])), e, sig);
+                uint32_t ru = silu_times_fast(g, d, e, sig);
+                if (rg_ == kNeedF64) {
+                    need[0] |= 1ull << (8 * i + k);
+                    rg_ = 0;
+                }
+                if (ru == kNeedF64) {
+                    need[1] |= 1ull << (8 * i + k);
+                    ru = 0;
+                }
+                if (k & 1) {
+                    wg[k >> 1] |= rg_ << 16;
+                    wu[k >> 1] |= ru << 16;
+                } else {
+                    wg[k >> 1] = rg_;
+                    wu[k >> 1] = ru;
+                }
+            }
+            *reinterpret_cast<uint4*>(&vt[0][(rg * 8 + i) * kTile + cg * 8]) = make_uint4(wg[0], wg[1], wg[2], wg[3]);
+            *reinterpret_cast<uint4*>(&vt[1][(rg * 8 + i) * kTile + cg * 8]) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
+        }
+    }
+    // 1b: the marked values in fp64, one at a time
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        while (need[h] != 0) {
+            const int idx = __builtin_ctzll(need[h]);
+            need[h] &= need[h] - 1;
             const int i = idx >> 3, k = idx & 7;
             const int64_t r = r0 + rg * 8 + i;          // marked values lie in valid rows
             const float g = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + cc + k]) * s_gu[j * lds_gu + r]));
             const float d = bf16_value(dh[r * lddh + cc + k]);
             uint32_t v;
-            if (half == 0) {
+            if (h == 0) {
                 const float u = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + F + cc + k]) *
                                                            s_gu[(nb + j) * lds_gu + r]));
                 v = dsilu_times_f64(g, d, u);
             } else {
                 v = silu_times_f64(g, d);
             }
-            vt[(rg * 8 + i) * kTile + cg * 8 + k] = (uint16_t)v;
+            vt[h][(rg * 8 + i) * kTile + cg * 8 + k] = (uint16_t)v;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+
+    for (int half = 0; half < 2; ++half) {
+        const int64_t oc0 = (half == 0 ? 0 : F) + j * kTile;      // first output column of the tile
+        const int64_t tile = (half == 0 ? 0 : nb) + j;            // its 1x128 block index
+        const uint16_t* vh = vt[half];
         if (dgu != nullptr) {
             uint16_t* po = dgu + (r0 + rg * 8) * lddgu + oc0 + cg * 8;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t r = r0 + rg * 8 + i;
-                const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
+                const uint4 w = *reinterpret_cast<const uint4*>(&vh[(rg * 8 + i) * kTile + cg * 8]);
                 if (r < R) st16(po + i * lddgu, w);
             }
         }
@@ -368,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
         auto patch = [&](float (&v)[8][8]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint4 w = *reinterpret_cast<const uint4*>(&vt[(rg * 8 + i) * kTile + cg * 8]);
+                const uint4 w = *reinterpret_cast<const uint4*>(&vh[(rg * 8 + i) * kTile + cg * 8]);
                 v[i][0] = bf16_lo(w.x); v[i][1] = bf16_hi(w.x); v[i][2] = bf16_lo(w.y); v[i][3] = bf16_hi(w.y);
                 v[i][4] = bf16_lo(w.z); v[i][5] = bf16_hi(w.z); v[i][6] = bf16_lo(w.w); v[i][7] = bf16_hi(w.w);
             }
@@ -437,10 +464,13 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             const int64_t rr = r0 + rg * 8 + cg;
             if (cg < 8 && rr < R) s[tile * lds + rr] = s_own;
         }
-        // transposed codes through LDS: column k of the patch -> 8 row bytes
+        // transposed codes through LDS: column k of the patch -> 8 row bytes.  The
+        // staged codes overlay vt[0]: for the first tile every thread reads its
+        // patch before any thread writes there.
         {
             float v[8][8];
             patch(v);
+            if (half == 0) __syncthreads();
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
