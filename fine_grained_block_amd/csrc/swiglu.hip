@@ -323,14 +323,23 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             const float2 u2 = e4m3x2_decode<false>(cuw[ii].y), u3 = e4m3x2_decode<true>(cuw[ii].y);
             const float ud[8] = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
             const uint32_t dd[4] = {dw[ii].x, dw[ii].y, dw[ii].z, dw[ii].w};
+            // G~ and U~ of the row's 8 columns, rounded to bf16 two at a time by
+            // the hardware converter (finite values: the same RNE as the integer form)
+            uint32_t gb[4], ub[4];
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                gb[k2] = cvt_pk_bf16(gd[2 * k2] * sg[ii], gd[2 * k2 + 1] * sg[ii]);
+                ub[k2] = cvt_pk_bf16(ud[2 * k2] * su[ii], ud[2 * k2 + 1] * su[ii]);
+            }
             uint32_t wg[4], wu[4];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float g = bf16_value(f32_to_bf16_rne(gd[k] * sg[ii]));
+                const float g = (k & 1) ? bf16_hi(gb[k >> 1]) : bf16_lo(gb[k >> 1]);
+                const float u = (k & 1) ? bf16_hi(ub[k >> 1]) : bf16_lo(ub[k >> 1]);
                 const float d = (k & 1) ? bf16_hi(dd[k >> 1]) : bf16_lo(dd[k >> 1]);
                 float e, sig;
                 sigmoid_pieces(g, e, sig);
-                uint32_t rg_ = dsilu_times_fast(g, d, bf16_value(f32_to_bf16_rne(ud[k] * su[ii])), e, sig);
+                uint32_t rg_ = dsilu_times_fast(g, d, u, e, sig);
                 uint32_t ru = silu_times_fast(g, d, e, sig);
                 if (rg_ == kNeedF64) {
                     need[0] |= 1ull << (8 * i + k);
