@@ -531,7 +531,7 @@ def make_runner(torch, dev, kernels, overlap):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only).", file=sys.stderr)
         sys.exit(2)
 

@@ -70,7 +70,7 @@ typedef enum {
     FGB_E_SHAPE = -2,       /* a dimension is negative or violates a multiple-of rule */
     FGB_E_ALIGN = -3,       /* a pointer or leading dimension is misaligned      */
     FGB_E_LD = -4,          /* a leading dimension is smaller than required     */
-    FGB_E_UNSUPPORTED = -5, /* a valid request this build does not implement    */
+    FGB_E_UNSUPPORTED = -5, /* a valid request this library does not implement  */
     FGB_E_HIP = -6,         /* the HIP runtime reported an error at launch      */
     FGB_E_ARG = -7          /* another invalid argument (e.g. a negative floor)  */
 } fgb_status;
