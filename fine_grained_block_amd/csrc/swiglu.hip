@@ -125,11 +125,18 @@ constexpr uint32_t kNeedF64 = 0xFFFFFFFFu;    // "not decided in fp32"
 // = 9 ulps of the result); accepted beyond 24 ulps.
 // e = expf(-g) and sig = rcp(1 + e) are passed in, so that silu and silu' of
 // one gate share them (for |g| > 80 they are discarded unused).
-__device__ __forceinline__ uint32_t silu_times_fast(float g, float f, float e, float sig) {
-    if (!(fabsf(g) <= 80.0f)) return kNeedF64;
-    (void)e;
+// The _v forms return the fp32 value and whether its bf16 rounding is decided;
+// the others return the bf16 bits or kNeedF64.
+__device__ __forceinline__ float silu_times_fast_v(float g, float f, float sig, bool& ok) {
     const float v = (g * sig) * f;
-    return midpoint_distance(v) > 24.0f ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
+    ok = fabsf(g) <= 80.0f && midpoint_distance(v) > 24.0f;
+    return v;
+}
+__device__ __forceinline__ uint32_t silu_times_fast(float g, float f, float e, float sig) {
+    (void)e;
+    bool ok;
+    const float v = silu_times_fast_v(g, f, sig, ok);
+    return ok ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
 }
 
 // silu'(g) * d * u = sigma (1 + t) f, t = g e sigma, f = d u (exact in fp32 for
@@ -137,16 +144,16 @@ __device__ __forceinline__ uint32_t silu_times_fast(float g, float f, float e, f
 // absolute error <= 5 |t| + 1/2 units and the result a relative error
 // <= 8 (1 + |t| / |1 + t|) units (<= 2^-20 (1 + |t|/|1+t|)); accepted beyond
 // twice that in ulps, plus 8.
-__device__ __forceinline__ uint32_t dsilu_times_fast(float g, float d, float u, float e, float sig) {
+__device__ __forceinline__ float dsilu_times_fast_v(float g, float d, float u, float e, float sig, bool& ok) {
     const float f = d * u;
-    if (!(fabsf(g) <= 80.0f) || !(f == 0.0f || fabsf(f) >= 0x1p-134f)) return kNeedF64;
     const float t = g * (e * sig);
     const float s1 = 1.0f + t;
     const float v = (sig * s1) * f;
     const float ratio = fabsf(t) * __builtin_amdgcn_rcpf(fabsf(s1)) * 1.0001f;
-    if (!(ratio < 1024.0f)) return kNeedF64;
     const float margin = 2.0f * 0x1p-20f * (1.0f + ratio) * 0x1p24f + 8.0f;
-    return midpoint_distance(v) > margin ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
+    ok = fabsf(g) <= 80.0f && (f == 0.0f || fabsf(f) >= 0x1p-134f) && ratio < 1024.0f &&
+         midpoint_distance(v) > margin;
+    return v;
 }
 
 // the sigmoid pieces of the fast paths: e = expf(-g), sig = rcp(1 + e)
@@ -332,6 +339,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
                 ub[k2] = cvt_pk_bf16(ud[2 * k2] * su[ii], ud[2 * k2 + 1] * su[ii]);
             }
             uint32_t wg[4], wu[4];
+            float vg[8], vu[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const float g = (k & 1) ? bf16_hi(gb[k >> 1]) : bf16_lo(gb[k >> 1]);
@@ -339,23 +347,22 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
                 const float d = (k & 1) ? bf16_hi(dd[k >> 1]) : bf16_lo(dd[k >> 1]);
                 float e, sig;
                 sigmoid_pieces(g, e, sig);
-                uint32_t rg_ = dsilu_times_fast(g, d, u, e, sig);
-                uint32_t ru = silu_times_fast(g, d, e, sig);
-                if (rg_ == kNeedF64) {
-                    need[0] |= 1ull << (8 * i + k);
-                    rg_ = 0;
-                }
-                if (ru == kNeedF64) {
-                    need[1] |= 1ull << (8 * i + k);
-                    ru = 0;
-                }
-                if (k & 1) {
-                    wg[k >> 1] |= rg_ << 16;
-                    wu[k >> 1] |= ru << 16;
-                } else {
-                    wg[k >> 1] = rg_;
-                    wu[k >> 1] = ru;
-                }
+                bool okg, oku;
+                vg[k] = dsilu_times_fast_v(g, d, u, e, sig, okg);
+                vu[k] = silu_times_fast_v(g, d, sig, oku);
+                if (!okg) need[0] |= 1ull << (8 * i + k);
+                if (!oku) need[1] |= 1ull << (8 * i + k);
+            }
+            // decided values rounded two at a time by the hardware converter (the
+            // same RNE as the integer form for finite values); the others stay 0
+            // for the fp64 pass
+            const uint32_t mg = (uint32_t)(need[0] >> (8 * i)) & 0xFFu, mu = (uint32_t)(need[1] >> (8 * i)) & 0xFFu;
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const uint32_t keep_g = ((mg >> (2 * k2)) & 1u ? 0u : 0x0000FFFFu) | ((mg >> (2 * k2 + 1)) & 1u ? 0u : 0xFFFF0000u);
+                const uint32_t keep_u = ((mu >> (2 * k2)) & 1u ? 0u : 0x0000FFFFu) | ((mu >> (2 * k2 + 1)) & 1u ? 0u : 0xFFFF0000u);
+                wg[k2] = cvt_pk_bf16(vg[2 * k2], vg[2 * k2 + 1]) & keep_g;
+                wu[k2] = cvt_pk_bf16(vu[2 * k2], vu[2 * k2 + 1]) & keep_u;
             }
             *reinterpret_cast<uint4*>(&vt[0][(rg * 8 + i) * kTile + cg * 8]) = make_uint4(wg[0], wg[1], wg[2], wg[3]);
             *reinterpret_cast<uint4*>(&vt[1][(rg * 8 + i) * kTile + cg * 8]) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
