@@ -119,24 +119,17 @@ __device__ __forceinline__ float midpoint_distance(float v) {
 // multiply <= 1/2.  A result is accepted when its distance to the nearest bf16
 // midpoint, in fp32 ulps of the result (at most 2^24 per unit relative error),
 // exceeds twice its error bound; otherwise the fp64 path decides.
-constexpr uint32_t kNeedF64 = 0xFFFFFFFFu;    // "not decided in fp32"
 
 // silu(g) * f: e (2) -> 1 + e (2.5) -> rcp (3.5) -> * g (4) -> * f (4.5 units
 // = 9 ulps of the result); accepted beyond 24 ulps.
 // e = expf(-g) and sig = rcp(1 + e) are passed in, so that silu and silu' of
 // one gate share them (for |g| > 80 they are discarded unused).
-// The _v forms return the fp32 value and whether its bf16 rounding is decided;
-// the others return the bf16 bits or kNeedF64.
+// The fast paths return the fp32 value and whether its bf16 rounding is
+// decided by it; undecided values go to the fp64 forms.
 __device__ __forceinline__ float silu_times_fast_v(float g, float f, float sig, bool& ok) {
     const float v = (g * sig) * f;
     ok = fabsf(g) <= 80.0f && midpoint_distance(v) > 24.0f;
     return v;
-}
-__device__ __forceinline__ uint32_t silu_times_fast(float g, float f, float e, float sig) {
-    (void)e;
-    bool ok;
-    const float v = silu_times_fast_v(g, f, sig, ok);
-    return ok ? (f32_to_bf16_rne(v) & 0xFFFFu) : kNeedF64;
 }
 
 // silu'(g) * d * u = sigma (1 + t) f, t = g e sigma, f = d u (exact in fp32 for
@@ -162,12 +155,6 @@ __device__ __forceinline__ void sigmoid_pieces(float g, float& e, float& sig) {
     sig = __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-__device__ __forceinline__ uint32_t silu_times(float g, float f) {
-    float e, sig;
-    sigmoid_pieces(g, e, sig);
-    const uint32_t r = silu_times_fast(g, f, e, sig);
-    return r != kNeedF64 ? r : silu_times_f64(g, f);
-}
 
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
@@ -235,13 +222,31 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
             }
         }
         // H = bf16(silu(G) U), then its 1x128 tile b
-        uint32_t hb[8];
+        // (decided values rounded two at a time by the hardware converter -- the
+        // same RNE as the integer form for finite values; the others in fp64)
+        float vh[8];
+        bool okh[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float e, sig;
+            sigmoid_pieces(g[k], e, sig);
+            vh[k] = silu_times_fast_v(g[k], u[k], sig, okh[k]);
+        }
+        uint32_t hw[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) hw[k2] = cvt_pk_bf16(vh[2 * k2], vh[2 * k2 + 1]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (!okh[k]) {
+                const uint32_t v = silu_times_f64(g[k], u[k]);
+                hw[k >> 1] = (k & 1) ? ((hw[k >> 1] & 0xFFFFu) | (v << 16)) : ((hw[k >> 1] & 0xFFFF0000u) | v);
+            }
+        }
         float hv[8];
         uint32_t mh = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            hb[k] = silu_times(g[k], u[k]);
-            hv[k] = bf16_value(hb[k]);
+            hv[k] = (k & 1) ? bf16_hi(hw[k >> 1]) : bf16_lo(hw[k >> 1]);
             mh = max(mh, __float_as_uint(hv[k]) & 0x7FFFFFFFu);
         }
         mh = max16(mh);
@@ -251,8 +256,7 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
             st8(q_h + r * ldq_h + c, make_uint2(codes4(hv, ih), codes4(hv + 4, ih)));
             if (lane16 == 0) s_h[b * lds_h + r] = sh;
             if (h_out != nullptr)
-                st16(h_out + r * ldh + c, make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
-                                                     hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)));
+                st16(h_out + r * ldh + c, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         }
     }
 }
