@@ -291,6 +291,10 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
     __shared__ __attribute__((aligned(16))) uint16_t vt[2][kTile * kTile];
     uint8_t* const tr = reinterpret_cast<uint8_t*>(&vt[0][0]);
     static_assert(kTile * kSwTr <= (int)sizeof(vt[0]), "staged codes fit one value tile");
+    // values the fp32 path leaves undecided: (tile << 14) | (row << 7) | column
+    constexpr int kFbMax = 1024;
+    __shared__ uint16_t fb_list[kFbMax];
+    __shared__ uint32_t fb_count;
 
     const int t = threadIdx.x;
     const int cg = t & 15, rg = t >> 4, wave = t >> 6;
@@ -304,6 +308,8 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
     // at a time, their raw inputs first, then every value whose fp32 form
     // decides its bf16 rounding; need[h] marks the others (bit 8 i + k).
     uint64_t need[2] = {0, 0};
+    if (t == 0) fb_count = 0;
+    __syncthreads();                                     // the count is zero before any thread adds to it
 #pragma unroll 1
     for (int i0 = 0; i0 < 8; i0 += 4) {
         uint2 cgw[4], cuw[4];
@@ -372,25 +378,54 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             *reinterpret_cast<uint4*>(&vt[1][(rg * 8 + i) * kTile + cg * 8]) = make_uint4(wu[0], wu[1], wu[2], wu[3]);
         }
     }
-    // 1b: the marked values in fp64, one at a time
+    // 1b: the marked values in fp64.  They are rare but scattered, so a lane
+    // would serialize its wave on them: the block gathers them into one list
+    // and spreads it over all threads.  Marks beyond the list's room stay with
+    // their thread.
+    auto fallback = [&](int h, int row, int col) __attribute__((always_inline)) {
+        const int64_t r = r0 + row;                      // marked values lie in valid rows
+        const int64_t c = j * kTile + col;
+        const float g = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + c]) * s_gu[j * lds_gu + r]));
+        const float d = bf16_value(dh[r * lddh + c]);
+        uint32_t v;
+        if (h == 0) {
+            const float u = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + F + c]) *
+                                                       s_gu[(nb + j) * lds_gu + r]));
+            v = dsilu_times_f64(g, d, u);
+        } else {
+            v = silu_times_f64(g, d);
+        }
+        vt[h][row * kTile + col] = (uint16_t)v;
+    };
+    {
+        const uint32_t cnt = (uint32_t)(__builtin_popcountll(need[0]) + __builtin_popcountll(need[1]));
+        uint32_t at = cnt ? atomicAdd(&fb_count, cnt) : 0u;
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            uint64_t m = need[h];
+            while (m != 0 && at < (uint32_t)kFbMax) {
+                const int idx = __builtin_ctzll(m);
+                m &= m - 1;
+                fb_list[at++] = (uint16_t)((h << 14) | ((rg * 8 + (idx >> 3)) << 7) | (cg * 8 + (idx & 7)));
+            }
+            need[h] = m;                                 // what did not fit
+        }
+    }
+    __syncthreads();
+    {
+        const uint32_t n = fb_count < (uint32_t)kFbMax ? fb_count : (uint32_t)kFbMax;
+#pragma unroll 1
+        for (uint32_t e = (uint32_t)t; e < n; e += 256u) {
+            const uint32_t code = fb_list[e];
+            fallback((int)(code >> 14), (int)((code >> 7) & 127u), (int)(code & 127u));
+        }
+    }
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
         while (need[h] != 0) {
             const int idx = __builtin_ctzll(need[h]);
             need[h] &= need[h] - 1;
-            const int i = idx >> 3, k = idx & 7;
-            const int64_t r = r0 + rg * 8 + i;          // marked values lie in valid rows
-            const float g = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + cc + k]) * s_gu[j * lds_gu + r]));
-            const float d = bf16_value(dh[r * lddh + cc + k]);
-            uint32_t v;
-            if (h == 0) {
-                const float u = bf16_value(f32_to_bf16_rne(e4m3_decode1(q_gu[r * ldq_gu + F + cc + k]) *
-                                                           s_gu[(nb + j) * lds_gu + r]));
-                v = dsilu_times_f64(g, d, u);
-            } else {
-                v = silu_times_f64(g, d);
-            }
-            vt[h][(rg * 8 + i) * kTile + cg * 8 + k] = (uint16_t)v;
+            fallback(h, rg * 8 + (idx >> 3), cg * 8 + (idx & 7));
         }
     }
     __syncthreads();
