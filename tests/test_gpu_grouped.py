@@ -9,7 +9,8 @@ import fine_grained_block_amd as fgb
 from fine_grained_block_amd import workloads as wl
 
 from parity import (assert_codes_equal, assert_scales_equal, bf16_dev, bf16_host_f64, check_gemm, f32_dev,
-                    host, hw_bound_dgrad, hw_bound_fprop, hw_bound_wgrad, sample_idx, u8_dev)
+                    host, hw_bound_dgrad, hw_bound_fprop, hw_bound_wgrad, model_dgrad, model_fprop,
+                    model_grouped_rows, model_grouped_wgrad, sample_idx, u8_dev)
 
 pytestmark = pytest.mark.gpu
 T = 128
@@ -85,11 +86,14 @@ def test_grouped_small_full(orc, loads):
             hww[e] = hw_bound_wgrad(oqxT[:, a:b], osxT[a // T:b // T], oqdyT[:, a:b], osdyT[a // T:b // T], b - a)
     nbw = max(1, max(int(offsets[e + 1] - offsets[e]) // T for e in range(len(loads))))
     r, aabs = orc.gemm_fprop_grouped(offsets, oqx, osx, oqwT, osw)
-    check_gemm(bf16_host_f64(y), r, aabs, True, f"fprop grouped {loads}", hwf, K // T)
+    check_gemm(bf16_host_f64(y), r, aabs, True, f"fprop grouped {loads}", hwf, K // T,
+               model=model_grouped_rows(offsets, model_fprop, oqx, osx, oqwT, osw))
     r, aabs = orc.gemm_dgrad_grouped(offsets, oqdy, osdy, oqw, osw)
-    check_gemm(bf16_host_f64(dx), r, aabs, True, f"dgrad grouped {loads}", hwd, N // T)
+    check_gemm(bf16_host_f64(dx), r, aabs, True, f"dgrad grouped {loads}", hwd, N // T,
+               model=model_grouped_rows(offsets, model_dgrad, oqdy, osdy, oqw, osw))
     r, aabs = orc.gemm_wgrad_grouped(offsets, oqxT, osxT, oqdyT, osdyT)
-    check_gemm(host(dw).reshape(r.shape), r, aabs, False, f"wgrad grouped {loads}", hww, nbw)
+    check_gemm(host(dw).reshape(r.shape), r, aabs, False, f"wgrad grouped {loads}", hww, nbw,
+               model=model_grouped_wgrad(offsets, oqxT, osxT, oqdyT, osdyT))
     for e, n in enumerate(loads):
         if n == 0:
             assert torch.all(dw[e] == 0)
@@ -157,18 +161,21 @@ def test_moe_gate_up_sampled(orc, moe):
         cols = sample_idx(N, 48, e + 100)
         r, aabs = orc.gemm_fprop(oqx[a:b], osx[:, a:b], oqT, os_, rows - a, cols)
         hw = hw_bound_fprop(oqx[a:b], osx[:, a:b], oqT, os_, rows - a, cols)
-        check_gemm(yh[np.ix_(rows, cols)], r, aabs, True, f"moe fprop e{e}", hw, K // T)
+        check_gemm(yh[np.ix_(rows, cols)], r, aabs, True, f"moe fprop e{e}", hw, K // T,
+                   model=model_fprop(oqx[a:b], osx[:, a:b], oqT, os_, rows - a, cols))
         colsK = sample_idx(K, 48, e + 200)
         r, aabs = orc.gemm_dgrad(oqdy[a:b], osdy[:, a:b], oq, os_, rows - a, colsK)
         hw = hw_bound_dgrad(oqdy[a:b], osdy[:, a:b], oq, os_, rows - a, colsK)
-        check_gemm(dxh[np.ix_(rows, colsK)], r, aabs, True, f"moe dgrad e{e}", hw, N // T)
+        check_gemm(dxh[np.ix_(rows, colsK)], r, aabs, True, f"moe dgrad e{e}", hw, N // T,
+                   model=model_dgrad(oqdy[a:b], osdy[:, a:b], oq, os_, rows - a, colsK))
     wrows = sample_idx(K, 32, 7)
     wcols = sample_idx(N, 32, 8)
     r, aabs = orc.gemm_wgrad_grouped(offsets, oqxT, osxT, oqdyT, osdyT, experts=list(range(E)),
                                      rows=wrows, cols=wcols)
     hw = wgrad_hw_grouped(offsets, oqxT, osxT, oqdyT, osdyT, wrows, wcols)
     dwh = np.stack([host(dw[e])[np.ix_(wrows, wcols)] for e in range(E)])
-    check_gemm(dwh, r, aabs, False, "moe wgrad (all experts)", hw, int(np.diff(offsets).max()) // T)
+    check_gemm(dwh, r, aabs, False, "moe wgrad (all experts)", hw, int(np.diff(offsets).max()) // T,
+               model=model_grouped_wgrad(offsets, oqxT, osxT, oqdyT, osdyT, wrows, wcols))
     for e in range(E):
         if d["loads"][e] == 0:
             assert torch.all(dw[e] == 0)
@@ -204,17 +211,20 @@ def test_moe_down_sampled(orc, moe):
         cols = sample_idx(N, 32, e + 1)
         r, aabs = orc.gemm_fprop(oqh[a:b], osh[:, a:b], oqT, os_, rows - a, cols)
         hw = hw_bound_fprop(oqh[a:b], osh[:, a:b], oqT, os_, rows - a, cols)
-        check_gemm(yh[np.ix_(rows, cols)], r, aabs, True, f"moe down fprop e{e}", hw, K // T)
+        check_gemm(yh[np.ix_(rows, cols)], r, aabs, True, f"moe down fprop e{e}", hw, K // T,
+                   model=model_fprop(oqh[a:b], osh[:, a:b], oqT, os_, rows - a, cols))
         colsK = sample_idx(K, 32, e + 2)
         r, aabs = orc.gemm_dgrad(oqdy[a:b], osdy[:, a:b], oq, os_, rows - a, colsK)
         hw = hw_bound_dgrad(oqdy[a:b], osdy[:, a:b], oq, os_, rows - a, colsK)
-        check_gemm(dxh[np.ix_(rows, colsK)], r, aabs, True, f"moe down dgrad e{e}", hw, N // T)
+        check_gemm(dxh[np.ix_(rows, colsK)], r, aabs, True, f"moe down dgrad e{e}", hw, N // T,
+                   model=model_dgrad(oqdy[a:b], osdy[:, a:b], oq, os_, rows - a, colsK))
     wrows = sample_idx(K, 24, 9)
     wcols = sample_idx(N, 24, 10)
     r, aabs = orc.gemm_wgrad_grouped(offsets, oqhT, oshT, oqdyT, osdyT, rows=wrows, cols=wcols)
     hw = wgrad_hw_grouped(offsets, oqhT, oshT, oqdyT, osdyT, wrows, wcols)
     dwh = np.stack([host(dw[e])[np.ix_(wrows, wcols)] for e in range(E)])
-    check_gemm(dwh, r, aabs, False, "moe down wgrad (all experts)", hw, int(np.diff(offsets).max()) // T)
+    check_gemm(dwh, r, aabs, False, "moe down wgrad (all experts)", hw, int(np.diff(offsets).max()) // T,
+               model=model_grouped_wgrad(offsets, oqhT, oshT, oqdyT, osdyT, wrows, wcols))
 
 
 @pytest.mark.parametrize("E,N", [(100, 256), (70, 896)])
@@ -263,14 +273,17 @@ def test_grouped_many_experts_tail_rows_untouched(orc, E, N):
             hwf[pick] = hw_bound_fprop(oqx[a:b], osx[:, a:b], oqwT[e], osw[e], rows[pick] - a, cols)
             hwd[pick] = hw_bound_dgrad(oqdy[a:b], osdy[:, a:b], oqw[e], osw[e], rows[pick] - a, colsK)
     r, aabs = orc.gemm_fprop_grouped(offsets, oqx, osx, oqwT, osw, rows=rows, cols=cols)
-    check_gemm(bf16_host_f64(y)[np.ix_(rows, cols)], r, aabs, True, f"fprop grouped E={E}", hwf, K // T)
+    check_gemm(bf16_host_f64(y)[np.ix_(rows, cols)], r, aabs, True, f"fprop grouped E={E}", hwf, K // T,
+               model=model_grouped_rows(offsets, model_fprop, oqx, osx, oqwT, osw, rows, cols))
     r, aabs = orc.gemm_dgrad_grouped(offsets, oqdy, osdy, oqw, osw, rows=rows, cols=colsK)
-    check_gemm(bf16_host_f64(dx)[np.ix_(rows, colsK)], r, aabs, True, f"dgrad grouped E={E}", hwd, N // T)
+    check_gemm(bf16_host_f64(dx)[np.ix_(rows, colsK)], r, aabs, True, f"dgrad grouped E={E}", hwd, N // T,
+               model=model_grouped_rows(offsets, model_dgrad, oqdy, osdy, oqw, osw, rows, colsK))
     wr, wc = sample_idx(K, 24, 3), sample_idx(N, 24, 4)
     r, aabs = orc.gemm_wgrad_grouped(offsets, oqxT, osxT, oqdyT, osdyT, rows=wr, cols=wc)
     hw = wgrad_hw_grouped(offsets, oqxT, osxT, oqdyT, osdyT, wr, wc)
     nbw = max(1, int(np.diff(offsets).max()) // T)
-    check_gemm(host(dw)[:, wr][:, :, wc], r, aabs, False, f"wgrad grouped E={E}", hw, nbw)
+    check_gemm(host(dw)[:, wr][:, :, wc], r, aabs, False, f"wgrad grouped E={E}", hw, nbw,
+               model=model_grouped_wgrad(offsets, oqxT, osxT, oqdyT, osdyT, wr, wc))
 
 
 def test_grouped_all_experts_empty():

@@ -12,6 +12,7 @@ import torch
 import fine_grained_block_amd as fgb
 from fine_grained_block_amd import workloads as wl
 
+from parity import (model_dgrad, model_fprop, model_grouped_rows, model_grouped_wgrad, model_wgrad)
 from parity import (assert_codes_equal, assert_scales_equal, bf16_dev, bf16_host_f64, check_gemm, f32_dev,
                     host, hw_bound_dgrad, hw_bound_fprop, hw_bound_wgrad, sample_idx, u8_dev)
 from test_gpu_quant import SMALL, stress
@@ -115,7 +116,7 @@ def test_fprop_small(orc, M, N, K):
     y = fgb.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qwT), f32_dev(sw), ue8m0=True)
     r, aabs = orc.gemm_fprop(qx, sx, qwT, sw)
     check_gemm(bf16_host_f64(y), r, aabs, True, f"ue8m0 fprop {M}x{N}x{K}", hw_bound_fprop(qx, sx, qwT, sw),
-               SUBGROUPS * (K // T))
+               SUBGROUPS * (K // T), stated=False)
 
 
 @pytest.mark.parametrize("M,K,N", [(300, 384, 640), (200, 256, 1152), (333, 896, 384)])
@@ -126,7 +127,7 @@ def test_dgrad_small(orc, M, K, N):
     dx = fgb.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw), ue8m0=True)
     r, aabs = orc.gemm_dgrad(qdy, sdy, qw, sw)
     check_gemm(bf16_host_f64(dx), r, aabs, True, f"ue8m0 dgrad {M}x{K}x{N}", hw_bound_dgrad(qdy, sdy, qw, sw),
-               SUBGROUPS * (N // T))
+               SUBGROUPS * (N // T), stated=False)
 
 
 @pytest.mark.parametrize("K,N,M", [(256, 384, 300), (128, 128, 1), (384, 256, 1024), (256, 896, 300),
@@ -142,11 +143,11 @@ def test_wgrad_small(orc, K, N, M):
     dw = fgb.gemm_wgrad(u8_dev(qxT), f32_dev(sxT), u8_dev(qdyT), f32_dev(sdyT), M, ue8m0=True)
     r, aabs = orc.gemm_wgrad(qxT, sxT, qdyT, sdyT, M)
     hw = hw_bound_wgrad(qxT, sxT, qdyT, sdyT, M)
-    check_gemm(host(dw), r, aabs, False, f"ue8m0 wgrad {K}x{N}x{M}", hw, SUBGROUPS * nb)
+    check_gemm(host(dw), r, aabs, False, f"ue8m0 wgrad {K}x{N}x{M}", hw, SUBGROUPS * nb, stated=False)
     prev = g.standard_normal((K, N)).astype(np.float32)
     dw2 = f32_dev(prev)
     fgb.gemm_wgrad(u8_dev(qxT), f32_dev(sxT), u8_dev(qdyT), f32_dev(sdyT), M, dw=dw2, accumulate=True, ue8m0=True)
-    check_gemm(host(dw2), r + prev, aabs + np.abs(prev), False, "ue8m0 wgrad accumulate", hw, SUBGROUPS * nb + 1)
+    check_gemm(host(dw2), r + prev, aabs + np.abs(prev), False, "ue8m0 wgrad accumulate", hw, SUBGROUPS * nb + 1, stated=False)
 
 
 SMALL_INT_CODES = np.array([0x00, 0x80, 0x38, 0xB8, 0x40, 0xC0, 0x44, 0xC4, 0x48, 0xC8, 0x4C, 0xCC, 0x50, 0xD0],
@@ -233,11 +234,14 @@ def test_grouped_small(orc):
             hwd[a:b] = hw_bound_dgrad(oqdy[a:b], osdy[:, a:b], oqw[e], osw[e])
             hww[e] = hw_bound_wgrad(oqxT[:, a:b], osxT[a // T:b // T], oqdyT[:, a:b], osdyT[a // T:b // T], b - a)
     r, aabs = orc.gemm_fprop_grouped(offsets, oqx, osx, oqwT, osw)
-    check_gemm(bf16_host_f64(y), r, aabs, True, "ue8m0 fprop grouped", hwf, SUBGROUPS * (K // T))
+    check_gemm(bf16_host_f64(y), r, aabs, True, "ue8m0 fprop grouped", hwf, SUBGROUPS * (K // T),
+               model=model_grouped_rows(offsets, model_fprop, oqx, osx, oqwT, osw), po2=True)
     r, aabs = orc.gemm_dgrad_grouped(offsets, oqdy, osdy, oqw, osw)
-    check_gemm(bf16_host_f64(dx), r, aabs, True, "ue8m0 dgrad grouped", hwd, SUBGROUPS * (N // T))
+    check_gemm(bf16_host_f64(dx), r, aabs, True, "ue8m0 dgrad grouped", hwd, SUBGROUPS * (N // T),
+               model=model_grouped_rows(offsets, model_dgrad, oqdy, osdy, oqw, osw), po2=True)
     r, aabs = orc.gemm_wgrad_grouped(offsets, oqxT, osxT, oqdyT, osdyT)
-    check_gemm(host(dw).reshape(r.shape), r, aabs, False, "ue8m0 wgrad grouped", hww, SUBGROUPS * 2)
+    check_gemm(host(dw).reshape(r.shape), r, aabs, False, "ue8m0 wgrad grouped", hww, SUBGROUPS * 2,
+               model=model_grouped_wgrad(offsets, oqxT, osxT, oqdyT, osdyT), po2=True)
 
 
 def test_linear_dsv3_attn_sampled(orc):
@@ -269,12 +273,15 @@ def test_linear_dsv3_attn_sampled(orc):
     rows, cols = sample_idx(M, 40, 1), sample_idx(N, 40, 2)
     r, aabs = orc.gemm_fprop(oqx, osx, oqwT, osw, rows, cols)
     check_gemm(bf16_host_f64(y)[np.ix_(rows, cols)], r, aabs, True, "dsv3 ue8m0 fprop",
-               hw_bound_fprop(oqx, osx, oqwT, osw, rows, cols), SUBGROUPS * (K // T))
+               hw_bound_fprop(oqx, osx, oqwT, osw, rows, cols), SUBGROUPS * (K // T),
+               model=model_fprop(oqx, osx, oqwT, osw, rows, cols), po2=True)
     colsK = sample_idx(K, 40, 3)
     r, aabs = orc.gemm_dgrad(oqdy, osdy, oqw, osw, rows, colsK)
     check_gemm(bf16_host_f64(dx)[np.ix_(rows, colsK)], r, aabs, True, "dsv3 ue8m0 dgrad",
-               hw_bound_dgrad(oqdy, osdy, oqw, osw, rows, colsK), SUBGROUPS * (N // T))
+               hw_bound_dgrad(oqdy, osdy, oqw, osw, rows, colsK), SUBGROUPS * (N // T),
+               model=model_dgrad(oqdy, osdy, oqw, osw, rows, colsK), po2=True)
     wr, wc = sample_idx(K, 40, 4), sample_idx(N, 40, 5)
     r, aabs = orc.gemm_wgrad(oqxT, osxT, oqdyT, osdyT, M, wr, wc)
     check_gemm(host(dw)[np.ix_(wr, wc)], r, aabs, False, "dsv3 ue8m0 wgrad",
-               hw_bound_wgrad(oqxT, osxT, oqdyT, osdyT, M, wr, wc), SUBGROUPS * (M // T))
+               hw_bound_wgrad(oqxT, osxT, oqdyT, osdyT, M, wr, wc), SUBGROUPS * (M // T),
+               model=model_wgrad(oqxT, osxT, oqdyT, osdyT, M, wr, wc), po2=True)
