@@ -62,8 +62,57 @@ __device__ __forceinline__ float2 e4m3x2_decode(uint32_t w) {
 // Both are IEEE divisions (HIP's default correctly rounded fp32 divide).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void tile_scale(float a, float& s, float& inv) {
+    if (a != a) {                   // a NaN in the tile: NaN scale and multiplier
+        s = inv = __uint_as_float(0x7FC00000u);
+        return;
+    }
     s = a / kE4M3Max;
     inv = (a == 0.0f) ? 0.0f : fminf(kE4M3Max / a, 3.40282346638528859812e+38f);
+}
+
+// ---------------------------------------------------------------------------
+// NaN tiles.  The absmax is an integer max over magnitude bits, and a NaN's
+// bits exceed +inf's, so one NaN element makes the tile's absmax NaN; the
+// floor (>= 0, finite) is applied the same way so that it cannot drop it.  A
+// NaN tile gets a NaN scale (the canonical quiet NaN; E8M0 byte 0xFF for
+// power-of-two scales) and the E4M3 NaN code 0x7F for every element, so the
+// NaN reaches every GEMM output the tile feeds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float floored_absmax(uint32_t abs_bits, float amax_floor) {
+    return __uint_as_float(max(abs_bits, __float_as_uint(amax_floor)));
+}
+// A tile whose multiplier is 0 (an all-zero tile, or an infinite absmax: 448/Inf)
+// casts Inf * 0 = NaN for its infinite elements; the clamp to +-448 before the
+// cast would turn that NaN into -448, so such products get the NaN code 0x7F.
+__device__ __forceinline__ uint32_t nan_products(uint32_t codes, float p0, float p1, float p2, float p3) {
+    const uint32_t nan = (p0 != p0 ? 0x000000FFu : 0u) | (p1 != p1 ? 0x0000FF00u : 0u) |
+                         (p2 != p2 ? 0x00FF0000u : 0u) | (p3 != p3 ? 0xFF000000u : 0u);
+    return (codes & ~nan) | (0x7F7F7F7Fu & nan);
+}
+// Four codes of one tile with cast multiplier `mul` and products p_i = x_i * mul:
+// a NaN tile gives 0x7F in every byte, a zero multiplier the NaN code for NaN
+// products; otherwise the codes are returned unchanged.  Both cases are rare
+// and branch around the common path.
+__device__ __forceinline__ uint32_t fix_codes(uint32_t codes, float mul, float p0, float p1, float p2, float p3) {
+    if (__builtin_expect(mul != mul, 0)) return 0x7F7F7F7Fu;
+    if (__builtin_expect(mul == 0.0f, 0)) return nan_products(codes, p0, p1, p2, p3);
+    return codes;
+}
+// The same for four codes of four different tiles (byte i: multiplier m_i, product p_i).
+__device__ __forceinline__ uint32_t fix_codes4(uint32_t codes, float m0, float m1, float m2, float m3,
+                                               float p0, float p1, float p2, float p3) {
+    const uint32_t tile = (m0 != m0 ? 0x000000FFu : 0u) | (m1 != m1 ? 0x0000FF00u : 0u) |
+                          (m2 != m2 ? 0x00FF0000u : 0u) | (m3 != m3 ? 0xFF000000u : 0u);
+    codes = nan_products(codes, p0, p1, p2, p3);
+    return (codes & ~tile) | (0x7F7F7F7Fu & tile);
+}
+// Byte mask of the valid rows among 8 consecutive rows of which `nv` exist
+// (lo: rows 0..3, hi: rows 4..7): padding rows of transposed codes stay 0x00.
+__device__ __forceinline__ uint32_t rows_mask_lo(int nv) {
+    return nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << (8 * nv)) - 1u);
+}
+__device__ __forceinline__ uint32_t rows_mask_hi(int nv) {
+    return nv >= 8 ? 0xFFFFFFFFu : (nv <= 4 ? 0u : (1u << (8 * (nv - 4))) - 1u);
 }
 
 // ---------------------------------------------------------------------------

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
             m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
         uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
         m = max16(m);
-        if (lane16 == it) a_own = fmaxf(__uint_as_float(m << 16), amax_floor);
+        if (lane16 == it) a_own = floored_absmax(m << 16, amax_floor);
     }
     float sc_own = 0.0f, inv_own;
     uint32_t eb_own = 0;
@@ -85,6 +85,8 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
             o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
             o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
         }
+        o0 = fix_codes(o0, inv, bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
+        o1 = fix_codes(o1, inv, bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
         if (cok && r < R) st8(q + r * ldq + c, make_uint2(o0, o1));
     }
     if (lane16 < 4) {          // the block's segment j exists (grid = ceil(C/128)): only rows can be past the end
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(256) void k_tile128(
 #pragma unroll
             for (int k = 0; k < 8; ++k) m = max(m, abs_bits(V(i, k)));
             m = max16(m);
-            if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+            if (cg == i) a_own = floored_absmax(m, amax_floor);
         }
         float sr_own = 0.0f, iv_own;
         uint32_t er_own = 0;
@@ -237,8 +239,10 @@ __global__ __launch_bounds__(256) void k_tile128(
         for (int i = 0; i < 8; ++i) {
             const float iv = __shfl(iv_own, (lane & 48) | i, 64);
             const int64_t r = r0 + rg * 8 + i;
-            const uint32_t o0 = e4m3x4(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
-            const uint32_t o1 = e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
+            const uint32_t o0 = fix_codes(e4m3x4(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv), iv,
+                                          V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
+            const uint32_t o1 = fix_codes(e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv), iv,
+                                          V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
             if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
         }
         // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         if ((t & 63) == 0) red[wave][0] = m;
         __syncthreads();
         m = max(max(red[0][0], red[1][0]), max(red[2][0], red[3][0]));
-        const float a = fmaxf(__uint_as_float(m), amax_floor);
+        const float a = floored_absmax(m, amax_floor);
         float sc = 0.0f, iv;
         uint32_t eb = 0;
         scale_of(a, sc, eb, iv);
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         // the block and shares its multiplier through LDS
         if (t < kTile) {
             const uint32_t m = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
-            const float a = fmaxf(__uint_as_float(m), amax_floor);
+            const float a = floored_absmax(m, amax_floor);
             float sc = 0.0f, iv;
             uint32_t eb = 0;
             scale_of(a, sc, eb, iv);
@@ -315,20 +319,30 @@ __global__ __launch_bounds__(256) void k_tile128(
 #pragma unroll
                 for (int k = 0; k < 8; ++k) m = max(m, abs_bits(V(i, k)));
                 m = max16(m);
-                const float a = fmaxf(__uint_as_float(m), amax_floor);
+                const float a = floored_absmax(m, amax_floor);
                 float sc, iv;
                 tile_scale(a, sc, iv);
                 if (cg == i) sr_own = sc;
-                const uint32_t o0 = e4m3x4_sr(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv,
-                                              u[0], u[1], u[2], u[3]);
-                const uint32_t o1 = e4m3x4_sr(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv,
-                                              u[4], u[5], u[6], u[7]);
+                const uint32_t o0 = fix_codes(e4m3x4_sr(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv,
+                                                        V(i, 3) * iv, u[0], u[1], u[2], u[3]), iv,
+                                              V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
+                const uint32_t o1 = fix_codes(e4m3x4_sr(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv,
+                                                        V(i, 7) * iv, u[4], u[5], u[6], u[7]), iv,
+                                              V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
                 if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
             }
-            cr[i][0] = e4m3x4_sr(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3],
-                                 u[0], u[1], u[2], u[3]);
-            cr[i][1] = e4m3x4_sr(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7],
-                                 u[4], u[5], u[6], u[7]);
+            // rows past R are the zero padding of the transposed codes
+            const bool rok = r < R;
+            cr[i][0] = rok ? fix_codes4(e4m3x4_sr(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2],
+                                                  V(i, 3) * inv[3], u[0], u[1], u[2], u[3]),
+                                        inv[0], inv[1], inv[2], inv[3],
+                                        V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3])
+                           : 0u;
+            cr[i][1] = rok ? fix_codes4(e4m3x4_sr(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6],
+                                                  V(i, 7) * inv[7], u[4], u[5], u[6], u[7]),
+                                        inv[4], inv[5], inv[6], inv[7],
+                                        V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7])
+                           : 0u;
             if constexpr (TILE) {
                 if (q != nullptr && cok && r < R) st8(q + r * ldq + cc, make_uint2(cr[i][0], cr[i][1]));
             }
@@ -369,19 +383,30 @@ __global__ __launch_bounds__(256) void k_tile128(
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t r = r0 + rg * 8 + i;
-                const uint32_t o0 = e4m3x4(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]);
-                const uint32_t o1 = e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
+                const uint32_t o0 = fix_codes(
+                    e4m3x4(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]), inv[0],
+                    V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]);
+                const uint32_t o1 = fix_codes(
+                    e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]), inv[4],
+                    V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
                 if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
             }
         }
         if (qT == nullptr) return;
     }
 
-    // Transposed codes: column k of the patch -> 8 row bytes, staged in LDS.
+    // Transposed codes: column k of the patch -> 8 row bytes, staged in LDS;
+    // rows past R are the zero padding (a NaN tile's codes must not reach it).
+    const int nv = (int)(R - (r0 + rg * 8) < 8 ? (R - (r0 + rg * 8) < 0 ? 0 : R - (r0 + rg * 8)) : 8);
+    const uint32_t vlo = rows_mask_lo(nv), vhi = rows_mask_hi(nv);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const uint32_t lo = e4m3x4(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]);
-        const uint32_t hi = e4m3x4(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]);
+        const uint32_t lo = fix_codes(e4m3x4(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]),
+                                      inv[k], V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k])
+                            & vlo;
+        const uint32_t hi = fix_codes(e4m3x4(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]),
+                                      inv[k], V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k])
+                            & vhi;
         *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
     }
     __syncthreads();

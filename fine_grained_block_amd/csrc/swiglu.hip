@@ -163,7 +163,8 @@ __device__ __forceinline__ float e4m3_decode1(uint8_t code) { return e4m3x2_deco
 
 // RN codes of four values times inv (the quantizers' cast).
 __device__ __forceinline__ uint32_t codes4(const float* v, float inv) {
-    return e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    return fix_codes(e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv), inv,
+                     v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
 }
 
 }  // namespace
@@ -210,8 +211,8 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
             mg = max16(mg);
             mu = max16(mu);
             float sg, ig, su, iu;
-            tile_scale(fmaxf(__uint_as_float(mg), amax_floor), sg, ig);
-            tile_scale(fmaxf(__uint_as_float(mu), amax_floor), su, iu);
+            tile_scale(floored_absmax(mg, amax_floor), sg, ig);
+            tile_scale(floored_absmax(mu, amax_floor), su, iu);
             if (ok) {
                 st8(q_gu + r * ldq_gu + c, make_uint2(codes4(g, ig), codes4(g + 4, ig)));
                 st8(q_gu + r * ldq_gu + F + c, make_uint2(codes4(u, iu), codes4(u + 4, iu)));
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
         }
         mh = max16(mh);
         float sh, ih;
-        tile_scale(fmaxf(__uint_as_float(mh), amax_floor), sh, ih);
+        tile_scale(floored_absmax(mh, amax_floor), sh, ih);
         if (ok) {
             st8(q_h + r * ldq_h + c, make_uint2(codes4(hv, ih), codes4(hv + 4, ih)));
             if (lane16 == 0) s_h[b * lds_h + r] = sh;
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
 #pragma unroll
                 for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
                 m = max16(m);
-                if (cg == i) a_own = fmaxf(__uint_as_float(m), amax_floor);
+                if (cg == i) a_own = floored_absmax(m, amax_floor);
             }
             float iv_own;
             tile_scale(a_own, s_own, iv_own);
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
         if (t < kTile) {
             const uint32_t m = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
             float sc, iv;
-            tile_scale(fmaxf(__uint_as_float(m), amax_floor), sc, iv);
+            tile_scale(floored_absmax(m, amax_floor), sc, iv);
             col_mul[t] = iv;
             sT[(int64_t)blockIdx.x * ldsT + oc0 + t] = sc;
         }
@@ -526,10 +527,17 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             float v[8][8];
             patch(v);
             if (half == 0) __syncthreads();
+            // rows past R are the zero padding of the transposed codes
+            const int nv = (int)(R - (r0 + rg * 8) < 8 ? (R - (r0 + rg * 8) < 0 ? 0 : R - (r0 + rg * 8)) : 8);
+            const uint32_t vlo = rows_mask_lo(nv), vhi = rows_mask_hi(nv);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t lo = e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]);
-                const uint32_t hi = e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]);
+                const uint32_t lo = fix_codes(
+                    e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]), inv[k],
+                    v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]) & vlo;
+                const uint32_t hi = fix_codes(
+                    e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]), inv[k],
+                    v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]) & vhi;
                 *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
             }
         }

@@ -84,7 +84,8 @@ def _load():
     if _LIB_OVERRIDE:
         lib = ctypes.CDLL(_LIB_OVERRIDE)
     else:
-        if not os.path.exists(_LIB_PATH):
+        # (re)build when the library is missing or older than its source
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
@@ -128,6 +129,7 @@ def _load():
     lib.orc_swiglu_h.argtypes = [P, I64, I64, I64, P, I64]
     lib.orc_swiglu_dgu.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64]
     lib.orc_max_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -147,6 +149,11 @@ def _cdiv(a: int, b: int) -> int:
 
 def max_threads() -> int:
     return int(_load().orc_max_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops from now on (timing only)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

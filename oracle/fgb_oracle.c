@@ -141,7 +141,9 @@ uint16_t orc_bf16_round(double r)
  *   s   = fl32(a' / 448)                 (stored scale; dequant = s * dec(q))
  *   inv = a' == 0 ? 0 : min(fl32(448 / a'), FLT_MAX)
  *   q_i = enc(fl32(v_i * inv))
- * A NaN anywhere in the tile makes a NaN.                              */
+ * A NaN anywhere in the tile makes a NaN: the pages say nothing about
+ * NaN; read here as propagating it to the scale (the quiet NaN) and to every
+ * code of the tile (the E4M3 NaN 0x7F), so that it reaches the GEMM.    */
 static void quantize_tile(const float* v, int64_t n, float amax_floor,
                           float* s_out, uint8_t* q_out)
 {
@@ -150,6 +152,11 @@ static void quantize_tile(const float* v, int64_t n, float amax_floor,
         float av = fabsf(v[i]);
         if (isnan(av) || av > a) a = av;
         if (isnan(a)) break;
+    }
+    if (isnan(a)) {
+        *s_out = NAN;
+        for (int64_t i = 0; i < n; ++i) q_out[i] = 0x7F;
+        return;
     }
     if (amax_floor > a) a = amax_floor;
     float s = a / 448.0f;
@@ -163,7 +170,9 @@ static void quantize_tile(const float* v, int64_t n, float amax_floor,
     *s_out = s;
     for (int64_t i = 0; i < n; ++i) {
         float t = v[i] * inv;
-        q_out[i] = orc_e4m3_encode(t);
+        /* t is NaN only for an infinite element of an infinite tile (Inf * 0): the
+         * sign of that NaN is not fixed by IEEE arithmetic; it encodes as 0x7F */
+        q_out[i] = isnan(t) ? 0x7F : orc_e4m3_encode(t);
     }
 }
 
@@ -302,7 +311,7 @@ static void quantize_tile_ue8m0(const float* v, int64_t n, float amax_floor,
     if (amax_floor > a) a = amax_floor;
     if (isnan(a)) {
         *e_out = 0xFF;
-        for (int64_t i = 0; i < n; ++i) q_out[i] = orc_e4m3_encode(NAN);
+        for (int64_t i = 0; i < n; ++i) q_out[i] = 0x7F;
         return;
     }
     int e = -127;
@@ -538,6 +547,17 @@ void orc_bf16_round_array(const double* r, int64_t n, uint16_t* out)
     for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(r[i]);
 }
 
+/* Thread count for the OpenMP loops that follow (n >= 1); benchmark plumbing only. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP
@@ -629,7 +649,8 @@ uint8_t orc_e4m3_encode_sr(float v, uint32_t u)
     return sign | (uint8_t)(up ? a + 1 : a);
 }
 
-/* One tile as quantize_tile, with the SR cast; u[i] is element i's word. */
+/* One tile as quantize_tile, with the SR cast; u[i] is element i's word.
+ * A NaN tile as in quantize_tile.                                      */
 static void quantize_tile_sr(const float* v, const uint32_t* u, int64_t n, float amax_floor,
                              float* s_out, uint8_t* q_out)
 {
@@ -638,6 +659,11 @@ static void quantize_tile_sr(const float* v, const uint32_t* u, int64_t n, float
         float av = fabsf(v[i]);
         if (isnan(av) || av > a) a = av;
         if (isnan(a)) break;
+    }
+    if (isnan(a)) {
+        *s_out = NAN;
+        for (int64_t i = 0; i < n; ++i) q_out[i] = 0x7F;
+        return;
     }
     if (amax_floor > a) a = amax_floor;
     float s = a / 448.0f;
@@ -649,7 +675,10 @@ static void quantize_tile_sr(const float* v, const uint32_t* u, int64_t n, float
         if (inv > FLT_MAX) inv = FLT_MAX;
     }
     *s_out = s;
-    for (int64_t i = 0; i < n; ++i) q_out[i] = orc_e4m3_encode_sr(v[i] * inv, u[i]);
+    for (int64_t i = 0; i < n; ++i) {
+        float t = v[i] * inv;
+        q_out[i] = isnan(t) ? 0x7F : orc_e4m3_encode_sr(t, u[i]);      /* Inf * 0: as quantize_tile */
+    }
 }
 
 /* As orc_quantize_1x128 with the SR cast. */

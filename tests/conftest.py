@@ -20,6 +20,5 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def orc():
     import oracle
-    if not os.path.exists(oracle._LIB_PATH):
-        oracle.build(force=True)
+    oracle._load()            # builds the library when it is missing or older than its source
     return oracle

@@ -266,3 +266,101 @@ def test_per_tensor_scale_negative_control(orc):
     a = np.float32(np.abs(xf).max())
     qt = torch_enc(xf * (np.float32(448) / a))
     assert not np.array_equal(q, qt)
+
+
+# ---------------------------------------------------------------------------
+# NaN tiles: the pages say nothing about NaN; the reading is that a NaN element
+# makes its tile's scale NaN and every code of that tile the E4M3 NaN 0x7F (the
+# GPU kernels follow the same rule), while every other tile is unaffected.
+# ---------------------------------------------------------------------------
+
+def _nan_input():
+    g = np.random.default_rng(17)
+    x = g.standard_normal((256, 384)).astype(np.float32)
+    bits = wl.bf16_bits(x)
+    clean = bits.copy()
+    bits[5, 130] = 0x7FC0            # quiet NaN in row 5, column tile 1, row tile 0
+    bits[200, 7] = 0xFFC1            # negative NaN with a payload: row 200, column tile 0, row tile 1
+    return bits, clean
+
+
+def test_nan_tile_1x128(orc):
+    bits, clean = _nan_input()
+    q, s = orc.quantize_1x128(bits)
+    q0, s0 = orc.quantize_1x128(clean)
+    nan_tiles = {(5, 1), (200, 0)}
+    for r in range(256):
+        for j in range(3):
+            seg = slice(128 * j, 128 * j + 128)
+            if (r, j) in nan_tiles:
+                assert np.isnan(s[j, r]) and np.all(q[r, seg] == 0x7F)
+            else:
+                assert s[j, r].view(np.uint32) == s0[j, r].view(np.uint32)
+                assert np.array_equal(q[r, seg], q0[r, seg])
+
+
+def test_nan_tile_128x1_and_128x128(orc):
+    bits, clean = _nan_input()
+    qT, sT = orc.quantize_128x1(bits)
+    qT0, sT0 = orc.quantize_128x1(clean)
+    for c in range(384):
+        for i in range(2):
+            seg = slice(128 * i, 128 * i + 128)
+            if (i, c) in {(0, 130), (1, 7)}:
+                assert np.isnan(sT[i, c]) and np.all(qT[c, seg] == 0x7F)
+            else:
+                assert sT[i, c].view(np.uint32) == sT0[i, c].view(np.uint32)
+                assert np.array_equal(qT[c, seg], qT0[c, seg])
+    q, qt, s = orc.quantize_128x128(bits)
+    q0, qt0, s0 = orc.quantize_128x128(clean)
+    for i in range(2):
+        for j in range(3):
+            blk = (slice(128 * i, 128 * i + 128), slice(128 * j, 128 * j + 128))
+            if (i, j) in {(0, 1), (1, 0)}:
+                assert np.isnan(s[i, j]) and np.all(q[blk] == 0x7F) and np.all(qt[blk[::-1]] == 0x7F)
+            else:
+                assert s[i, j].view(np.uint32) == s0[i, j].view(np.uint32)
+                assert np.array_equal(q[blk], q0[blk])
+
+
+def test_nan_tile_requant_and_power_of_two(orc):
+    bits, clean = _nan_input()
+    q, s = orc.quantize_1x128(bits)
+    qT, sT = orc.requant_128x1(q, s)
+    # a NaN 1x128 tile dequantizes to NaN and makes every 128x1 tile it crosses NaN
+    for c in range(384):
+        for i in range(2):
+            hit = (i == 0 and 128 <= c < 256) or (i == 1 and c < 128)
+            assert np.isnan(sT[i, c]) == hit
+            if hit:
+                assert np.all(qT[c, 128 * i:128 * i + 128] == 0x7F)
+    qe, e = orc.quantize_1x128_ue8m0(bits)
+    assert e[1, 5] == 0xFF and np.all(qe[5, 128:256] == 0x7F)
+    assert e[0, 200] == 0xFF and np.all(qe[200, :128] == 0x7F)
+    assert e[0, 5] != 0xFF
+    qs, ss = orc.quantize_1x128_sr(bits, 3, 4)
+    assert np.isnan(ss[1, 5]) and np.all(qs[5, 128:256] == 0x7F)
+    assert not np.isnan(ss[0, 5])
+
+
+def test_inf_tile(orc):
+    """An infinite element makes its tile's absmax Inf: s = Inf/448 = Inf and the
+    multiplier 448/Inf = 0, so finite elements cast to +-0 (each with its sign)
+    and the infinite element, Inf * 0, is NaN: code 0x7F.  Other tiles unchanged."""
+    g = np.random.default_rng(23)
+    bits = wl.bf16_bits(g.standard_normal((4, 256)).astype(np.float32))
+    clean = bits.copy()
+    bits[1, 3] = 0x7F80          # +Inf in row 1, tile 0
+    bits[2, 200] = 0xFF80        # -Inf in row 2, tile 1
+    q, s = orc.quantize_1x128(bits)
+    q0, s0 = orc.quantize_1x128(clean)
+    for r, j, c in [(1, 0, 3), (2, 1, 200)]:
+        seg = slice(128 * j, 128 * j + 128)
+        assert np.isinf(s[j, r]) and s[j, r] > 0
+        assert q[r, c] == 0x7F
+        others = [k for k in range(128 * j, 128 * j + 128) if k != c]
+        sign = (bits[r, others] >> 15).astype(np.uint8) << 7
+        assert np.array_equal(q[r, others], sign)                 # +-0 with the input's sign
+    mask = np.ones_like(q, bool)
+    mask[1, :128] = mask[2, 128:] = False
+    assert np.array_equal(q[mask], q0[mask])
