@@ -1,19 +1,33 @@
-#!/usr/bin/env python3
-"""Benchmark: one step = the whole FP8 linear-layer path, forward and backward,
-at the DeepSeek-V3 attention-projection shape X [4096, 7168], W [7168, 7168],
-dY [4096, 7168] (synthetic, seeded; inputs resident in HBM):
+"""Benchmark: one step = the whole FP8 linear-layer path, forward and backward.
+
+Default workload `ffn_dense`, the dense FFN's two linears (synthetic, seeded;
+inputs resident in HBM): up X [8192, 7168] (Student-t(3)), W_up [7168, 18432],
+dY_up [8192, 18432]; down H [8192, 18432] (Student-t(3)), W_down [18432, 7168],
+dY_down [8192, 7168].  Per linear, in order:
 
   quantize X 1x128 -> quantize W 128x128 (both layouts) -> Fprop Y = X W (bf16)
   -> quantize dY 1x128 and 128x1 (one fused read) -> Dgrad dX = dY W^T (bf16)
   -> requant X 128x1 -> Wgrad dW = X^T dY (fp32)
 
-Prints one JSON line.  `value` is the step's GEMM throughput (3 x 2*M*N*K
-FLOP over the whole step time, quantization included) in TFLOP/s.  Per-kernel
-durations come from HIP events recorded around every launch on the stream the
-kernels run on, over the timed steps; `roofline` prices the dominant kernel
-against MI355X's dense FP8 MFMA peak, and `kernels` lists every kernel's rate
-against its own roofline (HBM for the quantizers).  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step.
+six GEMMs of 2*8192*7168*18432 FLOP each; the down projection's Fprop and the
+up projection's Dgrad contract over 18432 = 144 blocks.
+`--workload linear_dsv3_attn` runs the same step once at the DeepSeek-V3
+attention-projection shape X [4096, 7168], W [7168, 7168], dY [4096, 7168].
+
+Prints one JSON line.  `value` is the step's GEMM throughput (GEMM FLOP over
+the whole step time, quantization included) in TFLOP/s.  Per-kernel durations
+come from HIP events recorded around every launch on the stream the kernels
+run on, over the timed steps (warm: the steps run back to back); `roofline`
+prices the dominant kernel against MI355X's dense FP8 MFMA peak (5.0 PFLOP/s
+at 2.4 GHz) and, with the clock the chip sustains under an MFMA-saturating
+probe (`clock_mhz`), against the peak at that clock (`frac_at_clock`).
+`kernels` lists every kernel's rate against its own roofline (HBM for the
+quantizers).  `cold` is the median of 50 steps after 10 warm-ups, each after a
+1 GiB read scrub outside its events, labelled as such.  `cpu_baseline` times
+the CPU oracle on a bounded, seeded sample of the same work (for ffn_dense and
+moe_grouped 1/8 of the 128x128 output tiles, first and last tiles included;
+the fraction is printed), with the host's CPU model, thread count and the
+oracle's one-thread quantizer rate.
 
 `--recipe ue8m0` runs the same step with power-of-two (UE8M0) scales, which the
 matrix core applies itself (no vector-ALU rescale).  Its weight cast has two
@@ -60,6 +74,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -108,11 +124,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["linear_dsv3_attn", "moe_grouped", "quant_stress"],
-                   default="linear_dsv3_attn",
-                   help="linear_dsv3_attn (default): the DeepSeek-V3 attention projection's linear; "
-                        "moe_grouped: one GPU's MoE expert share as a SwiGLU FFN, fwd+bwd (no CPU baseline); "
-                        "quant_stress: the quantizers alone on X [16384,7168], cold cache")
+    p.add_argument("--workload", choices=["ffn_dense", "linear_dsv3_attn", "moe_grouped", "quant_stress"],
+                   default="ffn_dense",
+                   help="ffn_dense (default): the dense FFN's up and down linears, fwd+bwd (the largest "
+                        "single-GPU workload, contraction up to 18432); linear_dsv3_attn: the DeepSeek-V3 "
+                        "attention projection's linear; moe_grouped: one GPU's MoE expert share as a SwiGLU "
+                        "FFN, fwd+bwd; quant_stress: the quantizers alone on X [16384,7168], cold cache")
     p.add_argument("--recipe", choices=["fp32", "ue8m0"], default="fp32",
                    help="fp32: scales absmax/448 (default); ue8m0: power-of-two scales, applied by the matrix core")
     p.add_argument("--ue8m0-weights", choices=["two-stage", "direct"], default="two-stage",
@@ -130,6 +147,12 @@ def parse():
     p.add_argument("--schedule", choices=["serial", "overlap"], default="serial",
                    help="serial (default): every kernel on one stream, in step order; "
                         "overlap: casts that no GEMM waits for run on a second stream")
+    p.add_argument("--cold-iters", type=int, default=50,
+                   help="cold-cache step timings after the timed region: median of this many steps, each "
+                        "after a 1 GiB scrub (0 = skip)")
+    p.add_argument("--cpu-tile-frac", type=float, default=0.125,
+                   help="ffn_dense / moe_grouped CPU baseline: fraction of the 128x128 output tiles the oracle "
+                        "computes (seeded; first and last tiles included)")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="Fprop/Dgrad output rows in the CPU-baseline sample (0 = auto, ~15 s of GEMM work)")
     return p.parse_args()
@@ -528,6 +551,43 @@ def make_runner(torch, dev, kernels, overlap):
     return step
 
 
+def prefixed(kernels, p):
+    """The same kernel list with every name (and dependency) prefixed by p."""
+    return [(p + n, fn, work, lane, [p + x for x in deps]) for n, fn, work, lane, deps in kernels]
+
+
+def cpu_model():
+    """(model name, logical CPUs) of the host, from /proc/cpuinfo."""
+    name, n = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name") and name == "unknown":
+                    name = line.split(":", 1)[1].strip()
+                if line.startswith("processor"):
+                    n += 1
+    except OSError:
+        pass
+    return name, n or os.cpu_count()
+
+
+def probe_clock_mhz(torch, dev, iters=200000):
+    """Median shader clock (MHz) over the CUs while every SIMD runs FP8 MFMAs
+    (libfgb_probe.so, built beside libfgb.so), or None if the probe is missing."""
+    import ctypes
+    path = os.path.join(ROOT, "fine_grained_block_amd", "libfgb_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.fgb_probe_clock.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    L.fgb_probe_clock.restype = ctypes.c_int
+    mhz = ctypes.c_double(0.0)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if L.fgb_probe_clock(iters, ctypes.byref(mhz), st) != 0:
+        return None
+    return mhz.value
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -545,10 +605,24 @@ def main():
         quant_stress_main(args, np, torch, fgb, wl)
         return
     dev = torch.device("cuda:0")
-    if args.workload == "linear_dsv3_attn":
+    ue8m0 = args.recipe == "ue8m0"
+    sr = args.rounding == "sr"
+    if (ue8m0 or sr) and args.workload != "linear_dsv3_attn":
+        print("bench.py: --recipe ue8m0 and --rounding sr apply to --workload linear_dsv3_attn", file=sys.stderr)
+        sys.exit(2)
+    cpu_inputs = None
+    if args.workload == "ffn_dense":
+        up, down = wl.ffn_dense_up(), wl.ffn_dense_down()
+        kernels = prefixed(linear_step(fgb, torch, dev, up), "up.") + \
+            prefixed(linear_step(fgb, torch, dev, down), "down.")
+        config = {"workload": "ffn_dense fwd+bwd: up X[8192,7168] (Student-t(3)) W_up[7168,18432] "
+                              "dY_up[8192,18432]; down H[8192,18432] (Student-t(3)) W_down[18432,7168] "
+                              "dY_down[8192,7168]; 6 GEMMs, contraction up to 18432 (144 blocks)",
+                  "M": up["M"], "d_model": up["K"], "d_ff": up["N"], "scales": "fp32", "rounding": "rn"}
+        data = "synthetic (seeded Student-t(3) X and H, N(0,0.02) W, N(0,1e-3) dY; bf16)"
+        cpu_inputs = ("ffn_dense", (up, down))
+    elif args.workload == "linear_dsv3_attn":
         d = wl.linear_dsv3_attn()
-        ue8m0 = args.recipe == "ue8m0"
-        sr = args.rounding == "sr"
         if ue8m0 and sr:
             print("bench.py: stochastic rounding uses absmax/448 scales (--recipe fp32)", file=sys.stderr)
             sys.exit(2)
@@ -561,6 +635,7 @@ def main():
                               + (", stochastic rounding of the X, W and dY casts" if sr else ""),
                   "M": d["M"], "K": d["K"], "N": d["N"], "scales": args.recipe, "rounding": args.rounding}
         data = "synthetic (seeded N(0,0.02) X and W, N(0,1e-3) dY; bf16)"
+        cpu_inputs = ("linear_dsv3_attn", d)
     else:
         d = wl.moe_grouped()
         kernels = moe_step(fgb, torch, dev, d)
@@ -569,8 +644,7 @@ def main():
                               "expert, SwiGLU casts fused",
                   "experts": d["E"], "routed_rows": int(np.sum(d["loads"])), "R_pad": d["R_pad"]}
         data = "synthetic (seeded N(0,1) X, N(0,0.02) W, N(0,1e-3) dY; bf16)"
-        del d
-        args.no_cpu_baseline = True
+        cpu_inputs = ("moe_grouped", d)
 
     overlap = args.schedule == "overlap"
     step = make_runner(torch, dev, kernels, overlap)
@@ -595,6 +669,34 @@ def main():
                      for i, (name, _, _, _, _) in enumerate(kernels)}
     work = {name: w for name, _, w, _, _ in kernels}
 
+    # cold-cache step times, labelled as such: 10 warm-ups, then the median of 50
+    # steps, each after a 1 GiB read scrub (outside its events) that evicts L2
+    # and the 256 MB Infinity Cache
+    cold = None
+    if args.cold_iters > 0:
+        scrub = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        cst, cev = [], []
+        for _ in range(args.cold_iters):
+            torch.sum(scrub, dim=(0,), out=sink)
+            e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kernels]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step(e)
+            b.record()
+            torch.cuda.synchronize()
+            cst.append(a.elapsed_time(b))
+            cev.append([x.elapsed_time(y) for x, y in e])
+        del scrub
+        cold = {"what": f"median of {args.cold_iters} steps after 10 warm-ups, each step after a 1 GiB read "
+                        "scrub outside its events (L2 and Infinity Cache cold at the step's start)",
+                "ms_per_step": round(float(np.median(cst)), 4),
+                "kernels_us": {name: round(float(np.median([c[i] for c in cev])) * 1e3, 2)
+                               for i, (name, _, _, _, _) in enumerate(kernels)}}
+
     step_flop = sum(w.get("flop", 0.0) for w in work.values())
     quant_bytes = sum(w.get("bytes", 0) for w in work.values())
     value = step_flop / (ms_per_step * 1e-3) / 1e12
@@ -614,6 +716,13 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_rate / 1e12, 1),
                 "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(dom_rate / FP8_PEAK, 4),
                 "traffic": traffic_record(dom)}
+    mhz = probe_clock_mhz(torch, dev)
+    if mhz:
+        # the MFMA peak scales with the clock: 5.0 PFLOP/s is quoted at 2.4 GHz
+        roofline["clock_mhz"] = round(mhz, 1)
+        roofline["frac_at_clock"] = round(dom_rate / (FP8_PEAK * mhz / 2400.0), 4)
+        roofline["clock_how"] = ("median shader clock over the CUs under an MFMA-saturating probe "
+                                 "(s_memtime ticks per s_memrealtime time)")
     quant_ms = sum(v for k, v in per_kernel_ms.items() if "bytes" in work[k])
     config.update({"gemm_flop_per_step": step_flop, "quant_bytes_per_step": quant_bytes,
                    "schedule": ("overlap: casts " + ", ".join(n for n, _, _, lane, _ in kernels if lane == 1)
@@ -638,6 +747,9 @@ def main():
         "roofline": roofline,
         "kernels": kinfo,
     }
+    if cold is not None:
+        cold["TFLOP/s"] = round(step_flop / (cold["ms_per_step"] * 1e-3) / 1e12, 1)
+        out["cold"] = cold
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -648,12 +760,166 @@ def main():
         del a, c
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl.linear_dsv3_attn(), args.cpu_rows, args.recipe == "ue8m0",
-                                           args.rounding == "sr")
+        kind, inp = cpu_inputs
+        if kind == "linear_dsv3_attn":
+            out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, ue8m0, sr)
+        elif kind == "ffn_dense":
+            out["cpu_baseline"] = cpu_baseline_tiles_linear(list(inp), args.cpu_tile_frac)
+        else:
+            out["cpu_baseline"] = cpu_baseline_tiles_moe(inp, args.cpu_tile_frac)
     print(json.dumps(out), flush=True)
 
 
+def tile_sample(n, frac, g):
+    """Element indices of a seeded sample of the 128-wide tiles of range(n):
+    about frac of them (at least one), always the first and the last tile."""
+    nt = -(-n // T)
+    k = max(1, int(round(frac * nt)))
+    pick = {0, nt - 1} if k >= 2 else {0}
+    rest = [t for t in range(nt) if t not in pick]
+    extra = max(0, k - len(pick))
+    if extra and rest:
+        pick |= set(g.choice(rest, size=min(extra, len(rest)), replace=False).tolist())
+    idx = np.concatenate([np.arange(t * T, min(n, t * T + T)) for t in sorted(pick)])
+    return idx.astype(np.int64), len(pick), nt
+
+
+def host_info(oracle):
+    model, ncpu = cpu_model()
+    return {"cores": oracle.max_threads(), "cpu_model": model, "nproc": ncpu}
+
+
+def quant_t1(oracle, x_bits):
+    """GB/s of the oracle's 1x128 quantizer on x_bits with one thread."""
+    threads = oracle.max_threads()
+    oracle.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        oracle.quantize_1x128(x_bits)
+        dt = time.perf_counter() - t
+    finally:
+        oracle.set_num_threads(threads)
+    R, C = x_bits.shape
+    return {"quant_T1_GBps": round((R * C * 3 + 4 * R * (-(-C // T))) / dt / 1e9, 3),
+            "quant_T1_what": f"oracle quantize_1x128 of [{R},{C}] on one thread ({dt:.2f} s)"}
+
+
+def cpu_baseline_tiles_linear(ds, frac):
+    """The CPU oracle on a seeded sample of the dense linears' output tiles:
+    quantizers on the full tensors, then for every linear the Fprop, Dgrad and
+    Wgrad outputs of frac of the 128x128 output tiles (half the tile rows x a
+    quarter of the tile columns at frac = 1/8, first and last tiles included),
+    each over the full contraction.  value = sampled GEMM FLOP / GEMM time."""
+    import oracle
+    g = np.random.default_rng(0)
+    fr, fc = np.sqrt(frac * 2.0), np.sqrt(frac / 2.0)     # 1/2 x 1/4 at frac = 1/8
+    tq = tg = 0.0
+    qbytes = flop = 0.0
+    parts = []
+    for d in ds:
+        M, K, N = d["M"], d["K"], d["N"]
+        t0 = time.perf_counter()
+        qx, sx = oracle.quantize_1x128(d["x"])
+        q, qT, sw = oracle.quantize_128x128(d["w"])
+        qdy, sdy = oracle.quantize_1x128(d["dy"])
+        qdyT, sdyT = oracle.quantize_128x1(d["dy"])
+        qxT, sxT = oracle.requant_128x1(qx, sx)
+        tq += time.perf_counter() - t0
+        qbytes += sum(v for k, v in algorithmic_bytes(M, K, N).items()
+                      if k in ("quantize_1x128_x", "quantize_128x128_w", "quantize_1x128_dy",
+                               "quantize_128x1_dy", "requant_128x1_x"))
+        rows, nrt, ntm = tile_sample(M, fr, g)
+        colsN, nct, ntn = tile_sample(N, fc, g)
+        colsK, nck, ntk = tile_sample(K, fc, g)
+        rowsK, nrk, _ = tile_sample(K, fr, g)
+        t0 = time.perf_counter()
+        oracle.gemm_fprop(qx, sx, qT, sw, rows=rows, cols=colsN)
+        oracle.gemm_dgrad(qdy, sdy, q, sw, rows=rows, cols=colsK)
+        oracle.gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows=rowsK, cols=colsN)
+        tg += time.perf_counter() - t0
+        flop += 2.0 * rows.size * colsN.size * K + 2.0 * rows.size * colsK.size * N + 2.0 * rowsK.size * colsN.size * M
+        parts.append(f"[{M}x{K}x{N}] Fprop {nrt}/{ntm} x {nct}/{ntn} tiles, Dgrad {nrt}/{ntm} x {nck}/{ntk}, "
+                     f"Wgrad {nrk}/{ntk} x {nct}/{ntn}")
+    out = {"value": round(flop / tg / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"quantizers on the full tensors ({tq:.1f} s); GEMMs on a seeded sample of about {frac:g} of "
+                     "the 128x128 output tiles, first and last tile rows and columns included, full contraction "
+                     f"({tg:.1f} s): " + "; ".join(parts) + ". value = sampled GEMM FLOP / GEMM time",
+           "sample_fraction": round(flop / sum(6.0 * d["M"] * d["K"] * d["N"] for d in ds), 4),
+           "quant_GBps": round(qbytes / tq / 1e9, 3), "quant_s": round(tq, 2)}
+    out.update(host_info(oracle))
+    out.update(quant_t1(oracle, ds[0]["x"]))
+    return out
+
+
+def cpu_baseline_tiles_moe(d, frac):
+    """The CPU oracle on one GPU's MoE expert share: the 1x128/128x1 casts of
+    the grouped activations and gradients and both projections' expert weights
+    on the full tensors, then the grouped Fprop, Dgrad and Wgrad of both
+    projections on a seeded sample of about frac of every expert's 128x128
+    output tiles (each expert's first and last tile rows, the first and last
+    tile columns).  The backward GEMMs take the workload's dY tensors as their
+    gradients.  value = sampled GEMM FLOP (routed rows) / GEMM time."""
+    import oracle
+    g = np.random.default_rng(0)
+    fr, fc = np.sqrt(frac * 2.0), np.sqrt(frac / 2.0)
+    offsets, loads, E = np.asarray(d["offsets"]), np.asarray(d["loads"]), d["E"]
+    Dm, F2, F = d["d_model"], d["d_ff2"], d["d_ff"]
+    t0 = time.perf_counter()
+    qx, sx = oracle.quantize_1x128(d["x"])
+    qxT, sxT = oracle.requant_128x1(qx, sx)
+    qh, sh = oracle.quantize_1x128(d["h"])
+    qhT, shT = oracle.requant_128x1(qh, sh)
+    qdu, sdu = oracle.quantize_1x128(d["dy_up"])
+    qduT, sduT = oracle.quantize_128x1(d["dy_up"])
+    qdd, sdd = oracle.quantize_1x128(d["dy_down"])
+    qddT, sddT = oracle.quantize_128x1(d["dy_down"])
+    wu = [oracle.quantize_128x128(w) for w in d["w_up"]]
+    wd = [oracle.quantize_128x128(w) for w in d["w_down"]]
+    tq = time.perf_counter() - t0
+    qwu, qwuT, swu = (np.stack([w[k] for w in wu]) for k in range(3))
+    qwd, qwdT, swd = (np.stack([w[k] for w in wd]) for k in range(3))
+    # rows: per expert, a sample of its own row tiles (its first and last included)
+    rows, valid_rows = [], 0
+    for e in range(E):
+        a, n = int(offsets[e]), int(loads[e])
+        if n == 0:
+            continue
+        idx, _, _ = tile_sample(n, fr, g)
+        rows.append(a + idx)
+        valid_rows += idx.size
+    rows = np.concatenate(rows)
+    cu, _, _ = tile_sample(F2, fc, g)          # gate/up output columns
+    cd, _, _ = tile_sample(Dm, fc, g)          # down output columns / gate-up Dgrad columns
+    cf, _, _ = tile_sample(F, fc, g)           # down Dgrad columns
+    kD, _, _ = tile_sample(Dm, fr, g)          # Wgrad rows (gate/up: d_model)
+    kF, _, _ = tile_sample(F, fr, g)           # Wgrad rows (down: d_ff)
+    t0 = time.perf_counter()
+    oracle.gemm_fprop_grouped(offsets, qx, sx, qwuT, swu, rows=rows, cols=cu)
+    oracle.gemm_fprop_grouped(offsets, qh, sh, qwdT, swd, rows=rows, cols=cd)
+    oracle.gemm_dgrad_grouped(offsets, qdd, sdd, qwd, swd, rows=rows, cols=cf)
+    oracle.gemm_dgrad_grouped(offsets, qdu, sdu, qwu, swu, rows=rows, cols=cd)
+    oracle.gemm_wgrad_grouped(offsets, qhT, shT, qddT, sddT, rows=kF, cols=cd)
+    oracle.gemm_wgrad_grouped(offsets, qxT, sxT, qduT, sduT, rows=kD, cols=cu)
+    tg = time.perf_counter() - t0
+    routed = int(loads.sum())
+    flop = (2.0 * valid_rows * (cu.size * Dm + cd.size * F + cf.size * Dm + cd.size * F2)
+            + 2.0 * routed * (kF.size * cd.size + kD.size * cu.size))
+    total = 2.0 * routed * Dm * F2 * 3 + 2.0 * routed * F * Dm * 3     # Fprop+Dgrad+Wgrad, both projections
+    out = {"value": round(flop / tg / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"casts of X, H, both dY and all {E} experts' weights on the full tensors ({tq:.1f} s); "
+                     f"grouped GEMMs of both projections on a seeded sample of about {frac:g} of every expert's "
+                     f"128x128 output tiles ({valid_rows} of {routed} routed rows x about {fc:.2f} of the columns; "
+                     f"Wgrad about {fr:.2f} x {fc:.2f} of each expert's tiles), full contraction ({tg:.1f} s). "
+                     "value = sampled GEMM FLOP over routed rows / GEMM time",
+           "sample_fraction": round(flop / total, 4),
+           "quant_s": round(tq, 2)}
+    out.update(host_info(oracle))
+    out.update(quant_t1(oracle, d["x"][:8192]))
+    return out
+
+
 def cpu_baseline(d, rows_arg, ue8m0=False, sr=False):
+
     """The CPU oracle, as it stands, on a bounded sample of the same step: the
     three quantizers of X/dY and W on full tensors, then Fprop, Dgrad and Wgrad
     on a sample of output rows (all columns, full contraction).  Reported as the
@@ -706,11 +972,11 @@ def cpu_baseline(d, rows_arg, ue8m0=False, sr=False):
     tg, nr, nk = run(frac, 0)
     flop = 2.0 * nr * N * K + 2.0 * nr * K * N + 2.0 * nk * N * M
     what = "the whole step" if nr == M and nk == K else f"{nr}/{M} Fprop and Dgrad rows, {nk}/{K} Wgrad rows"
-    return {"value": round(flop / tg / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+    return {"value": round(flop / tg / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
             "sample": f"quantizers on the full tensors ({tq:.1f} s), then GEMMs over {what} "
                       f"(all columns, full contraction; {tg:.1f} s); value = GEMM FLOP / GEMM time",
-            "quant_GBps": round(qbytes / tq / 1e9, 3), "quant_s": round(tq, 2)}
+            "quant_GBps": round(qbytes / tq / 1e9, 3), "quant_s": round(tq, 2),
+            **host_info(oracle), **quant_t1(oracle, d["x"])}
 
 
 if __name__ == "__main__":

@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfgb.so")
 SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "swiglu.hip"]
+# the benchmark's clock probe: a library of its own, not linked into libfgb.so
+PROBE_LIB = os.path.join(PKG, "libfgb_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -66,19 +69,26 @@ def _compile(src: str, build_dir: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    build_dir = os.path.join(PKG, "_build")
-    os.makedirs(build_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Build libfgb.so and the benchmark's libfgb_probe.so; returns libfgb.so's path."""
+    build_dir = os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, build_dir), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -57,3 +57,18 @@ def test_quant_stress_bytes():
     assert ab["requant_128x1"] == tensor_bytes(((R, C), 1), ((C // 128, R), 4), ((C, R), 1),
                                                ((R // 128, C), 4))
     assert round(ab["quantize_1x128"] / MB, 1) == 356.0
+
+
+def test_tile_sample_covers_edges_and_fraction():
+    import numpy as np
+    g = np.random.default_rng(0)
+    for n, frac in [(8192, 0.5), (18432, 0.25), (7168, 0.25), (300, 0.5), (128, 0.25), (1, 0.5)]:
+        idx, k, nt = bench.tile_sample(n, frac, g)
+        assert nt == -(-n // 128)
+        assert k == max(1, int(round(frac * nt)))
+        tiles = np.unique(idx // 128)
+        assert tiles.size == k and tiles[0] == 0 and (k < 2 or tiles[-1] == nt - 1)
+        # whole tiles, clipped at n, no duplicates
+        assert np.all(np.diff(idx) > 0) and idx[-1] < n
+        for t in tiles:
+            assert np.sum(idx // 128 == t) == min(128, n - 128 * t)
