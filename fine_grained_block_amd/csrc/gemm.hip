@@ -563,30 +563,66 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     int64_t kb = kb0;
     for (; kb + 1 < kb1; ++kb) kstep(kb, std::true_type{});
     if (kb < kb1) kstep(kb, std::false_type{});
-    if (SPLIT && !active) return;
-
-    // epilogue: row m0 + wm*WTM + 16*i + frow, columns n0 + wn*WTN + 16*j + 4*fg .. +3
+    // ---- Epilogue through LDS.  Stored straight from the MFMA layout, one store
+    // instruction would write 16 rows x 32 bytes; instead the waves write the
+    // tile into the (now idle) stage area in that layout, and every thread then
+    // stores whole 16-byte pieces of output rows, a wave covering one to two
+    // full rows.  Staged rows have a power-of-two pitch and their 16-byte
+    // chunks are XOR-swizzled by (row & 15), so the 16 rows a fragment write
+    // touches land in 16 different chunk positions.  BF16 tiles go in one pass;
+    // FP32 tiles in two passes of 128 rows.  Waves of a half-tile block that
+    // compute nothing still share the stores.
+    constexpr int OB = BF16_OUT ? 2 : 4;                       // bytes per output element
+    constexpr int PITCH = BF16_OUT ? 512 : 1024;               // staged row pitch (>= TN * OB)
+    constexpr int CH = PITCH / 16;                             // 16-byte chunks per staged row
+    constexpr int PASS_ROWS = BF16_OUT ? kTM : kTM / 2;
+    constexpr int PASSES = kTM / PASS_ROWS;
+    static_assert(TN * OB <= PITCH && PASS_ROWS * PITCH <= 2 * kStageBytes, "staged tile fits");
+    static_assert(PASS_ROWS % WTM == 0, "a wave's rows fall in one pass");
+    const int ncols = (int)((g.N - n0) < (SPLIT && half >= 0 ? TN / 2 : TN)
+                            ? (g.N - n0) : (SPLIT && half >= 0 ? TN / 2 : TN));
+    const int nch = ncols * OB / 16;                           // chunks of a stored row (N % 128 == 0)
+    const int nrows = (int)((mend - m0) < kTM ? (mend - m0) : kTM);
+    uint8_t* const st = smem;                                  // LDS (the stage area)
+    __syncthreads();                                           // every wave is done with the stages
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int64_t row = m0 + wm * WTM + i * 16 + frow;
-        if (row >= mend) continue;
+    for (int pass = 0; pass < PASSES; ++pass) {
+        if (pass > 0) __syncthreads();                         // the previous pass's rows are stored
+        const int prow0 = pass * PASS_ROWS;
+        if (active && wm * WTM >= prow0 && wm * WTM < prow0 + PASS_ROWS) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int64_t col = n0 + wn * WTN + j * 16 + fg * 4;
-            if (col >= g.N) continue;
-            if constexpr (BF16_OUT) {
-                const uint32_t lo = cvt_pk_bf16(acc[i][j][0], acc[i][j][1]);
-                const uint32_t hi = cvt_pk_bf16(acc[i][j][2], acc[i][j][3]);
-                st8(reinterpret_cast<uint16_t*>(outp) + row * g.ldo + col, make_uint2(lo, hi));
-            } else {
-                float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(outp) + row * g.ldo + col);
-                float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                if (g.accumulate) {
-                    const float4 pv = *o;
-                    v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+            for (int i = 0; i < MI; ++i) {
+                const int r = wm * WTM - prow0 + i * 16 + frow;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int byte = (wn * WTN + j * 16 + fg * 4) * OB;
+                    const int off = r * PITCH + (((byte >> 4) ^ (r & 15)) << 4) + (byte & 15);
+                    if constexpr (BF16_OUT) {
+                        const uint2 v = make_uint2(cvt_pk_bf16(acc[i][j][0], acc[i][j][1]),
+                                                   cvt_pk_bf16(acc[i][j][2], acc[i][j][3]));
+                        *reinterpret_cast<uint2*>(st + off) = v;
+                    } else {
+                        const float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+                        *reinterpret_cast<float4*>(st + off) = v;
+                    }
                 }
-                *o = v;
             }
+        }
+        __syncthreads();                                       // the pass's rows are staged
+        for (int idx = tid; idx < PASS_ROWS * CH; idx += kV1Threads) {
+            const int r = idx / CH, c = idx % CH;
+            if (c >= nch || prow0 + r >= nrows) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(st + r * PITCH + ((c ^ (r & 15)) << 4));
+            uint8_t* o = reinterpret_cast<uint8_t*>(outp) + ((m0 + prow0 + r) * g.ldo + n0) * OB + c * 16;
+            if constexpr (!BF16_OUT) {
+                if (g.accumulate) {
+                    const float4 pv = *reinterpret_cast<const float4*>(o);
+                    const float4 a = __builtin_bit_cast(float4, v);
+                    st16(o, __builtin_bit_cast(uint4, make_float4(a.x + pv.x, a.y + pv.y, a.z + pv.z, a.w + pv.w)));
+                    continue;
+                }
+            }
+            st16(o, v);
         }
     }
 }
