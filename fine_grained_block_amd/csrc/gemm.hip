@@ -46,32 +46,32 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // across the issue; the _nc forms, used inside the computation for the stage
 // that it does not read, leave the compiler free to schedule around them (the
 // next barrier orders them).
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* lds) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_u8*)lds));
-}
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, const uint8_t* lds) {
+// `lds` is the LDS byte address as an integer (wave-uniform): computed from
+// the shared array's address once, so no generic-to-LDS pointer conversion
+// (and its null check) is repeated per load.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
                  "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)) : "memory");
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, const uint8_t* lds) {
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
                  "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)) : "memory");
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds) : "memory");
 }
-__device__ __forceinline__ void dma16_nc(const void* base, uint32_t off, const uint8_t* lds) {
+__device__ __forceinline__ void dma16_nc(const void* base, uint32_t off, uint32_t lds) {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
                  "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)));
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds));
 }
-__device__ __forceinline__ void dma4_nc(const void* base, uint32_t off, const uint8_t* lds) {
+__device__ __forceinline__ void dma4_nc(const void* base, uint32_t off, uint32_t lds) {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
                  "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds_addr(lds)));
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds));
 }
 
 // Calls f(integral_constant<int, t>) for t = 0 .. N-1, so that every index
@@ -238,6 +238,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     using S = TileShape<TN>;
     constexpr int MI = S::MI, NJ = S::NJ, WTM = S::WTM, WTN = S::WTN;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];   // two stages
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_u8*)smem;           // its LDS byte address
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave % S::WAVES_M, wn = wave / S::WAVES_M;
@@ -361,24 +362,27 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     // from inside the computation; B groups past b_rows are then loaded anyway
     // (from clamped, valid rows into staged rows no fragment read touches), so
     // that no branch splits the computation.
-    auto issue_one = [&](int k, int64_t kb, uint8_t* sbase, auto spread) __attribute__((always_inline)) {
+    auto issue_one = [&](int k, int64_t kb, uint32_t sbase, auto spread) __attribute__((always_inline)) {
         constexpr bool SP = decltype(spread)::value;
         if (k < 4) {
             const uint8_t* A = g.A + kb * kTile;
-            if constexpr (SP) dma16_nc(A, a_off[k], sbase + (wave + 8 * k) * 8 * kTile);
-            else dma16(A, a_off[k], sbase + (wave + 8 * k) * 8 * kTile);
+            const uint32_t d = sbase + (uint32_t)((wave + 8 * k) * 8 * kTile);
+            if constexpr (SP) dma16_nc(A, a_off[k], d);
+            else dma16(A, a_off[k], d);
         } else if (k < 4 + NB) {
             const int i = k - 4;
             const uint8_t* B = Bp + kb * kTile;
-            if constexpr (SP) dma16_nc(B, b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
-            else if ((wave + 8 * i) * 8 < b_rows) dma16(B, b_off[i], sbase + kStageA + (wave + 8 * i) * 8 * kTile);
+            const uint32_t d = sbase + (uint32_t)(kStageA + (wave + 8 * i) * 8 * kTile);
+            if constexpr (SP) dma16_nc(B, b_off[i], d);
+            else if ((wave + 8 * i) * 8 < b_rows) dma16(B, b_off[i], d);
         } else {
             const float* sp = s_base + kb * s_kb;
-            if constexpr (SP) dma4_nc(sp, s_off * 4u, sbase + kStageA + kStageB + wave * 256);
-            else dma4(sp, s_off * 4u, sbase + kStageA + kStageB + wave * 256);
+            const uint32_t d = sbase + (uint32_t)(kStageA + kStageB + wave * 256);
+            if constexpr (SP) dma4_nc(sp, s_off * 4u, d);
+            else dma4(sp, s_off * 4u, d);
         }
     };
-    auto issue = [&](int64_t kb, uint8_t* sbase) __attribute__((always_inline)) {
+    auto issue = [&](int64_t kb, uint32_t sbase) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NL; ++k) issue_one(k, kb, sbase, std::false_type{});
     };
@@ -398,12 +402,14 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     const uint32_t b_lo = (uint32_t)(kStageA + (wn * WTN + frow) * kTile) + fo_lo, b_hi = b_lo ^ 16u;
 
     // One 128-block: MI*NJ MFMAs in a flat schedule where step t issues MFMA t
-    // and folds the partial of MFMA t-2 (a ring of four partials), so no fold
-    // waits on a result still in the matrix pipeline.  The operands of the first
+    // and folds the partial of MFMA t-3 (a ring of four partials), so no fold
+    // waits on a result still in the matrix pipeline and no wait states need
+    // padding between an MFMA and the first read of its result.  The operands of the first
     // MFMA are requested first.  The shorter side's fragments (B for TN = 256,
     // A for TN = 224) stay in registers for the whole block; the other side's
     // stream two pieces ahead through a ring of three.  With a next block
     // (NEXT), its load k is issued at step 1 + 2k.
+    constexpr int kLag = 3;                        // steps between an MFMA and the fold of its result
     constexpr bool ROW_MAJOR = MI >= NJ;           // steps walk columns inside a row piece
     constexpr int NH = ROW_MAJOR ? NJ : MI;        // held fragments
     constexpr int NS = ROW_MAJOR ? MI : NJ;        // streamed fragments
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     constexpr bool kDense1 = OUTER && !SPLIT;
     constexpr int kSpreadFirst = kDense1 ? 0 : 1, kSpreadEvery = kDense1 ? 1 : 2;
     static_assert(kSpreadFirst + kSpreadEvery * (NL - 1) < T, "every spread load falls on a step");
-    auto compute = [&](const uint8_t* sA, uint8_t* nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
+    auto compute = [&](const uint8_t* sA, uint32_t nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next)::value;
         const float* sSA = reinterpret_cast<const float*>(sA + kStageA + kStageB);
         const float* sSB = sSA + 4 * 64;           // region of wave 4 onwards
@@ -446,10 +452,21 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
                 c[0] = sSB[wn * SBW + j];
             }
         };
-        float cs[ROW_MAJOR ? NJ : 1][4];
-        if constexpr (ROW_MAJOR) {
+        // TN = 256, weight-tile scales: a wave's 64 columns start 64-aligned and
+        // lie inside one 128-wide weight tile, so every piece of the block folds
+        // with f[i] = SA(row piece i) * SB(the wave's tile): MI products per block
+        // instead of one per piece
+        constexpr bool ONE_TILE = !OUTER && TN == 256;
+        static_assert(!ONE_TILE || (WTN == 64 && ROW_MAJOR), "one weight tile per wave");
+        float cs[ROW_MAJOR && !ONE_TILE ? NJ : 1][4];
+        if constexpr (ROW_MAJOR && !ONE_TILE) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) col_scales(j, cs[j]);
+        }
+        if constexpr (ONE_TILE) {
+            const float sbw = sSB[wn * SBW];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) sa[i] *= sbw;
         }
         // column-major walk: the scales of column piece p live in cbuf[p & 1]
         float cbuf[2][4];
@@ -463,6 +480,9 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i] * c[r], acc[i][j][r]);
+            } else if constexpr (ONE_TILE) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i], acc[i][j][r]);
             } else {
                 const float f = sa[i] * c[0];
 #pragma unroll
@@ -470,10 +490,11 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             }
         };
         auto scales_of_step = [&](int t) -> const float (&)[4] {
-            if constexpr (ROW_MAJOR) return cs[t % NJ];
+            if constexpr (ONE_TILE) return cs[0];
+            else if constexpr (ROW_MAJOR) return cs[t % NJ];
             else return cbuf[(t / MI) & 1];
         };
-        static_assert(ROW_MAJOR || MI >= 3, "column-major walk needs >= 3 row pieces");
+        static_assert(ROW_MAJOR || MI > kLag, "column-major walk: a scale slot frees up inside a piece");
         static_for<T>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int q = t / PER, h = t % PER;        // streamed piece, held piece
@@ -481,23 +502,28 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
                           (t - kSpreadFirst) / kSpreadEvery < NL)
                 issue_one((t - kSpreadFirst) / kSpreadEvery, kbn, nxt, std::true_type{});
             if constexpr (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
-            // piece q-1's last fold runs at step q*PER + 1, so its scale slot is
-            // free from step q*PER + 2 on: load piece q+1's scales there
-            if constexpr (!ROW_MAJOR && h == 2 && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
+            // piece q-1's last fold runs at step q*PER + kLag - 1, so its scale
+            // slot is free from step q*PER + kLag on: load piece q+1's scales there
+            if constexpr (!ROW_MAJOR && h == kLag && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
             P[t & 3] = ROW_MAJOR
                 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], zero, 0, 0, 0, 0, 0, 0)
                 : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], zero, 0, 0, 0, 0, 0, 0);
-            if constexpr (t >= 2) fold(t - 2, scales_of_step(t - 2));
+            if constexpr (t >= kLag) fold(t - kLag, scales_of_step(t - kLag));
+            // keep the steps in this order: the scheduler would otherwise pull
+            // each fold up behind its own MFMA and pad the wait with s_nop
+            __builtin_amdgcn_sched_barrier(0);
         });
-        fold(T - 2, scales_of_step(T - 2));
-        fold(T - 1, scales_of_step(T - 1));
+        static_for<kLag>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            fold(T - kLag + u, scales_of_step(T - kLag + u));
+        });
     };
 
     // Power-of-two scales: one MFMA per 16x16 piece and block, accumulating
     // through C; the scale operand of a lane is the exponent field (the E8M0
     // byte) of its fragment row's scale: B rows are output columns 16j + frow,
     // A rows are output rows 16i + frow.  Loads of the next block as above.
-    auto compute_po2 = [&](const uint8_t* sA, uint8_t* nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
+    auto compute_po2 = [&](const uint8_t* sA, uint32_t nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next)::value;
         const float* sSA = reinterpret_cast<const float*>(sA + kStageA + kStageB);
         const float* sSB = sSA + 4 * 64;
@@ -549,7 +575,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     auto kstep = [&](int64_t kb, auto next) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next)::value;
         const int st = (int)((kb - kb0) & 1);
-        uint8_t* nxt = smem + (st ^ 1) * kStageBytes;
+        const uint32_t nxt = smem_lds + (uint32_t)((st ^ 1) * kStageBytes);
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads of block kb
         lds_barrier();
         if (!SPLIT || active) {
@@ -559,7 +585,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             issue(kb + 1, nxt);
         }
     };
-    if (kb1 > kb0) issue(kb0, smem);
+    if (kb1 > kb0) issue(kb0, smem_lds);
     int64_t kb = kb0;
     for (; kb + 1 < kb1; ++kb) kstep(kb, std::true_type{});
     if (kb < kb1) kstep(kb, std::false_type{});
