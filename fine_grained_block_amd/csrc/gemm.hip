@@ -468,15 +468,58 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
 #pragma unroll
             for (int i = 0; i < MI; ++i) sa[i] *= sbw;
         }
+        // Wgrad at 224-wide tiles forms its outer-product scales on the matrix core
+        // (below); 256-wide Wgrad tiles have no registers to spare for it
+        constexpr bool MS = OUTER && TN == 224;
         // column-major walk: the scales of column piece p live in cbuf[p & 1]
+        // (not for matrix-core scales)
         float cbuf[2][4];
-        if constexpr (!ROW_MAJOR) col_scales(0, cbuf[0]);
+        if constexpr (!ROW_MAJOR && !MS) col_scales(0, cbuf[0]);
+
+        // Outer-product scales (Wgrad): the products SA(row) * SB(column) of four
+        // 16x16 pieces come from one fp32 4-block 16x16x1 MFMA, already in the
+        // fold's lane layout -- output register 4*b + r of lane l is A_b[4*(l>>4)
+        // + r] * B_b[l & 15] -- instead of 16 vector multiplies.  A group is the
+        // PER pieces of one streamed fragment (a row piece for the row-major
+        // walk, block b = column piece b; a column piece for the column-major
+        // walk, block b = row piece b), so A_b carries the column scales and B_b
+        // the row scales.  The products of group g are formed at the last step
+        // of group g-1 into S[g & 1]; a group's last fold comes kLag < PER steps
+        // after its last MFMA, before group g+2 overwrites the slot.
+        typedef float v16f __attribute__((ext_vector_type(16)));
+        v16f S[MS ? 2 : 1];
+        float ocol = 0.0f, orow = 0.0f, ocol_next = 0.0f;
+        auto outer_products = [&](int g) __attribute__((always_inline)) {
+            if constexpr (MS) {
+                const v16f z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if constexpr (ROW_MAJOR)      // row piece g: columns of the wave (one per lane), row 16g + frow
+                    S[g & 1] = __builtin_amdgcn_mfma_f32_16x16x1f32(ocol, sa[g], z, 0, 0, 0);
+                else                          // column piece g: its columns 16g + frow, rows 16b + frow
+                    S[g & 1] = __builtin_amdgcn_mfma_f32_16x16x1f32(ocol, orow, z, 0, 0, 0);
+            }
+        };
+        if constexpr (MS) {
+            static_assert(PER > kLag && PER == 4, "four pieces per outer-product MFMA; a slot frees in time");
+            if constexpr (ROW_MAJOR) {
+                ocol = sSB[wn * WTN + lane];                      // column 16*(lane>>4) + (lane&15) of the wave
+            } else {
+                ocol = sSB[wn * WTN + frow];                      // column piece 0
+                ocol_next = sSB[wn * WTN + 16 + frow];
+                orow = fg == 0 ? sa[0] : (fg == 1 ? sa[1] : (fg == 2 ? sa[2] : sa[3]));   // row 16*fg + frow
+            }
+            outer_products(0);
+        }
 
         v4f P[4];
         auto fold = [&](int t, const float (&c)[4]) {
             const int i = ROW_MAJOR ? t / NJ : t % MI;
             const int j = ROW_MAJOR ? t % NJ : t / MI;
-            if constexpr (OUTER) {
+            if constexpr (MS) {
+                const int g = t / PER, h = t % PER;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], S[g & 1][4 * h + r], acc[i][j][r]);
+            } else if constexpr (OUTER) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i] * c[r], acc[i][j][r]);
@@ -490,7 +533,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             }
         };
         auto scales_of_step = [&](int t) -> const float (&)[4] {
-            if constexpr (ONE_TILE) return cs[0];
+            if constexpr (ONE_TILE || MS) return cs[0];
             else if constexpr (ROW_MAJOR) return cs[t % NJ];
             else return cbuf[(t / MI) & 1];
         };
@@ -504,7 +547,14 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             if constexpr (h == 0 && q + 2 < NS) sf[(q + 2) % 3] = streamed(q + 2);
             // piece q-1's last fold runs at step q*PER + kLag - 1, so its scale
             // slot is free from step q*PER + kLag on: load piece q+1's scales there
-            if constexpr (!ROW_MAJOR && h == kLag && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
+            if constexpr (!ROW_MAJOR && !MS && h == kLag && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
+            if constexpr (MS && h == PER - 1 && q + 1 < NS) {
+                if constexpr (!ROW_MAJOR) {
+                    ocol = ocol_next;                                             // column piece q + 1
+                    if (q + 2 < NS) ocol_next = sSB[wn * WTN + 16 * (q + 2) + frow];
+                }
+                outer_products(q + 1);
+            }
             P[t & 3] = ROW_MAJOR
                 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], zero, 0, 0, 0, 0, 0, 0)
                 : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], zero, 0, 0, 0, 0, 0, 0);
