@@ -25,7 +25,8 @@ namespace fgb {
 // group reads the tile's 256 contiguous bytes) and reduces its absmax with
 // DPP inside the 16-lane row.
 // ---------------------------------------------------------------------------
-constexpr int kQ1Rows = 64;
+constexpr int kQ1Per = 4;                       // rows per 16-lane group
+constexpr int kQ1Rows = 16 * kQ1Per;
 
 // PO2: power-of-two scales (the UE8M0 values, held in fp32); otherwise absmax/448.
 // SR: stochastic rounding of the cast with the words of `sr` (absmax/448 scales).
@@ -42,9 +43,9 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     const int64_t c = j * kTile + lane16 * 8;
     const bool cok = c < C;
 
-    uint4 v[4];
+    uint4 v[kQ1Per];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kQ1Per; ++it) {
         const int64_t r = rb + grp + 16 * it;
         v[it] = (cok && r < R) ? ld16_stream(x + r * ldx + c) : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     // multiplier of row it from that lane
     float a_own = 0.0f;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kQ1Per; ++it) {
         const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
         u16x2 m2 = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
 #pragma unroll
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     else tile_scale(a_own, sc_own, inv_own);
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kQ1Per; ++it) {
         const int64_t r = rb + grp + 16 * it;
         const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
         const float inv = __shfl(inv_own, (lane & 48) | it, 64);
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
         o1 = fix_codes(o1, inv, bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
         if (cok && r < R) st8(q + r * ldq + c, make_uint2(o0, o1));
     }
-    if (lane16 < 4) {          // the block's segment j exists (grid = ceil(C/128)): only rows can be past the end
+    if (lane16 < kQ1Per) {     // the block's segment j exists (grid = ceil(C/128)): only rows can be past the end
         const int64_t r = rb + grp + 16 * lane16;
         if (r < R) s[j * lds + r] = PO2 ? e8m0_to_f32(eb_own) : sc_own;
     }
@@ -188,22 +189,46 @@ __global__ __launch_bounds__(256) void k_tile128(
     constexpr bool REQ = MODE == kTileRequant || MODE == kTileRequant128x128;
     uint32_t vw[REQ ? 1 : 8][4];
     float vf[REQ ? 8 : 1][8];
+    if constexpr (REQ) {
+        // dequantize: v = fl32(dec(q) * s) with the row's 1x128 scale, or the
+        // tile's scale s_in[i * lds_in + j] for a 128x128 weight tile.  The
+        // codes are requested first; the 128 row scales of the block go through
+        // LDS, one load per thread instead of eight per thread.
+        const uint8_t* p = static_cast<const uint8_t*>(in);
+        uint2 w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + rg * 8 + i;
+            w[i] = (cok && r < R) ? ld8(p + r * ldin + cc) : make_uint2(0u, 0u);
+        }
+        float sr[8];
+        if constexpr (MODE == kTileRequant) {
+            if (t < kTile) col_mul[t] = r0 + t < R ? s_in[(int64_t)blockIdx.y * lds_in + r0 + t] : 0.0f;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sr[i] = col_mul[rg * 8 + i];
+            // (col_mul is rewritten with the column multipliers only after the
+            // barrier that publishes the column maxima, which every thread
+            // reaches after these reads)
+        } else {
+            const float st = s_in[(int64_t)blockIdx.x * lds_in + blockIdx.y];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sr[i] = st;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float si = (cok && r0 + rg * 8 + i < R) ? sr[i] : 0.0f;
+            const float2 d0 = e4m3x2_decode<false>(w[i].x), d1 = e4m3x2_decode<true>(w[i].x);
+            const float2 d2 = e4m3x2_decode<false>(w[i].y), d3 = e4m3x2_decode<true>(w[i].y);
+            vf[i][0] = d0.x * si; vf[i][1] = d0.y * si; vf[i][2] = d1.x * si; vf[i][3] = d1.y * si;
+            vf[i][4] = d2.x * si; vf[i][5] = d2.y * si; vf[i][6] = d3.x * si; vf[i][7] = d3.y * si;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t r = r0 + rg * 8 + i;
         const bool ok = cok && r < R;
         if constexpr (REQ) {
-            // dequantize: v = fl32(dec(q) * s) with the row's 1x128 scale, or
-            // the tile's scale s_in[i * lds_in + j] for a 128x128 weight tile
-            const uint8_t* p = static_cast<const uint8_t*>(in);
-            const uint2 w = ok ? ld8(p + r * ldin + cc) : make_uint2(0u, 0u);
-            const float sr = !ok ? 0.0f
-                : MODE == kTileRequant ? s_in[(int64_t)blockIdx.y * lds_in + r]
-                                       : s_in[(int64_t)blockIdx.x * lds_in + blockIdx.y];
-            const float2 d0 = e4m3x2_decode<false>(w.x), d1 = e4m3x2_decode<true>(w.x);
-            const float2 d2 = e4m3x2_decode<false>(w.y), d3 = e4m3x2_decode<true>(w.y);
-            vf[i][0] = d0.x * sr; vf[i][1] = d0.y * sr; vf[i][2] = d1.x * sr; vf[i][3] = d1.y * sr;
-            vf[i][4] = d2.x * sr; vf[i][5] = d2.y * sr; vf[i][6] = d3.x * sr; vf[i][7] = d3.y * sr;
         } else {
             const uint16_t* p = static_cast<const uint16_t*>(in);
             const uint4 w = ok ? ld16_stream(p + r * ldin + cc) : make_uint4(0u, 0u, 0u, 0u);
