@@ -1,5 +1,5 @@
-// Internal launch interface of libfgb: the C ABI (abi.cpp) validates arguments
-// and calls these; the kernels live in quant.hip and gemm.hip.
+// Internal launch interface of libfgb: the C ABI (abi.hip) validates arguments
+// and calls these; the kernels live in quant.hip, gemm.hip and swiglu.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
