@@ -19,8 +19,10 @@ the whole step time, quantization included) in TFLOP/s.  Per-kernel durations
 come from HIP events recorded around every launch on the stream the kernels
 run on, over the timed steps (warm: the steps run back to back); `roofline`
 prices the dominant kernel against MI355X's dense FP8 MFMA peak (5.0 PFLOP/s
-at 2.4 GHz) and, with the clock the chip sustains under an MFMA-saturating
-probe (`clock_mhz`), against the peak at that clock (`frac_at_clock`).
+at 2.4 GHz) and, with the shader clock measured while that kernel runs back to
+back (`clock_mhz`; the chip lowers it under this load), against the peak at
+that clock (`frac_at_clock`); `clock_mhz_mfma_only` is the clock under a probe
+that runs FP8 MFMAs and nothing else.
 `kernels` lists every kernel's rate against its own roofline (HBM for the
 quantizers).  `cold` is the median of 50 steps after 10 warm-ups, each after a
 1 GiB read scrub outside its events, labelled as such.  `cpu_baseline` times
@@ -571,9 +573,7 @@ def cpu_model():
     return name, n or os.cpu_count()
 
 
-def probe_clock_mhz(torch, dev, iters=200000):
-    """Median shader clock (MHz) over the CUs while every SIMD runs FP8 MFMAs
-    (libfgb_probe.so, built beside libfgb.so), or None if the probe is missing."""
+def _probe_lib():
     import ctypes
     path = os.path.join(ROOT, "fine_grained_block_amd", "libfgb_probe.so")
     if not os.path.exists(path):
@@ -581,11 +581,58 @@ def probe_clock_mhz(torch, dev, iters=200000):
     L = ctypes.CDLL(path)
     L.fgb_probe_clock.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     L.fgb_probe_clock.restype = ctypes.c_int
+    L.fgb_probe_clock_begin.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_void_p]
+    L.fgb_probe_clock_begin.restype = ctypes.c_int
+    L.fgb_probe_clock_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    L.fgb_probe_clock_end.restype = ctypes.c_int
+    return L
+
+
+def probe_clock_mhz(torch, dev, iters=200000):
+    """Median shader clock (MHz) over the CUs while every SIMD runs FP8 MFMAs
+    and nothing else (libfgb_probe.so, built beside libfgb.so), or None if the
+    probe is missing."""
+    import ctypes
+    L = _probe_lib()
+    if L is None:
+        return None
     mhz = ctypes.c_double(0.0)
     st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     if L.fgb_probe_clock(iters, ctypes.byref(mhz), st) != 0:
         return None
     return mhz.value
+
+
+def clock_during_mhz(torch, dev, fn, kernel_ms, reps=3):
+    """Median shader clock (MHz) while `fn` (one kernel launch) runs back to
+    back: the kernel is queued on the current stream for about 4 windows, then
+    single-wave sleeping samplers on a second stream (default priority) read
+    s_memtime against the constant-rate counter over one window; the median of
+    `reps` such samples.  None if the probe is missing."""
+    import ctypes
+    L = _probe_lib()
+    if L is None:
+        return None
+    main_s = torch.cuda.current_stream(dev)
+    side_s = torch.cuda.Stream(dev)
+    window_us = max(200.0, min(2000.0, 2.0 * kernel_ms * 1e3))
+    launches = max(4, int(4 * window_us / (kernel_ms * 1e3)) + 1)
+    out = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            fn()
+        st = ctypes.c_void_p(side_s.cuda_stream)
+        if L.fgb_probe_clock_begin(64, window_us, st) != 0:
+            torch.cuda.synchronize()
+            return None
+        mhz = ctypes.c_double(0.0)
+        rc = L.fgb_probe_clock_end(ctypes.byref(mhz), st)
+        torch.cuda.synchronize()
+        if rc != 0:
+            return None
+        out.append(mhz.value)
+    return float(sorted(out)[len(out) // 2])
 
 
 def main():
@@ -716,13 +763,24 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_rate / 1e12, 1),
                 "peak": FP8_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(dom_rate / FP8_PEAK, 4),
                 "traffic": traffic_record(dom)}
-    mhz = probe_clock_mhz(torch, dev)
+    # the shader clock while each GEMM runs back to back, and the GEMM's rate
+    # against the MFMA peak at that clock
+    fns = {name: fn for name, fn, _, _, _ in kernels}
+    for name in gemms:
+        c = clock_during_mhz(torch, dev, fns[name], gemms[name])
+        if c:
+            kinfo[name]["clock_mhz"] = round(c, 1)
+            kinfo[name]["frac_at_clock"] = round(work[name]["flop"] / (gemms[name] * 1e-3) / (FP8_PEAK * c / 2400.0), 4)
+    mhz = kinfo[dom].get("clock_mhz")
+    mhz_probe = probe_clock_mhz(torch, dev)
     if mhz:
         # the MFMA peak scales with the clock: 5.0 PFLOP/s is quoted at 2.4 GHz
         roofline["clock_mhz"] = round(mhz, 1)
         roofline["frac_at_clock"] = round(dom_rate / (FP8_PEAK * mhz / 2400.0), 4)
-        roofline["clock_how"] = ("median shader clock over the CUs under an MFMA-saturating probe "
-                                 "(s_memtime ticks per s_memrealtime time)")
+        roofline["clock_how"] = ("median shader clock while the kernel runs back to back (sleeping "
+                                 "single-wave samplers beside it: s_memtime ticks per s_memrealtime time)")
+    if mhz_probe:
+        roofline["clock_mhz_mfma_only"] = round(mhz_probe, 1)
     quant_ms = sum(v for k, v in per_kernel_ms.items() if "bytes" in work[k])
     config.update({"gemm_flop_per_step": step_flop, "quant_bytes_per_step": quant_bytes,
                    "schedule": ("overlap: casts " + ", ".join(n for n, _, _, lane, _ in kernels if lane == 1)

@@ -41,37 +41,34 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // 32-bit byte offset.  Issued from inline assembly so that the compiler's wait
 // insertion does not treat the in-flight loads as pending writes to every LDS
 // location (which would make every LDS read wait for the prefetch); the kernel
-// waits for each stage itself with vmcnt.  M0 carries the LDS address and is
-// restored afterwards.  The "memory" clobber keeps LDS accesses from moving
-// across the issue; the _nc forms, used inside the computation for the stage
+// waits for each stage itself with vmcnt.  M0 carries the LDS address; the
+// asm declares it clobbered, so the compiler re-establishes M0 only where it
+// needs it itself, and no save and restore is spent per load.  The "memory"
+// clobber keeps LDS accesses from moving across the issue; the _nc forms, used inside the computation for the stage
 // that it does not read, leave the compiler free to schedule around them (the
 // next barrier orders them).
 // `lds` is the LDS byte address as an integer (wave-uniform): computed from
 // the shared array's address once, so no generic-to-LDS pointer conversion
 // (and its null check) is repeated per load.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "m0", "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "m0", "memory");
 }
 __device__ __forceinline__ void dma16_nc(const void* base, uint32_t off, uint32_t lds) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "m0");
 }
 __device__ __forceinline__ void dma4_nc(const void* base, uint32_t off, uint32_t lds) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "m0");
 }
 
 // Calls f(integral_constant<int, t>) for t = 0 .. N-1, so that every index
@@ -420,6 +417,18 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     constexpr bool kDense1 = OUTER && !SPLIT;
     constexpr int kSpreadFirst = kDense1 ? 0 : 1, kSpreadEvery = kDense1 ? 1 : 2;
     static_assert(kSpreadFirst + kSpreadEvery * (NL - 1) < T, "every spread load falls on a step");
+    // The two waves of a SIMD share its issue port, and among waves of equal
+    // priority the older one wins, so one wave of each pair would finish its
+    // block early and then sit at the barrier while the other runs alone.  Each
+    // wave takes the higher priority for the first half of its steps and drops
+    // back for the second, so the one that is ahead yields.  (Not for Wgrad's
+    // matrix-core outer products, where it measured no gain.)
+    constexpr bool kBalance = !(OUTER && TN == 224 && !PO2);
+    auto balance_priority = [&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (kBalance && t == 0) __builtin_amdgcn_s_setprio(1);
+        if constexpr (kBalance && t == T / 2) __builtin_amdgcn_s_setprio(0);
+    };
     auto compute = [&](const uint8_t* sA, uint32_t nxt, int64_t kbn, auto next) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next)::value;
         const float* sSA = reinterpret_cast<const float*>(sA + kStageA + kStageB);
@@ -541,6 +550,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         static_for<T>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int q = t / PER, h = t % PER;        // streamed piece, held piece
+            balance_priority(tc);
             if constexpr (NEXT && t >= kSpreadFirst && (t - kSpreadFirst) % kSpreadEvery == 0 &&
                           (t - kSpreadFirst) / kSpreadEvery < NL)
                 issue_one((t - kSpreadFirst) / kSpreadEvery, kbn, nxt, std::true_type{});
@@ -605,6 +615,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         static_for<T>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int q = t / PER, h = t % PER;
+            balance_priority(tc);
             if constexpr (NEXT && t >= kSpreadFirst && (t - kSpreadFirst) % kSpreadEvery == 0 &&
                           (t - kSpreadFirst) / kSpreadEvery < NL)
                 issue_one((t - kSpreadFirst) / kSpreadEvery, kbn, nxt, std::true_type{});

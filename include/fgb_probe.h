@@ -12,6 +12,16 @@
  * Allocates a small device buffer, launches on `stream` (a hipStream_t) and
  * synchronizes it.  Returns 0, -1 for a bad argument (mhz NULL, iters <= 0),
  * -2 for a HIP error.
+ *
+ * fgb_probe_clock_begin / fgb_probe_clock_end: the clock while some other
+ * kernel runs.  begin launches `blocks` single-wave blocks on `stream` (give
+ * it a stream other than the measured kernel's, after that kernel was
+ * launched); each mostly sleeps and measures s_memtime ticks over `window_us`
+ * microseconds of the constant-rate counter.  end waits for them on `stream`
+ * and returns in *mhz the median over the blocks.  One sample at a time per
+ * process: begin returns -1 while one is running, as for a bad argument
+ * (blocks outside 1..4096, window outside (0, 1e6] us); end returns -1 with no
+ * sample running or mhz NULL; both return -2 for a HIP error.
  */
 #ifndef FGB_PROBE_H
 #define FGB_PROBE_H
@@ -21,6 +31,8 @@ extern "C" {
 #endif
 
 int fgb_probe_clock(int iters, double* mhz, void* stream);
+int fgb_probe_clock_begin(int blocks, double window_us, void* stream);
+int fgb_probe_clock_end(double* mhz, void* stream);
 
 #ifdef __cplusplus
 }
