@@ -42,12 +42,16 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     const int64_t j = blockIdx.y;
     const int64_t c = j * kTile + lane16 * 8;
     const bool cok = c < C;
+    // all kQ1Rows rows and the whole 128-column block inside the tensor
+    // (block-uniform): no checks, rows addressed from one 64-bit pointer
+    const bool full = rb + kQ1Rows <= R && (j + 1) * kTile <= C;
+    const uint16_t* const xrow = x + (rb + grp) * ldx + c;
 
     uint4 v[kQ1Per];
 #pragma unroll
     for (int it = 0; it < kQ1Per; ++it) {
-        const int64_t r = rb + grp + 16 * it;
-        v[it] = (cok && r < R) ? ld16_stream(x + r * ldx + c) : make_uint4(0u, 0u, 0u, 0u);
+        const bool ok = full || (cok && rb + grp + 16 * it < R);
+        v[it] = ok ? ld16_stream(xrow + 16 * it * ldx) : make_uint4(0u, 0u, 0u, 0u);
     }
     // the 4 row maxima; lane it of the 16-lane row group then computes row it's
     // scale (one pair of divisions per wave) and every lane fetches the
@@ -69,6 +73,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     if constexpr (PO2) tile_scale_ue8m0(a_own, eb_own, inv_own);
     else tile_scale(a_own, sc_own, inv_own);
     const int lane = threadIdx.x & 63;
+    uint8_t* const qrow = q + (rb + grp) * ldq + c;
 #pragma unroll
     for (int it = 0; it < kQ1Per; ++it) {
         const int64_t r = rb + grp + 16 * it;
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
         }
         o0 = fix_codes(o0, inv, bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
         o1 = fix_codes(o1, inv, bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
-        if (cok && r < R) st8(q + r * ldq + c, make_uint2(o0, o1));
+        if (full || (cok && r < R)) st8(qrow + 16 * it * ldq, make_uint2(o0, o1));
     }
     if (lane16 < kQ1Per) {     // the block's segment j exists (grid = ceil(C/128)): only rows can be past the end
         const int64_t r = rb + grp + 16 * lane16;
@@ -182,6 +187,10 @@ __global__ __launch_bounds__(256) void k_tile128(
     const int64_t c0 = (int64_t)blockIdx.y * kTile;
     const int64_t cc = c0 + cg * 8;
     const bool cok = cc < C;
+    // the whole 128x128 tile lies inside the tensor (block-uniform): then no
+    // row or column checks, and row i of a patch is its row 0 plus i leading
+    // dimensions (one 64-bit address per thread, scalar row steps)
+    const bool full = r0 + kTile <= R && c0 + kTile <= C;
 
     // The thread's 8x8 patch, V(i, k) = row i, column k: bf16 inputs stay
     // packed two to a word and are widened where used (exact); requant inputs
@@ -194,12 +203,15 @@ __global__ __launch_bounds__(256) void k_tile128(
         // tile's scale s_in[i * lds_in + j] for a 128x128 weight tile.  The
         // codes are requested first; the 128 row scales of the block go through
         // LDS, one load per thread instead of eight per thread.
-        const uint8_t* p = static_cast<const uint8_t*>(in);
+        const uint8_t* prow = static_cast<const uint8_t*>(in) + (r0 + rg * 8) * ldin + cc;
         uint2 w[8];
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t r = r0 + rg * 8 + i;
-            w[i] = (cok && r < R) ? ld8(p + r * ldin + cc) : make_uint2(0u, 0u);
+            for (int i = 0; i < 8; ++i) w[i] = ld8(prow + i * ldin);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                w[i] = (cok && r0 + rg * 8 + i < R) ? ld8(prow + i * ldin) : make_uint2(0u, 0u);
         }
         float sr[8];
         if constexpr (MODE == kTileRequant) {
@@ -224,14 +236,12 @@ __global__ __launch_bounds__(256) void k_tile128(
             vf[i][4] = d2.x * si; vf[i][5] = d2.y * si; vf[i][6] = d3.x * si; vf[i][7] = d3.y * si;
         }
     }
+    if constexpr (!REQ) {
+        const uint16_t* prow = static_cast<const uint16_t*>(in) + (r0 + rg * 8) * ldin + cc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t r = r0 + rg * 8 + i;
-        const bool ok = cok && r < R;
-        if constexpr (REQ) {
-        } else {
-            const uint16_t* p = static_cast<const uint16_t*>(in);
-            const uint4 w = ok ? ld16_stream(p + r * ldin + cc) : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < 8; ++i) {
+            const bool ok = full || (cok && r0 + rg * 8 + i < R);
+            const uint4 w = ok ? ld16_stream(prow + i * ldin) : make_uint4(0u, 0u, 0u, 0u);
             vw[i][0] = w.x; vw[i][1] = w.y; vw[i][2] = w.z; vw[i][3] = w.w;
         }
     }
@@ -268,7 +278,7 @@ __global__ __launch_bounds__(256) void k_tile128(
                                           V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
             const uint32_t o1 = fix_codes(e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv), iv,
                                           V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
-            if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
+            if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
         }
         // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
         const int64_t rr = r0 + rg * 8 + cg;
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(256) void k_tile128(
                 const uint32_t o1 = fix_codes(
                     e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]), inv[4],
                     V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
-                if (cok && r < R) st8(q + r * ldq + cc, make_uint2(o0, o1));
+                if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
             }
         }
         if (qT == nullptr) return;
@@ -436,14 +446,14 @@ __global__ __launch_bounds__(256) void k_tile128(
     }
     __syncthreads();
     // 128 staged rows of 128 bytes; 8 threads per row, 16 bytes each, 4 passes.
+    uint8_t* const pq = qT + (c0 + (t >> 3)) * ldqT + r0 + (t & 7) * 16;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int row = p * 32 + (t >> 3);
         const int seg = t & 7;
-        const int64_t c = c0 + row;
         const uint2 a = *reinterpret_cast<const uint2*>(&tr[row * kTrStride + seg * 16]);
         const uint2 b = *reinterpret_cast<const uint2*>(&tr[row * kTrStride + seg * 16 + 8]);
-        if (c < C) st16(qT + c * ldqT + r0 + seg * 16, make_uint4(a.x, a.y, b.x, b.y));
+        if (full || c0 + row < C) st16(pq + p * 32 * ldqT, make_uint4(a.x, a.y, b.x, b.y));
     }
 }
 
