@@ -327,8 +327,37 @@ def moe_step(fgb, torch, dev, d, bufs=None):
     def quant_w(w, q, qT, s):                 # all experts' weights in one launch
         fgb.quantize_128x128_batched(w, q=q, qT=qT, s=s)
 
+    loads = [int(n) for n in d["loads"]]
+
+    def grouped_roofline(kind, K, N):
+        """Sum over experts of max(FLOP / FP8 peak, bytes / HBM peak) in
+        microseconds for one grouped call (routed rows only): Fprop/Dgrad read
+        the expert's [rows, K] codes, its [N, K] weight codes and their fp32
+        scales and write [rows, N] bf16; Wgrad reads both transposed operands
+        (K and N codes per row) and their scales and writes the expert's fp32
+        [K, N] dW, also for an empty expert (zeros).  Returns (us, number of
+        experts below the ridge)."""
+        tot, mem_bound = 0.0, 0
+        for n in loads:
+            fl = 2.0 * n * K * N
+            if kind == "rows":
+                by = n * K + 4 * n * (K // T) + N * K + 4 * (K // T) * (N // T) + 2 * n * N
+            else:
+                by = n * (K + N) + 4 * (n // T + (n % T > 0)) * (K + N) + 4 * K * N
+            tc, tm = fl / FP8_PEAK, by / HBM_PEAK
+            mem_bound += tm > tc
+            tot += max(tc, tm)
+        return tot * 1e6, mem_bound
+
+    def gwork(flop, kind, K, N):
+        us, mb = grouped_roofline(kind, K, N)
+        return {"flop": flop, "roofline_us": us, "experts_memory_bound": mb}
+
     up = {"flop": 2.0 * rows * Dm * F2}
     down = {"flop": 2.0 * rows * F * Dm}
+    fup, fdown = gwork(up["flop"], "rows", Dm, F2), gwork(down["flop"], "rows", F, Dm)
+    dup, ddown = gwork(up["flop"], "rows", F2, Dm), gwork(down["flop"], "rows", Dm, F)
+    wup, wdown = gwork(up["flop"], "k", Dm, F2), gwork(down["flop"], "k", F, Dm)
     nb2, nb1 = F2 // T, F // T
     swf_bytes = R * F2 * 2 + R * F2 + 4 * R * nb2 + R * F + 4 * R * nb1
     swb_bytes = R * F2 + 4 * R * nb2 + R * F * 2 + R * F2 + 4 * R * nb2 + F2 * R + 4 * Rt * F2
@@ -339,29 +368,29 @@ def moe_step(fgb, torch, dev, d, bufs=None):
         ("quantize_128x128_w_up", lambda: quant_w(w_up, b["qwu"], b["qwuT"], b["swu"]),
          {"bytes": E * algorithmic_bytes(R, Dm, F2)["quantize_128x128_w"]}),
         ("gemm_fprop_grouped_up", lambda: fgb.gemm_fprop_grouped(od, b["qx"], b["sx"], b["qwuT"], b["swu"], y=b["gu"]),
-         up),
+         fup),
         ("swiglu_fwd_quant", lambda: fgb.swiglu_fwd_quant(b["gu"], q_gu=b["q_gu"], s_gu=b["s_gu"], q_h=b["q_h"],
                                                           s_h=b["s_h"]), {"bytes": swf_bytes}),
         ("quantize_128x128_w_down", lambda: quant_w(w_down, b["qwd"], b["qwdT"], b["swd"]),
          {"bytes": E * algorithmic_bytes(R, F, Dm)["quantize_128x128_w"]}),
         ("gemm_fprop_grouped_down", lambda: fgb.gemm_fprop_grouped(od, b["q_h"], b["s_h"], b["qwdT"], b["swd"],
-                                                                   y=b["y"]), down),
+                                                                   y=b["y"]), fdown),
         ("quantize_dual_dy", lambda: fgb.quantize_dual(dy, q=b["qdy"], s=b["sdy"], qT=b["qdyT"], sT=b["sdyT"]),
          {"bytes": ab_h["quantize_dual_dy"]}),
         ("gemm_dgrad_grouped_down", lambda: fgb.gemm_dgrad_grouped(od, b["qdy"], b["sdy"], b["qwd"], b["swd"],
-                                                                   dx=b["dh"]), down),
+                                                                   dx=b["dh"]), ddown),
         ("requant_128x1_h", lambda: fgb.requant_128x1(b["q_h"], b["s_h"], qT=b["q_hT"], sT=b["s_hT"]),
          {"bytes": algorithmic_bytes(R, F, Dm)["requant_128x1_x"]}),
         ("gemm_wgrad_grouped_down", lambda: fgb.gemm_wgrad_grouped(od, b["q_hT"], b["s_hT"], b["qdyT"], b["sdyT"],
-                                                                   dw=b["dw_down"]), down),
+                                                                   dw=b["dw_down"]), wdown),
         ("swiglu_bwd_quant", lambda: fgb.swiglu_bwd_quant(b["q_gu"], b["s_gu"], b["dh"], q=b["q_dgu"], s=b["s_dgu"],
                                                           qT=b["q_dguT"], sT=b["s_dguT"]), {"bytes": swb_bytes}),
         ("gemm_dgrad_grouped_up", lambda: fgb.gemm_dgrad_grouped(od, b["q_dgu"], b["s_dgu"], b["qwu"], b["swu"],
-                                                                 dx=b["dx"]), up),
+                                                                 dx=b["dx"]), dup),
         ("requant_128x1_x", lambda: fgb.requant_128x1(b["qx"], b["sx"], qT=b["qxT"], sT=b["sxT"]),
          {"bytes": ab_x["requant_128x1_x"]}),
         ("gemm_wgrad_grouped_up", lambda: fgb.gemm_wgrad_grouped(od, b["qxT"], b["sxT"], b["q_dguT"], b["s_dguT"],
-                                                                 dw=b["dw_up"]), up),
+                                                                 dw=b["dw_up"]), wup),
     ]
     # second stream: the down weights' cast, the dY casts and the two requants
     lanes = {"quantize_128x128_w_down": (1, []), "quantize_dual_dy": (1, []),
@@ -753,6 +782,11 @@ def main():
             rate = work[name]["flop"] / (ms * 1e-3)
             kinfo[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(rate / 1e12, 1),
                            "frac_fp8_peak": round(rate / FP8_PEAK, 4)}
+            if "roofline_us" in work[name]:
+                # grouped: the per-expert max(compute, memory) bound summed over experts
+                kinfo[name]["roofline_us"] = round(work[name]["roofline_us"], 1)
+                kinfo[name]["frac_of_roofline"] = round(work[name]["roofline_us"] / (ms * 1e3), 4)
+                kinfo[name]["experts_memory_bound"] = work[name]["experts_memory_bound"]
         else:
             rate = work[name]["bytes"] / (ms * 1e-3)
             kinfo[name] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
