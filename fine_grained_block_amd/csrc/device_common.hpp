@@ -98,6 +98,15 @@ __device__ __forceinline__ uint32_t fix_codes(uint32_t codes, float mul, float p
     if (__builtin_expect(mul == 0.0f, 0)) return nan_products(codes, p0, p1, p2, p3);
     return codes;
 }
+// A cast multiplier that needs no fix-up of its codes: finite and nonzero (the
+// common case, where no product can be NaN).  Callers test it once for all the
+// multipliers a thread uses and branch to a path without fix_codes.
+__device__ __forceinline__ bool plain_mul(float m) { return m == m && m != 0.0f; }
+template <bool FIX>
+__device__ __forceinline__ uint32_t fix_codes_if(uint32_t codes, float mul, float p0, float p1, float p2, float p3) {
+    if constexpr (FIX) return fix_codes(codes, mul, p0, p1, p2, p3);
+    else return codes;
+}
 // The same for four codes of four different tiles (byte i: multiplier m_i, product p_i).
 __device__ __forceinline__ uint32_t fix_codes4(uint32_t codes, float m0, float m1, float m2, float m3,
                                                float p0, float p1, float p2, float p3) {

@@ -74,27 +74,42 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     else tile_scale(a_own, sc_own, inv_own);
     const int lane = threadIdx.x & 63;
     uint8_t* const qrow = q + (rb + grp) * ldq + c;
+    float invs[kQ1Per];
+    bool plain = true;
 #pragma unroll
     for (int it = 0; it < kQ1Per; ++it) {
-        const int64_t r = rb + grp + 16 * it;
-        const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-        const float inv = __shfl(inv_own, (lane & 48) | it, 64);
-        uint32_t o0, o1;
-        if constexpr (SR) {
-            uint32_t u[8];
-            sr_words8(sr, r, c, u);
-            o0 = e4m3x4_sr(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv,
-                           u[0], u[1], u[2], u[3]);
-            o1 = e4m3x4_sr(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv,
-                           u[4], u[5], u[6], u[7]);
-        } else {
-            o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
-            o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
-        }
-        o0 = fix_codes(o0, inv, bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
-        o1 = fix_codes(o1, inv, bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
-        if (full || (cok && r < R)) st8(qrow + 16 * it * ldq, make_uint2(o0, o1));
+        invs[it] = __shfl(inv_own, (lane & 48) | it, 64);
+        plain = plain && plain_mul(invs[it]);
     }
+    auto emit = [&](auto fix) __attribute__((always_inline)) {
+        constexpr bool FIX = decltype(fix)::value;
+#pragma unroll
+        for (int it = 0; it < kQ1Per; ++it) {
+            const int64_t r = rb + grp + 16 * it;
+            const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+            const float inv = invs[it];
+            uint32_t o0, o1;
+            if constexpr (SR) {
+                uint32_t u[8];
+                sr_words8(sr, r, c, u);
+                o0 = e4m3x4_sr(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv,
+                               u[0], u[1], u[2], u[3]);
+                o1 = e4m3x4_sr(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv,
+                               u[4], u[5], u[6], u[7]);
+            } else {
+                o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
+                o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
+            }
+            o0 = fix_codes_if<FIX>(o0, inv, bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv,
+                                   bf16_hi(w[1]) * inv);
+            o1 = fix_codes_if<FIX>(o1, inv, bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv,
+                                   bf16_hi(w[3]) * inv);
+            if (full || (cok && r < R)) st8(qrow + 16 * it * ldq, make_uint2(o0, o1));
+        }
+    };
+    // finite nonzero multipliers (the common case): no product is NaN, no fix-up
+    if (plain) emit(std::false_type{});
+    else emit(std::true_type{});
     if (lane16 < kQ1Per) {     // the block's segment j exists (grid = ceil(C/128)): only rows can be past the end
         const int64_t r = rb + grp + 16 * lane16;
         if (r < R) s[j * lds + r] = PO2 ? e8m0_to_f32(eb_own) : sc_own;
@@ -270,16 +285,28 @@ __global__ __launch_bounds__(256) void k_tile128(
         uint32_t er_own = 0;
         scale_of(a_own, sr_own, er_own, iv_own);
         const int lane = t & 63;
+        float ivs[8];
+        bool plain = true;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float iv = __shfl(iv_own, (lane & 48) | i, 64);
-            const int64_t r = r0 + rg * 8 + i;
-            const uint32_t o0 = fix_codes(e4m3x4(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv), iv,
-                                          V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
-            const uint32_t o1 = fix_codes(e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv), iv,
-                                          V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
-            if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
+            ivs[i] = __shfl(iv_own, (lane & 48) | i, 64);
+            plain = plain && plain_mul(ivs[i]);
         }
+        auto emit = [&](auto fix) __attribute__((always_inline)) {
+            constexpr bool FIX = decltype(fix)::value;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float iv = ivs[i];
+                const int64_t r = r0 + rg * 8 + i;
+                const uint32_t o0 = fix_codes_if<FIX>(e4m3x4(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv),
+                                                      iv, V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
+                const uint32_t o1 = fix_codes_if<FIX>(e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv),
+                                                      iv, V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
+                if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
+            }
+        };
+        if (plain) emit(std::false_type{});
+        else emit(std::true_type{});
         // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
         const int64_t rr = r0 + rg * 8 + cg;
         if (cg < 8 && rr < R) put_scale(s_row, (int64_t)blockIdx.y * lds_row + rr, sr_own, er_own);
@@ -415,17 +442,22 @@ __global__ __launch_bounds__(256) void k_tile128(
     // Row-major codes (128x128 weights, q != nullptr): 8 bytes per patch row.
     if constexpr (TILE) {
         if (q != nullptr) {
+            auto emit = [&](auto fix) __attribute__((always_inline)) {
+                constexpr bool FIX = decltype(fix)::value;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int64_t r = r0 + rg * 8 + i;
-                const uint32_t o0 = fix_codes(
-                    e4m3x4(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]), inv[0],
-                    V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]);
-                const uint32_t o1 = fix_codes(
-                    e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]), inv[4],
-                    V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
-                if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
-            }
+                for (int i = 0; i < 8; ++i) {
+                    const int64_t r = r0 + rg * 8 + i;
+                    const uint32_t o0 = fix_codes_if<FIX>(
+                        e4m3x4(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]), inv[0],
+                        V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]);
+                    const uint32_t o1 = fix_codes_if<FIX>(
+                        e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]), inv[4],
+                        V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
+                    if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
+                }
+            };
+            if (plain_mul(inv[0])) emit(std::false_type{});          // one multiplier for the whole tile
+            else emit(std::true_type{});
         }
         if (qT == nullptr) return;
     }
@@ -434,16 +466,26 @@ __global__ __launch_bounds__(256) void k_tile128(
     // rows past R are the zero padding (a NaN tile's codes must not reach it).
     const int nv = (int)(R - (r0 + rg * 8) < 8 ? (R - (r0 + rg * 8) < 0 ? 0 : R - (r0 + rg * 8)) : 8);
     const uint32_t vlo = rows_mask_lo(nv), vhi = rows_mask_hi(nv);
+    auto emit_t = [&](auto fix) __attribute__((always_inline)) {
+        constexpr bool FIX = decltype(fix)::value;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t lo = fix_codes(e4m3x4(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]),
-                                      inv[k], V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k])
-                            & vlo;
-        const uint32_t hi = fix_codes(e4m3x4(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]),
-                                      inv[k], V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k])
-                            & vhi;
-        *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
-    }
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t lo = fix_codes_if<FIX>(
+                                    e4m3x4(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]),
+                                    inv[k], V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k])
+                                & vlo;
+            const uint32_t hi = fix_codes_if<FIX>(
+                                    e4m3x4(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]),
+                                    inv[k], V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k])
+                                & vhi;
+            *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
+        }
+    };
+    bool plain = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) plain = plain && plain_mul(inv[k]);
+    if (plain) emit_t(std::false_type{});
+    else emit_t(std::true_type{});
     __syncthreads();
     // 128 staged rows of 128 bytes; 8 threads per row, 16 bytes each, 4 passes.
     uint8_t* const pq = qT + (c0 + (t >> 3)) * ldqT + r0 + (t & 7) * 16;
