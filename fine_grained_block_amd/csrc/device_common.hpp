@@ -49,6 +49,24 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
 }
 
+// The same without the clamp, for values known to be finite with |v| at most
+// 448 up to the rounding of a cast multiplier (x * fl32(448/a) for |x| <= a).
+// The converter rounds to nearest even within the format and gives the NaN
+// code only past 464, the midpoint above 448 (measured on gfx950 for every
+// fp32 value in [440, 500) and its negation: all equal the saturating
+// conversion up to 464).
+__device__ __forceinline__ uint32_t e4m3x4_inrange(float a, float b, float c, float d) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+// FIX: the general cast (clamp, then the fix-ups of fix_codes by the caller);
+// otherwise the in-range cast for finite nonzero multipliers.
+template <bool FIX>
+__device__ __forceinline__ uint32_t e4m3x4_t(float a, float b, float c, float d) {
+    if constexpr (FIX) return e4m3x4(a, b, c, d);
+    else return e4m3x4_inrange(a, b, c, d);
+}
+
 // Codes in byte 0,1 (HI = false) or byte 2,3 (HI = true) of w -> two fp32 values (exact).
 template <bool HI>
 __device__ __forceinline__ float2 e4m3x2_decode(uint32_t w) {
@@ -102,6 +120,14 @@ __device__ __forceinline__ uint32_t fix_codes(uint32_t codes, float mul, float p
 // common case, where no product can be NaN).  Callers test it once for all the
 // multipliers a thread uses and branch to a path without fix_codes.
 __device__ __forceinline__ bool plain_mul(float m) { return m == m && m != 0.0f; }
+// For power-of-two scales the multiplier 2^-e stays finite and nonzero even for
+// an infinite tile (e clamps at 127, reached only by an infinite absmax): such
+// a tile's products are infinite and need the clamp, so 2^-127 is not plain.
+template <bool PO2>
+__device__ __forceinline__ bool plain_mul_t(float m) {
+    if constexpr (PO2) return plain_mul(m) && m > 0x1p-127f;
+    else return plain_mul(m);
+}
 template <bool FIX>
 __device__ __forceinline__ uint32_t fix_codes_if(uint32_t codes, float mul, float p0, float p1, float p2, float p3) {
     if constexpr (FIX) return fix_codes(codes, mul, p0, p1, p2, p3);

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
 #pragma unroll
     for (int it = 0; it < kQ1Per; ++it) {
         invs[it] = __shfl(inv_own, (lane & 48) | it, 64);
-        plain = plain && plain_mul(invs[it]);
+        plain = plain && plain_mul_t<PO2>(invs[it]);
     }
     auto emit = [&](auto fix) __attribute__((always_inline)) {
         constexpr bool FIX = decltype(fix)::value;
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
                 o1 = e4m3x4_sr(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv,
                                u[4], u[5], u[6], u[7]);
             } else {
-                o0 = e4m3x4(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
-                o1 = e4m3x4(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
+                o0 = e4m3x4_t<FIX>(bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv, bf16_hi(w[1]) * inv);
+                o1 = e4m3x4_t<FIX>(bf16_lo(w[2]) * inv, bf16_hi(w[2]) * inv, bf16_lo(w[3]) * inv, bf16_hi(w[3]) * inv);
             }
             o0 = fix_codes_if<FIX>(o0, inv, bf16_lo(w[0]) * inv, bf16_hi(w[0]) * inv, bf16_lo(w[1]) * inv,
                                    bf16_hi(w[1]) * inv);
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void k_tile128(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             ivs[i] = __shfl(iv_own, (lane & 48) | i, 64);
-            plain = plain && plain_mul(ivs[i]);
+            plain = plain && plain_mul_t<PO2>(ivs[i]);
         }
         auto emit = [&](auto fix) __attribute__((always_inline)) {
             constexpr bool FIX = decltype(fix)::value;
@@ -298,9 +298,9 @@ __global__ __launch_bounds__(256) void k_tile128(
             for (int i = 0; i < 8; ++i) {
                 const float iv = ivs[i];
                 const int64_t r = r0 + rg * 8 + i;
-                const uint32_t o0 = fix_codes_if<FIX>(e4m3x4(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv),
+                const uint32_t o0 = fix_codes_if<FIX>(e4m3x4_t<FIX>(V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv),
                                                       iv, V(i, 0) * iv, V(i, 1) * iv, V(i, 2) * iv, V(i, 3) * iv);
-                const uint32_t o1 = fix_codes_if<FIX>(e4m3x4(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv),
+                const uint32_t o1 = fix_codes_if<FIX>(e4m3x4_t<FIX>(V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv),
                                                       iv, V(i, 4) * iv, V(i, 5) * iv, V(i, 6) * iv, V(i, 7) * iv);
                 if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
             }
@@ -448,15 +448,15 @@ __global__ __launch_bounds__(256) void k_tile128(
                 for (int i = 0; i < 8; ++i) {
                     const int64_t r = r0 + rg * 8 + i;
                     const uint32_t o0 = fix_codes_if<FIX>(
-                        e4m3x4(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]), inv[0],
+                        e4m3x4_t<FIX>(V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]), inv[0],
                         V(i, 0) * inv[0], V(i, 1) * inv[1], V(i, 2) * inv[2], V(i, 3) * inv[3]);
                     const uint32_t o1 = fix_codes_if<FIX>(
-                        e4m3x4(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]), inv[4],
+                        e4m3x4_t<FIX>(V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]), inv[4],
                         V(i, 4) * inv[4], V(i, 5) * inv[5], V(i, 6) * inv[6], V(i, 7) * inv[7]);
                     if (full || (cok && r < R)) st8(q + (r0 + rg * 8) * ldq + cc + i * ldq, make_uint2(o0, o1));
                 }
             };
-            if (plain_mul(inv[0])) emit(std::false_type{});          // one multiplier for the whole tile
+            if (plain_mul_t<PO2>(inv[0])) emit(std::false_type{});          // one multiplier for the whole tile
             else emit(std::true_type{});
         }
         if (qT == nullptr) return;
@@ -471,11 +471,11 @@ __global__ __launch_bounds__(256) void k_tile128(
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const uint32_t lo = fix_codes_if<FIX>(
-                                    e4m3x4(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]),
+                                    e4m3x4_t<FIX>(V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k]),
                                     inv[k], V(0, k) * inv[k], V(1, k) * inv[k], V(2, k) * inv[k], V(3, k) * inv[k])
                                 & vlo;
             const uint32_t hi = fix_codes_if<FIX>(
-                                    e4m3x4(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]),
+                                    e4m3x4_t<FIX>(V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k]),
                                     inv[k], V(4, k) * inv[k], V(5, k) * inv[k], V(6, k) * inv[k], V(7, k) * inv[k])
                                 & vhi;
             *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kTrStride + rg * 8]) = make_uint2(lo, hi);
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256) void k_tile128(
     };
     bool plain = true;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) plain = plain && plain_mul(inv[k]);
+    for (int k = 0; k < 8; ++k) plain = plain && plain_mul_t<PO2>(inv[k]);
     if (plain) emit_t(std::false_type{});
     else emit_t(std::true_type{});
     __syncthreads();
