@@ -24,7 +24,9 @@ back (`clock_mhz`; the chip lowers it under this load), against the peak at
 that clock (`frac_at_clock`); `clock_mhz_mfma_only` is the clock under a probe
 that runs FP8 MFMAs and nothing else.
 `kernels` lists every kernel's rate against its own roofline (HBM for the
-quantizers).  `cold` is the median of 50 steps after 10 warm-ups, each after a
+quantizers).  The default line also carries `quant_stress`: the five
+quantizers alone on the stress tensor X [16384, 7168], each launch cold (the
+`--workload quant_stress` measurement condensed; `--no-quant-stress` skips it).  `cold` is the median of 50 steps after 10 warm-ups, each after a
 1 GiB read scrub outside its events, labelled as such.  `cpu_baseline` times
 the CPU oracle on a bounded, seeded sample of the same work (for ffn_dense and
 moe_grouped 1/8 of the 128x128 output tiles, first and last tiles included;
@@ -63,7 +65,9 @@ Cache.  Per kernel the median over the timed steps; `value` is the summed
 algorithmic bytes over the summed medians in GB/s, and `roofline` prices the
 slowest kernel against 8 TB/s.  `copy_reference` times a plain streaming
 kernel with the 1x128 cast's traffic (2 bytes read, 1 written per element)
-the same way, and each kernel's `frac_of_copy` compares its rate with it.
+the same way, and `copy_reference_1to1` a byte copy with the requant's (1
+read, 1 written); each kernel's `frac_of_copy` compares its rate with the
+reference of its own mix.
 `us_warm` / `GB/s_warm` are the same launches back to back without the scrub
 (warm cache), labelled as such; `value` uses the cold medians.
 
@@ -149,6 +153,9 @@ def parse():
     p.add_argument("--schedule", choices=["serial", "overlap"], default="serial",
                    help="serial (default): every kernel on one stream, in step order; "
                         "overlap: casts that no GEMM waits for run on a second stream")
+    p.add_argument("--no-quant-stress", action="store_true",
+                   help="ffn_dense: skip the quant_stress summary (the five quantizers cold on the stress "
+                        "tensor) that the line carries as `quant_stress`")
     p.add_argument("--cold-iters", type=int, default=50,
                    help="cold-cache step timings after the timed region: median of this many steps, each "
                         "after a 1 GiB scrub (0 = skip)")
@@ -421,8 +428,9 @@ def quant_stress_bytes(R, C):
     }
 
 
-def quant_stress_main(args, np, torch, fgb, wl):
-    """--workload quant_stress: each quantizer cold, median over the timed steps."""
+def quant_stress_main(args, np, torch, fgb, wl, emit=True):
+    """--workload quant_stress: each quantizer cold, median over the timed steps.
+    Prints the JSON line (emit) and returns it as a dict."""
     dev = torch.device("cuda:0")
     d = wl.quant_stress()
     R, C = d["R"], d["C"]
@@ -452,6 +460,11 @@ def quant_stress_main(args, np, torch, fgb, wl):
     ref_out = torch.empty(n_ref, dtype=torch.float32, device=dev)
     kernels.append(("copy_reference", lambda: torch.add(ref_in[:n_ref], ref_in[n_ref:], out=ref_out)))
     ab["copy_reference"] = 3 * n_ref * 4
+    # and one with the requant's traffic: 1 byte read and 1 written per element
+    ref8_in = torch.ones(R * C, dtype=torch.uint8, device=dev)
+    ref8_out = torch.empty(R * C, dtype=torch.uint8, device=dev)
+    kernels.append(("copy_reference_1to1", lambda: ref8_out.copy_(ref8_in)))
+    ab["copy_reference_1to1"] = 2 * R * C
     scrub = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
@@ -485,11 +498,16 @@ def quant_stress_main(args, np, torch, fgb, wl):
     ref_ms = med.pop("copy_reference")
     ref_b = ab.pop("copy_reference")
     ref_rate = ref_b / (ref_ms * 1e-3)
+    ref1_ms = med.pop("copy_reference_1to1")
+    ref1_b = ab.pop("copy_reference_1to1")
+    ref1_rate = ref1_b / (ref1_ms * 1e-3)
     kinfo = {}
     for n, ms in med.items():
         rate = ab[n] / (ms * 1e-3)
+        # each kernel against the copy with its own mix of reads and writes
+        rr = ref1_rate if n.startswith("requant") else ref_rate
         kinfo[n] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
-                    "frac_hbm_peak": round(rate / HBM_PEAK, 4), "frac_of_copy": round(rate / ref_rate, 3),
+                    "frac_hbm_peak": round(rate / HBM_PEAK, 4), "frac_of_copy": round(rate / rr, 3),
                     "bytes": ab[n], "us_warm": round(med_warm[n] * 1e3, 2),
                     "GB/s_warm": round(ab[n] / (med_warm[n] * 1e-3) / 1e9, 1)}
     total_ms = sum(med.values())
@@ -523,6 +541,10 @@ def quant_stress_main(args, np, torch, fgb, wl):
                            "frac_hbm_peak": round(ref_rate / HBM_PEAK, 4), "bytes": ref_b,
                            "what": "torch add of two fp32 halves into a third: reads 2 and writes 1 byte per "
                                    "byte of X's elements, cold like the casts"},
+        "copy_reference_1to1": {"us": round(ref1_ms * 1e3, 2), "GB/s": round(ref1_rate / 1e9, 1),
+                                "frac_hbm_peak": round(ref1_rate / HBM_PEAK, 4), "bytes": ref1_b,
+                                "what": "torch copy of R*C bytes: the requant's mix (1 byte read, 1 written "
+                                        "per element), cold like the casts; the requant's frac_of_copy uses it"},
     }
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -545,7 +567,23 @@ def quant_stress_main(args, np, torch, fgb, wl):
                                "kind": "oracle",
                                "sample": f"the whole workload: the five quantizers on the full tensor ({tq:.1f} s; "
                                          "the dual cast as the 1x128 and 128x1 oracle calls)"}
-    print(json.dumps(out), flush=True)
+    if emit:
+        print(json.dumps(out), flush=True)
+    return out
+
+
+def quant_stress_summary(args, np, torch, fgb, wl):
+    """The quant_stress measurement (20 cold launches of each quantizer after 5
+    warm-ups, no CPU baseline), condensed for another workload's line."""
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup, sub.no_cpu_baseline, sub.copy_calibration = 20, 5, True, False
+    q = quant_stress_main(sub, np, torch, fgb, wl, emit=False)
+    return {"what": q["config"]["workload"] + " (20 cold launches per kernel after 5 warm-ups)",
+            "GB/s": q["value"], "frac_hbm_peak": q["quant_frac_hbm_peak"],
+            "kernels": {k: {"us": v["us"], "GB/s": v["GB/s"], "frac_hbm_peak": v["frac_hbm_peak"],
+                            "frac_of_copy": v["frac_of_copy"]} for k, v in q["kernels"].items()},
+            "copy_reference_frac_hbm_peak": q["copy_reference"]["frac_hbm_peak"],
+            "copy_reference_1to1_frac_hbm_peak": q["copy_reference_1to1"]["frac_hbm_peak"]}
 
 
 def make_runner(torch, dev, kernels, overlap):
@@ -842,6 +880,9 @@ def main():
     if cold is not None:
         cold["TFLOP/s"] = round(step_flop / (cold["ms_per_step"] * 1e-3) / 1e12, 1)
         out["cold"] = cold
+    if args.workload == "ffn_dense" and not args.no_quant_stress:
+        # the quantizers' HBM row on the stress tensor, so that this line carries it too
+        out["quant_stress"] = quant_stress_summary(args, np, torch, fgb, wl)
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
