@@ -161,8 +161,11 @@ __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_fl
 // E4M3 code -> its value (exact).
 __device__ __forceinline__ float e4m3_decode1(uint8_t code) { return e4m3x2_decode<false>((uint32_t)code).x; }
 
-// RN codes of four values times inv (the quantizers' cast).
+// RN codes of four values times inv (the quantizers' cast); a finite nonzero
+// multiplier needs neither the clamp nor the NaN fix-ups.
 __device__ __forceinline__ uint32_t codes4(const float* v, float inv) {
+    if (__builtin_expect(plain_mul(inv), 1))
+        return e4m3x4_inrange(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     return fix_codes(e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv), inv,
                      v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
 }
@@ -530,16 +533,25 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             // rows past R are the zero padding of the transposed codes
             const int nv = (int)(R - (r0 + rg * 8) < 8 ? (R - (r0 + rg * 8) < 0 ? 0 : R - (r0 + rg * 8)) : 8);
             const uint32_t vlo = rows_mask_lo(nv), vhi = rows_mask_hi(nv);
+            auto emit = [&](auto fix) __attribute__((always_inline)) {
+                constexpr bool FIX = decltype(fix)::value;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t lo = fix_codes(
-                    e4m3x4(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]), inv[k],
-                    v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]) & vlo;
-                const uint32_t hi = fix_codes(
-                    e4m3x4(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]), inv[k],
-                    v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]) & vhi;
-                *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
-            }
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t lo = fix_codes_if<FIX>(
+                        e4m3x4_t<FIX>(v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]),
+                        inv[k], v[0][k] * inv[k], v[1][k] * inv[k], v[2][k] * inv[k], v[3][k] * inv[k]) & vlo;
+                    const uint32_t hi = fix_codes_if<FIX>(
+                        e4m3x4_t<FIX>(v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]),
+                        inv[k], v[4][k] * inv[k], v[5][k] * inv[k], v[6][k] * inv[k], v[7][k] * inv[k]) & vhi;
+                    *reinterpret_cast<uint2*>(&tr[(cg * 8 + k) * kSwTr + rg * 8]) = make_uint2(lo, hi);
+                }
+            };
+            // one test for all eight column multipliers: finite nonzero ones need no fix-ups
+            bool plain = true;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) plain = plain && plain_mul(inv[k]);
+            if (plain) emit(std::false_type{});
+            else emit(std::true_type{});
         }
         __syncthreads();
 #pragma unroll
