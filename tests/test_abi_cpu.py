@@ -271,3 +271,28 @@ def test_quantize_128x128_batched_validation():
     assert qb(s=P(0)) == E_NULL
     assert qb(w=MIS) == E_ALIGN
     assert qb(E=0) == OK and qb(K=0) == OK
+
+
+def test_probe_library_exports_and_argument_errors():
+    """libfgb_probe.so (the benchmark's clock probe, include/fgb_probe.h): every
+    declared function is exported, and bad arguments return -1 before any HIP call."""
+    path = os.path.join(ROOT, "fine_grained_block_amd", "libfgb_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libfgb_probe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fgb_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fgb_\w+)\s*\(", text)))
+    assert names == ["fgb_probe_clock", "fgb_probe_clock_begin", "fgb_probe_clock_end"]
+    L = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(L, n), n
+    L.fgb_probe_clock.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), P]
+    L.fgb_probe_clock_begin.argtypes = [ctypes.c_int, ctypes.c_double, P]
+    L.fgb_probe_clock_end.argtypes = [ctypes.POINTER(ctypes.c_double), P]
+    mhz = ctypes.c_double(0.0)
+    assert L.fgb_probe_clock(0, ctypes.byref(mhz), None) == -1
+    assert L.fgb_probe_clock(10, None, None) == -1
+    assert L.fgb_probe_clock_begin(0, 100.0, None) == -1
+    assert L.fgb_probe_clock_begin(4097, 100.0, None) == -1
+    assert L.fgb_probe_clock_begin(8, 0.0, None) == -1
+    assert L.fgb_probe_clock_begin(8, 2e6, None) == -1
+    assert L.fgb_probe_clock_end(ctypes.byref(mhz), None) == -1      # no sample running
