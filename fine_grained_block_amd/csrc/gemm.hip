@@ -729,16 +729,17 @@ static int device_cus()
 }
 
 // Pick the tile width: each block takes about TN units of time, and the blocks
-// run in rounds of (number of CUs) -- one block per CU.  With per-weight-tile
-// scales (Fprop/Dgrad) a 224-wide tile also costs about 5% more per unit: its
-// wave columns can straddle two weight tiles, so the fold forms one scale
-// product per MFMA instead of one per row piece.
-static int pick_tn(int64_t M, int64_t N, bool outer)
+// run in rounds of (number of CUs) -- one block per CU.  A 224-wide tile also
+// costs 3-5% more per unit of work: with per-weight-tile scales (Fprop/Dgrad)
+// its wave columns can straddle two weight tiles, so the fold forms one scale
+// product per MFMA instead of one per row piece; Wgrad forms its outer-product
+// scales with 7 extra fp32 MFMAs per 28.  It is priced 5% higher.
+static int pick_tn(int64_t M, int64_t N)
 {
     const int64_t cus = device_cus();
     const int64_t tm = (M + kTM - 1) / kTM;
     auto cost = [&](int64_t tn_w) { return ((tm * ((N + tn_w - 1) / tn_w) + cus - 1) / cus) * tn_w; };
-    if (N % 224 == 0 && (outer ? 20 : 21) * cost(224) < 20 * cost(256)) return 224;
+    if (N % 224 == 0 && 21 * cost(224) < 20 * cost(256)) return 224;
     return 256;
 }
 
@@ -812,7 +813,7 @@ bool gemm_supported(const GemmArgs& a, bool grouped)
 static hipError_t launch_one(GemmKind kind, bool grouped, bool po2, const GemmArgs& a, hipStream_t stream)
 {
     const int64_t units = grouped && kind == kWgrad ? a.M * a.E : a.M;
-    const bool w224 = pick_tn(units, a.N, kind == kWgrad) == 224;
+    const bool w224 = pick_tn(units, a.N) == 224;
     if (po2) {
         if (w224) launch_v1<224, true>(kind, grouped, a, stream);
         else launch_v1<256, true>(kind, grouped, a, stream);
