@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     // wave takes the higher priority for the first half of its steps and drops
     // back for the second, so the one that is ahead yields.  (Not for Wgrad's
     // matrix-core outer products, where it measured no gain.)
-    constexpr bool kBalance = !(OUTER && TN == 224 && !PO2);
+    constexpr bool kBalance = !(OUTER && !PO2);
     auto balance_priority = [&](auto tc) __attribute__((always_inline)) {
         constexpr int t = decltype(tc)::value;
         if constexpr (kBalance && t == 0) __builtin_amdgcn_s_setprio(1);
@@ -452,23 +452,20 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             const float4 t = *reinterpret_cast<const float4*>(sSA + wm * WTM + 64 * h + frow * 4);
             sa[4 * h] = t.x; sa[4 * h + 1] = t.y; sa[4 * h + 2] = t.z; sa[4 * h + 3] = t.w;
         }
-        // column scales of piece j: 4 per lane (Wgrad) or the piece's weight tile
-        auto col_scales = [&](int j, float (&c)[4]) {
-            if constexpr (OUTER) {
-                const float4 t = *reinterpret_cast<const float4*>(sSB + wn * WTN + j * 16 + fg * 4);
-                c[0] = t.x; c[1] = t.y; c[2] = t.z; c[3] = t.w;
-            } else {
-                c[0] = sSB[wn * SBW + j];
-            }
-        };
+        // Fprop/Dgrad: the weight-tile scale of column piece j
+        auto col_scales = [&](int j, float (&c)[4]) { c[0] = sSB[wn * SBW + j]; };
         // TN = 256, weight-tile scales: a wave's 64 columns start 64-aligned and
         // lie inside one 128-wide weight tile, so every piece of the block folds
         // with f[i] = SA(row piece i) * SB(the wave's tile): MI products per block
         // instead of one per piece
         constexpr bool ONE_TILE = !OUTER && TN == 256;
         static_assert(!ONE_TILE || (WTN == 64 && ROW_MAJOR), "one weight tile per wave");
-        float cs[ROW_MAJOR && !ONE_TILE ? NJ : 1][4];
-        if constexpr (ROW_MAJOR && !ONE_TILE) {
+        // Wgrad forms its outer-product scales on the matrix core (below): one
+        // fp32 MFMA per four pieces costs less than the 4 vector multiplies per
+        // piece it replaces
+        constexpr bool MS = OUTER;
+        float cs[ROW_MAJOR && !ONE_TILE && !MS ? NJ : 1][4];
+        if constexpr (ROW_MAJOR && !ONE_TILE && !MS) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) col_scales(j, cs[j]);
         }
@@ -477,9 +474,6 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
 #pragma unroll
             for (int i = 0; i < MI; ++i) sa[i] *= sbw;
         }
-        // Wgrad at 224-wide tiles forms its outer-product scales on the matrix core
-        // (below); 256-wide Wgrad tiles have no registers to spare for it
-        constexpr bool MS = OUTER && TN == 224;
         // column-major walk: the scales of column piece p live in cbuf[p & 1]
         // (not for matrix-core scales)
         float cbuf[2][4];
@@ -492,19 +486,24 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         // PER pieces of one streamed fragment (a row piece for the row-major
         // walk, block b = column piece b; a column piece for the column-major
         // walk, block b = row piece b), so A_b carries the column scales and B_b
-        // the row scales.  The products of group g are formed at the last step
-        // of group g-1 into S[g & 1]; a group's last fold comes kLag < PER steps
-        // after its last MFMA, before group g+2 overwrites the slot.
+        // the row scales.  Two slots (224-wide tiles): the products of group g
+        // are formed at the last step of group g-1 into S[g & 1]; a group's last
+        // fold comes kLag < PER steps after its last MFMA, before group g+2
+        // overwrites the slot.  One slot (256-wide tiles, whose 128 accumulators
+        // leave no room for a second): group g's products are formed at step
+        // PER*g + kLag - 1, right after the fold of group g-1's last piece, and
+        // its first fold follows one step later.
         typedef float v16f __attribute__((ext_vector_type(16)));
-        v16f S[MS ? 2 : 1];
+        constexpr int NSLOT = TN == 224 ? 2 : 1;
+        v16f S[MS ? NSLOT : 1];
         float ocol = 0.0f, orow = 0.0f, ocol_next = 0.0f;
         auto outer_products = [&](int g) __attribute__((always_inline)) {
             if constexpr (MS) {
                 const v16f z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 if constexpr (ROW_MAJOR)      // row piece g: columns of the wave (one per lane), row 16g + frow
-                    S[g & 1] = __builtin_amdgcn_mfma_f32_16x16x1f32(ocol, sa[g], z, 0, 0, 0);
+                    S[g % NSLOT] = __builtin_amdgcn_mfma_f32_16x16x1f32(ocol, sa[g], z, 0, 0, 0);
                 else                          // column piece g: its columns 16g + frow, rows 16b + frow
-                    S[g & 1] = __builtin_amdgcn_mfma_f32_16x16x1f32(ocol, orow, z, 0, 0, 0);
+                    S[g % NSLOT] = __builtin_amdgcn_mfma_f32_16x16x1f32(ocol, orow, z, 0, 0, 0);
             }
         };
         if constexpr (MS) {
@@ -527,11 +526,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
                 const int g = t / PER, h = t % PER;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], S[g & 1][4 * h + r], acc[i][j][r]);
-            } else if constexpr (OUTER) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i] * c[r], acc[i][j][r]);
+                    acc[i][j][r] = __builtin_fmaf(P[t & 3][r], S[g % NSLOT][4 * h + r], acc[i][j][r]);
             } else if constexpr (ONE_TILE) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[t & 3][r], sa[i], acc[i][j][r]);
@@ -558,7 +553,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             // piece q-1's last fold runs at step q*PER + kLag - 1, so its scale
             // slot is free from step q*PER + kLag on: load piece q+1's scales there
             if constexpr (!ROW_MAJOR && !MS && h == kLag && q + 1 < NS) col_scales(q + 1, cbuf[(q + 1) & 1]);
-            if constexpr (MS && h == PER - 1 && q + 1 < NS) {
+            if constexpr (MS && NSLOT == 2 && h == PER - 1 && q + 1 < NS) {
                 if constexpr (!ROW_MAJOR) {
                     ocol = ocol_next;                                             // column piece q + 1
                     if (q + 2 < NS) ocol_next = sSB[wn * WTN + 16 * (q + 2) + frow];
@@ -569,6 +564,7 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
                 ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], sf[q % 3], zero, 0, 0, 0, 0, 0, 0)
                 : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sf[q % 3], hf[h], zero, 0, 0, 0, 0, 0, 0);
             if constexpr (t >= kLag) fold(t - kLag, scales_of_step(t - kLag));
+            if constexpr (MS && NSLOT == 1 && h == kLag - 1 && q >= 1) outer_products(q);
             // keep the steps in this order: the scheduler would otherwise pull
             // each fold up behind its own MFMA and pad the wait with s_nop
             __builtin_amdgcn_sched_barrier(0);
@@ -732,8 +728,8 @@ static int device_cus()
 // run in rounds of (number of CUs) -- one block per CU.  A 224-wide tile also
 // costs 3-5% more per unit of work: with per-weight-tile scales (Fprop/Dgrad)
 // its wave columns can straddle two weight tiles, so the fold forms one scale
-// product per MFMA instead of one per row piece; Wgrad forms its outer-product
-// scales with 7 extra fp32 MFMAs per 28.  It is priced 5% higher.
+// product per MFMA instead of one per row piece; for Wgrad the difference is
+// measured, not derived.  It is priced 5% higher.
 static int pick_tn(int64_t M, int64_t N)
 {
     const int64_t cus = device_cus();
