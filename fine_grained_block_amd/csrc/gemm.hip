@@ -692,20 +692,59 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
             }
         }
         __syncthreads();                                       // the pass's rows are staged
-        for (int idx = tid; idx < PASS_ROWS * CH; idx += kV1Threads) {
-            const int r = idx / CH, c = idx % CH;
-            if (c >= nch || prow0 + r >= nrows) continue;
-            const uint4 v = *reinterpret_cast<const uint4*>(st + r * PITCH + ((c ^ (r & 15)) << 4));
-            uint8_t* o = reinterpret_cast<uint8_t*>(outp) + ((m0 + prow0 + r) * g.ldo + n0) * OB + c * 16;
-            if constexpr (!BF16_OUT) {
-                if (g.accumulate) {
-                    const float4 pv = *reinterpret_cast<const float4*>(o);
-                    const float4 a = __builtin_bit_cast(float4, v);
-                    st16(o, __builtin_bit_cast(uint4, make_float4(a.x + pv.x, a.y + pv.y, a.z + pv.z, a.w + pv.w)));
-                    continue;
+        // Stores in rounds of kU chunks per thread: a round's chunks are all read
+        // from LDS (and, when accumulating, the old outputs all loaded) before the
+        // first of them is stored, so each round waits for those latencies once.
+        // A thread keeps its chunk column c; round chunk k is RS*k rows further.
+        // Threads whose column lies past the tile's last column store nothing;
+        // whether every row of the pass exists is decided once per pass (uniform
+        // over the block), so full passes store without a per-chunk branch.
+        constexpr int RS = kV1Threads / CH;                    // rows one store of every thread covers
+        constexpr int kIt = PASS_ROWS / RS;                    // chunks per thread and pass
+        constexpr int kU = BF16_OUT ? 8 : 4;
+        static_assert(kV1Threads % CH == 0 && PASS_ROWS % RS == 0 && kIt % kU == 0, "whole store rounds");
+        const int c = tid % CH, r0 = tid / CH;
+        uint8_t* const ob = reinterpret_cast<uint8_t*>(outp) + ((m0 + prow0 + r0) * g.ldo + n0) * OB + c * 16;
+        const int64_t ostep = (int64_t)RS * g.ldo * OB;
+        auto store_rounds = [&](auto accumulate, auto all_rows) __attribute__((always_inline)) {
+            constexpr bool ACC = decltype(accumulate)::value, ALL = decltype(all_rows)::value;
+#pragma unroll
+            for (int it0 = 0; it0 < kIt; it0 += kU) {
+                uint4 v[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int r = r0 + (it0 + u) * RS;
+                    v[u] = *reinterpret_cast<const uint4*>(st + r * PITCH + ((c ^ (r & 15)) << 4));
+                }
+                auto row_ok = [&](int u) { return ALL || prow0 + r0 + (it0 + u) * RS < nrows; };
+                if constexpr (ACC) {
+                    float4 pv[kU];
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+                        if (row_ok(u)) pv[u] = *reinterpret_cast<const float4*>(ob + (it0 + u) * ostep);
+#pragma unroll
+                    for (int u = 0; u < kU; ++u) {
+                        if (!row_ok(u)) continue;
+                        const float4 x = __builtin_bit_cast(float4, v[u]);
+                        st16(ob + (it0 + u) * ostep, __builtin_bit_cast(uint4, make_float4(x.x + pv[u].x, x.y + pv[u].y,
+                                                                                          x.z + pv[u].z, x.w + pv[u].w)));
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kU; ++u)
+                        if (row_ok(u)) st16(ob + (it0 + u) * ostep, v[u]);
                 }
             }
-            st16(o, v);
+        };
+        if (c < nch) {
+            const bool all_rows = prow0 + PASS_ROWS <= nrows;
+            if (!BF16_OUT && g.accumulate) {
+                if (all_rows) store_rounds(std::true_type{}, std::true_type{});
+                else store_rounds(std::true_type{}, std::false_type{});
+            } else {
+                if (all_rows) store_rounds(std::false_type{}, std::true_type{});
+                else store_rounds(std::false_type{}, std::false_type{});
+            }
         }
     }
 }
