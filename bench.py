@@ -14,7 +14,8 @@ up projection's Dgrad contract over 18432 = 144 blocks.
 `--workload linear_dsv3_attn` runs the same step once at the DeepSeek-V3
 attention-projection shape X [4096, 7168], W [7168, 7168], dY [4096, 7168].
 
-Prints one JSON line.  `value` is the step's GEMM throughput (GEMM FLOP over
+Prints one JSON line (and keeps a copy as results/<workload>[_ue8m0][_sr].json;
+`--results DIR` moves it, `--results ''` drops it).  `value` is the step's GEMM throughput (GEMM FLOP over
 the whole step time, quantization included) in TFLOP/s.  Per-kernel durations
 come from HIP events recorded around every launch on the stream the kernels
 run on, over the timed steps (warm: the steps run back to back); `roofline`
@@ -164,7 +165,21 @@ def parse():
                         "computes (seeded; first and last tiles included)")
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="Fprop/Dgrad output rows in the CPU-baseline sample (0 = auto, ~15 s of GEMM work)")
+    p.add_argument("--results", default="results",
+                   help="directory that receives the printed JSON line as <workload>[_ue8m0][_sr].json "
+                        "(empty: write nothing)")
     return p.parse_args()
+
+
+def emit(args, out):
+    """Print the JSON line and keep a copy under --results, named for the workload and recipe."""
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.results:
+        name = args.workload + ("_ue8m0" if args.recipe == "ue8m0" else "") + ("_sr" if args.rounding == "sr" else "")
+        os.makedirs(args.results, exist_ok=True)
+        with open(os.path.join(args.results, name + ".json"), "w") as f:
+            f.write(line + "\n")
 
 
 def algorithmic_bytes(M, K, N):
@@ -428,7 +443,7 @@ def quant_stress_bytes(R, C):
     }
 
 
-def quant_stress_main(args, np, torch, fgb, wl, emit=True):
+def quant_stress_main(args, np, torch, fgb, wl, emit_line=True):
     """--workload quant_stress: each quantizer cold, median over the timed steps.
     Prints the JSON line (emit) and returns it as a dict."""
     dev = torch.device("cuda:0")
@@ -567,8 +582,8 @@ def quant_stress_main(args, np, torch, fgb, wl, emit=True):
                                "kind": "oracle",
                                "sample": f"the whole workload: the five quantizers on the full tensor ({tq:.1f} s; "
                                          "the dual cast as the 1x128 and 128x1 oracle calls)"}
-    if emit:
-        print(json.dumps(out), flush=True)
+    if emit_line:
+        emit(args, out)
     return out
 
 
@@ -577,7 +592,7 @@ def quant_stress_summary(args, np, torch, fgb, wl):
     warm-ups, no CPU baseline), condensed for another workload's line."""
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.no_cpu_baseline, sub.copy_calibration = 20, 5, True, False
-    q = quant_stress_main(sub, np, torch, fgb, wl, emit=False)
+    q = quant_stress_main(sub, np, torch, fgb, wl, emit_line=False)
     return {"what": q["config"]["workload"] + " (20 cold launches per kernel after 5 warm-ups)",
             "GB/s": q["value"], "frac_hbm_peak": q["quant_frac_hbm_peak"],
             "kernels": {k: {"us": v["us"], "GB/s": v["GB/s"], "frac_hbm_peak": v["frac_hbm_peak"],
@@ -900,7 +915,7 @@ def main():
             out["cpu_baseline"] = cpu_baseline_tiles_linear(list(inp), args.cpu_tile_frac)
         else:
             out["cpu_baseline"] = cpu_baseline_tiles_moe(inp, args.cpu_tile_frac)
-    print(json.dumps(out), flush=True)
+    emit(args, out)
 
 
 def tile_sample(n, frac, g):

@@ -72,3 +72,21 @@ def test_tile_sample_covers_edges_and_fraction():
         assert np.all(np.diff(idx) > 0) and idx[-1] < n
         for t in tiles:
             assert np.sum(idx // 128 == t) == min(128, n - 128 * t)
+
+
+def test_emit_writes_the_printed_line(tmp_path, capsys):
+    """bench.emit prints the JSON line and keeps the same line as
+    <workload>[_ue8m0][_sr].json under --results (nothing when it is empty)."""
+    import argparse, json
+    out = {"metric": "m", "value": 1.5}
+    for recipe, rounding, name in (("fp32", "rn", "ffn_dense"), ("ue8m0", "rn", "ffn_dense_ue8m0"),
+                                   ("fp32", "sr", "ffn_dense_sr")):
+        args = argparse.Namespace(workload="ffn_dense", recipe=recipe, rounding=rounding, results=str(tmp_path))
+        bench.emit(args, out)
+        printed = capsys.readouterr().out.strip()
+        assert json.loads(printed) == out
+        assert (tmp_path / f"{name}.json").read_text().strip() == printed
+    args = argparse.Namespace(workload="quant_stress", recipe="fp32", rounding="rn", results="")
+    bench.emit(args, out)
+    assert json.loads(capsys.readouterr().out) == out
+    assert not (tmp_path / "quant_stress.json").exists()
