@@ -293,5 +293,13 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
 __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+// Non-temporal 16-byte store, for a large output that no later part of the
+// same kernel reads: its lines are not kept in L2 / the MALL, where they would
+// evict the operand lines that the kernel's remaining tiles re-read.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_stream(void* p, uint4 v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
 
 }  // namespace fgb

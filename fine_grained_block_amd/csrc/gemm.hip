@@ -699,7 +699,11 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         // Threads whose column lies past the tile's last column store nothing;
         // whether every row of the pass exists is decided once per pass (uniform
         // over the block), so full passes store without a per-chunk branch.
-        constexpr int RS = kV1Threads / CH;                    // rows one store of every thread covers
+        // The stores are non-temporal: the output (hundreds of MB at these
+        // shapes) is written once and never read back by this kernel, and kept
+        // in L2 and the MALL it would displace the operand panels that the
+        // later tiles re-read (dense FFN GEMMs 1-7% faster, grouped 1-5%).
+        constexpr int RS = kV1Threads / CH;                  // rows one store of every thread covers
         constexpr int kIt = PASS_ROWS / RS;                    // chunks per thread and pass
         constexpr int kU = BF16_OUT ? 8 : 4;
         static_assert(kV1Threads % CH == 0 && PASS_ROWS % RS == 0 && kIt % kU == 0, "whole store rounds");
@@ -726,13 +730,13 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
                     for (int u = 0; u < kU; ++u) {
                         if (!row_ok(u)) continue;
                         const float4 x = __builtin_bit_cast(float4, v[u]);
-                        st16(ob + (it0 + u) * ostep, __builtin_bit_cast(uint4, make_float4(x.x + pv[u].x, x.y + pv[u].y,
+                        st16_stream(ob + (it0 + u) * ostep, __builtin_bit_cast(uint4, make_float4(x.x + pv[u].x, x.y + pv[u].y,
                                                                                           x.z + pv[u].z, x.w + pv[u].w)));
                     }
                 } else {
 #pragma unroll
                     for (int u = 0; u < kU; ++u)
-                        if (row_ok(u)) st16(ob + (it0 + u) * ostep, v[u]);
+                        if (row_ok(u)) st16_stream(ob + (it0 + u) * ostep, v[u]);
                 }
             }
         };
