@@ -38,8 +38,9 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     static_assert(!(PO2 && SR), "stochastic rounding uses absmax/448 scales");
     const int lane16 = threadIdx.x & 15;
     const int grp = threadIdx.x >> 4;
-    const int64_t rb = (int64_t)blockIdx.x * kQ1Rows;
-    const int64_t j = blockIdx.y;
+    const BlockRC bl = block_rc<true>((R + kQ1Rows - 1) / kQ1Rows, (C + kTile - 1) / kTile);
+    const int64_t rb = bl.r * kQ1Rows;
+    const int64_t j = bl.c;
     const int64_t c = j * kTile + lane16 * 8;
     const bool cok = c < C;
     // all kQ1Rows rows and the whole 128-column block inside the tensor
@@ -132,7 +133,8 @@ hipError_t launch_quantize_1x128(const uint16_t* x, int64_t R, int64_t C, int64_
                                  float* s, int64_t lds, bool po2, hipStream_t stream, const SrParams* sr)
 {
     if (po2 && sr) return hipErrorInvalidValue;
-    dim3 grid((unsigned)((R + kQ1Rows - 1) / kQ1Rows), (unsigned)((C + kTile - 1) / kTile));
+    const dim3 grid(grid_rc((R + kQ1Rows - 1) / kQ1Rows, (C + kTile - 1) / kTile));
+    if (grid.x == 0) return hipErrorInvalidValue;
     const SrArgs a = sr_args(sr);
     if (po2)
         hipLaunchKernelGGL((k_quantize_1x128<true, false>), grid, dim3(256), 0, stream,
@@ -198,8 +200,10 @@ __global__ __launch_bounds__(256) void k_tile128(
 
     const int t = threadIdx.x;
     const int cg = t & 15, rg = t >> 4, wave = t >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * kTile;
-    const int64_t c0 = (int64_t)blockIdx.y * kTile;
+    constexpr bool kColsFast = MODE == kTile128x128 || MODE == kTileDual || MODE == kTileRequant128x128;
+    const BlockRC bl = block_rc<kColsFast>((R + kTile - 1) / kTile, (C + kTile - 1) / kTile);
+    const int64_t r0 = bl.r * kTile;
+    const int64_t c0 = bl.c * kTile;
     const int64_t cc = c0 + cg * 8;
     const bool cok = cc < C;
     // the whole 128x128 tile lies inside the tensor (block-uniform): then no
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         }
         float sr[8];
         if constexpr (MODE == kTileRequant) {
-            if (t < kTile) col_mul[t] = r0 + t < R ? s_in[(int64_t)blockIdx.y * lds_in + r0 + t] : 0.0f;
+            if (t < kTile) col_mul[t] = r0 + t < R ? s_in[bl.c * lds_in + r0 + t] : 0.0f;
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < 8; ++i) sr[i] = col_mul[rg * 8 + i];
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(256) void k_tile128(
             // barrier that publishes the column maxima, which every thread
             // reaches after these reads)
         } else {
-            const float st = s_in[(int64_t)blockIdx.x * lds_in + blockIdx.y];
+            const float st = s_in[bl.r * lds_in + bl.c];
 #pragma unroll
             for (int i = 0; i < 8; ++i) sr[i] = st;
         }
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         else emit(std::true_type{});
         // lanes cg = 0..7 of each row group write the scales of rows rg*8 + cg
         const int64_t rr = r0 + rg * 8 + cg;
-        if (cg < 8 && rr < R) put_scale(s_row, (int64_t)blockIdx.y * lds_row + rr, sr_own, er_own);
+        if (cg < 8 && rr < R) put_scale(s_row, bl.c * lds_row + rr, sr_own, er_own);
     }
 
     float inv[8];
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         scale_of(a, sc, eb, iv);
 #pragma unroll
         for (int k = 0; k < 8; ++k) inv[k] = iv;
-        if (t == 0) put_scale(s_out, (int64_t)blockIdx.x * lds_out + blockIdx.y, sc, eb);
+        if (t == 0) put_scale(s_out, bl.r * lds_out + bl.c, sc, eb);
     } else {
         uint32_t mc[8];
 #pragma unroll
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(256) void k_tile128(
             uint32_t eb = 0;
             scale_of(a, sc, eb, iv);
             col_mul[t] = iv;
-            if (c0 + t < C) put_scale(s_out, (int64_t)blockIdx.x * lds_out + c0 + t, sc, eb);
+            if (c0 + t < C) put_scale(s_out, bl.r * lds_out + c0 + t, sc, eb);
         }
         __syncthreads();
 #pragma unroll
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void k_tile128(
         }
         if constexpr (MODE == kTileDual) {
             const int64_t rr = r0 + rg * 8 + cg;
-            if (cg < 8 && rr < R) s_row[(int64_t)blockIdx.y * lds_row + rr] = sr_own;
+            if (cg < 8 && rr < R) s_row[bl.c * lds_row + rr] = sr_own;
         }
         if constexpr (TILE) {
             if (qT == nullptr) return;
@@ -540,7 +544,8 @@ hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, i
 {
     if (sr && (po2 || mode == kTileRequant || mode == kTileRequant128x128)) return hipErrorInvalidValue;
     if (batch < 1 || batch > 65535) return hipErrorInvalidValue;
-    dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile), (unsigned)batch);
+    const dim3 grid(grid_rc((R + kTile - 1) / kTile, (C + kTile - 1) / kTile), 1, (unsigned)batch);
+    if (grid.x == 0) return hipErrorInvalidValue;
     const SrArgs a = sr_args(sr);
     if (po2)
         launch_tile128_t<true, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,

@@ -187,11 +187,12 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
 {
     const int lane16 = threadIdx.x & 15;
     const int grp = threadIdx.x >> 4;
-    const int64_t b = blockIdx.y;
-    const int64_t c = b * kTile + lane16 * 8;          // column in H and G; U at F + c
     const int64_t nb = F / kTile;
+    const BlockRC bl = block_rc<true>((R + kSwRows - 1) / kSwRows, nb);
+    const int64_t b = bl.c;
+    const int64_t c = b * kTile + lane16 * 8;          // column in H and G; U at F + c
     for (int it = 0; it < 4; ++it) {
-        const int64_t r = (int64_t)blockIdx.x * kSwRows + grp + 16 * it;
+        const int64_t r = bl.r * kSwRows + grp + 16 * it;
         const bool ok = r < R;
         // [G | U] is read once: non-temporal loads (see ld16_stream)
         const uint4 wg = ok ? ld16_stream(gu + r * ldgu + c) : make_uint4(0u, 0u, 0u, 0u);
@@ -302,9 +303,10 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
 
     const int t = threadIdx.x;
     const int cg = t & 15, rg = t >> 4, wave = t >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * kTile;
-    const int64_t j = blockIdx.y;
     const int64_t nb = F / kTile;
+    const BlockRC bl = block_rc<true>((R + kTile - 1) / kTile, nb);
+    const int64_t r0 = bl.r * kTile;
+    const int64_t j = bl.c;
     const int64_t cc = j * kTile + cg * 8;             // gate column; up column F + cc
 
     // phase 1: G~ = bf16(fl32(dec(q) s)), U~ likewise, dH; both tiles' values
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
             float sc, iv;
             tile_scale(floored_absmax(m, amax_floor), sc, iv);
             col_mul[t] = iv;
-            sT[(int64_t)blockIdx.x * ldsT + oc0 + t] = sc;
+            sT[bl.r * ldsT + oc0 + t] = sc;
         }
         __syncthreads();                                   // col_mul written
         float inv[8];
@@ -571,7 +573,8 @@ hipError_t launch_swiglu_fwd(const uint16_t* gu, int64_t R, int64_t F, int64_t l
                              uint8_t* q_h, int64_t ldq_h, float* s_h, int64_t lds_h,
                              uint16_t* h, int64_t ldh, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((R + kSwRows - 1) / kSwRows), (unsigned)(F / kTile));
+    const dim3 grid(grid_rc((R + kSwRows - 1) / kSwRows, F / kTile));
+    if (grid.x == 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_swiglu_fwd, grid, dim3(256), 0, stream, gu, R, F, ldgu, amax_floor,
                        q_gu, ldq_gu, s_gu, lds_gu, q_h, ldq_h, s_h, lds_h, h, ldh);
     return hipGetLastError();
@@ -583,7 +586,8 @@ hipError_t launch_swiglu_bwd(const uint8_t* q_gu, int64_t R, int64_t F, int64_t 
                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                              uint16_t* dgu, int64_t lddgu, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((R + kTile - 1) / kTile), (unsigned)(F / kTile));
+    const dim3 grid(grid_rc((R + kTile - 1) / kTile, F / kTile));
+    if (grid.x == 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_swiglu_bwd, grid, dim3(256), 0, stream, q_gu, R, F, ldq_gu, s_gu, lds_gu,
                        dh, lddh, amax_floor, q, ldq, s, lds, qT, ldqT, sT, ldsT, dgu, lddgu);
     return hipGetLastError();
