@@ -23,7 +23,11 @@ prices the dominant kernel against MI355X's dense FP8 MFMA peak (5.0 PFLOP/s
 at 2.4 GHz) and, with the shader clock measured while that kernel runs back to
 back (`clock_mhz`; the chip lowers it under this load), against the peak at
 that clock (`frac_at_clock`); `clock_mhz_mfma_only` is the clock under a probe
-that runs FP8 MFMAs and nothing else.
+that runs FP8 MFMAs and nothing else, and `staging_probe` the cycles that the
+GEMM's per-block staging traffic (fragment reads, direct-to-LDS operand loads,
+both) takes on one compute unit beside the 2048 its MFMAs need.
+`--blas-reference` adds, per GEMM, hipBLASLt's plain FP8 GEMM (one tensor-wide
+scale, no per-block rescale) on the same operands.
 `kernels` lists every kernel's rate against its own roofline (HBM for the
 quantizers).  The default line also carries `quant_stress`: the five
 quantizers alone on the stress tensor X [16384, 7168], each launch cold (the
@@ -154,6 +158,10 @@ def parse():
     p.add_argument("--schedule", choices=["serial", "overlap"], default="serial",
                    help="serial (default): every kernel on one stream, in step order; "
                         "overlap: casts that no GEMM waits for run on a second stream")
+    p.add_argument("--blas-reference", action="store_true",
+                   help="ffn_dense, linear_dsv3_attn: also time hipBLASLt's plain FP8 GEMM (torch._scaled_mm, "
+                        "one tensor-wide scale, no per-block rescale) on each step GEMM's operands; reported per "
+                        "GEMM as `hipblaslt_plain_fp8`")
     p.add_argument("--no-quant-stress", action="store_true",
                    help="ffn_dense: skip the quant_stress summary (the five quantizers cold on the stress "
                         "tensor) that the line carries as `quant_stress`")
@@ -667,7 +675,67 @@ def _probe_lib():
     L.fgb_probe_clock_begin.restype = ctypes.c_int
     L.fgb_probe_clock_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     L.fgb_probe_clock_end.restype = ctypes.c_int
+    L.fgb_probe_staging.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    L.fgb_probe_staging.restype = ctypes.c_int
     return L
+
+
+def probe_staging(torch, dev, iters=20000):
+    """Per-compute-unit cycles per 128-deep block of the GEMM's staging traffic
+    (libfgb_probe.so: the 256x256 tile's fragment reads, its direct-to-LDS
+    operand loads, both), beside the 2048 cycles its MFMAs take at the peak
+    rate; None if the probe is missing."""
+    import ctypes
+    L = _probe_lib()
+    if L is None:
+        return None
+    cyc = (ctypes.c_double * 3)()
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if L.fgb_probe_staging(iters, cyc, st) != 0:
+        return None
+    reads, dma, both = cyc[0], cyc[1], cyc[2]
+    return {"what": "one 256x256 tile per CU, per 128-deep block: cycles of the fragment reads alone (192 KB "
+                    "ds_read_b128), of the direct-to-LDS operand loads alone (64 KB global_load_lds_dwordx4 "
+                    "from L2), of both; the block's 64 FP8 MFMAs per SIMD take 2048 cycles at the peak rate",
+            "mfma_cycles": 2048, "read_cycles": round(reads, 1), "dma_cycles": round(dma, 1),
+            "both_cycles": round(both, 1), "read_B_per_clk": round(192 * 1024 / reads, 1),
+            "dma_B_per_clk": round(64 * 1024 / dma, 1)}
+
+
+def gemm_operands(torch, b, prefix=""):
+    """Each step GEMM's E4M3 operands as (A [rows, contraction], B [cols,
+    contraction], output dtype), from a linear step's buffers."""
+    return {prefix + "gemm_fprop": (b["qx"], b["qwT"], torch.bfloat16),
+            prefix + "gemm_dgrad": (b["qdy"], b["qw"], torch.bfloat16),
+            prefix + "gemm_wgrad": (b["qxT"], b["qdyT"], torch.float32)}
+
+
+def blas_reference(torch, dev, ops, work):
+    """hipBLASLt's plain FP8 GEMM (torch._scaled_mm, one tensor-wide scale of 1,
+    no per-block rescale) on each step GEMM's own E4M3 operands and output
+    dtype: a reference for what the matrix core reaches without the block
+    scaling, timed back to back (median of 3 x 10 launches)."""
+    out = {}
+    one = torch.tensor(1.0, device=dev)
+    f8 = torch.float8_e4m3fn
+    for name, (a, b, odt) in ops.items():
+        fn = lambda: torch._scaled_mm(a.view(f8), b.view(f8).t(), scale_a=one, scale_b=one, out_dtype=odt)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 100.0)
+        us = sorted(ts)[1]
+        rate = work[name]["flop"] / (us * 1e-6)
+        out[name] = {"us": round(us, 1), "TFLOP/s": round(rate / 1e12, 1), "frac_fp8_peak": round(rate / FP8_PEAK, 4)}
+    return out
 
 
 def probe_clock_mhz(torch, dev, iters=200000):
@@ -740,10 +808,13 @@ def main():
         print("bench.py: --recipe ue8m0 and --rounding sr apply to --workload linear_dsv3_attn", file=sys.stderr)
         sys.exit(2)
     cpu_inputs = None
+    blas_ops = None
     if args.workload == "ffn_dense":
         up, down = wl.ffn_dense_up(), wl.ffn_dense_down()
-        kernels = prefixed(linear_step(fgb, torch, dev, up), "up.") + \
-            prefixed(linear_step(fgb, torch, dev, down), "down.")
+        bu, bd = {}, {}
+        kernels = prefixed(linear_step(fgb, torch, dev, up, bufs=bu), "up.") + \
+            prefixed(linear_step(fgb, torch, dev, down, bufs=bd), "down.")
+        blas_ops = {**gemm_operands(torch, bu, "up."), **gemm_operands(torch, bd, "down.")}
         config = {"workload": "ffn_dense fwd+bwd: up X[8192,7168] (Student-t(3)) W_up[7168,18432] "
                               "dY_up[8192,18432]; down H[8192,18432] (Student-t(3)) W_down[18432,7168] "
                               "dY_down[8192,7168]; 6 GEMMs, contraction up to 18432 (144 blocks)",
@@ -756,8 +827,10 @@ def main():
             print("bench.py: stochastic rounding uses absmax/448 scales (--recipe fp32)", file=sys.stderr)
             sys.exit(2)
         two_stage = ue8m0 and args.ue8m0_weights == "two-stage"
+        bl = {}
         kernels = linear_step(fgb, torch, dev, d, separate_dy=args.separate_dy_casts, ue8m0=ue8m0, sr=sr,
-                              two_stage=two_stage)
+                              two_stage=two_stage, bufs=bl)
+        blas_ops = gemm_operands(torch, bl)
         config = {"workload": "linear_dsv3_attn fwd+bwd: X[4096,7168] W[7168,7168] dY[4096,7168]"
                               + (", power-of-two (UE8M0) scales" if ue8m0 else "")
                               + (" with the two-stage weight cast" if two_stage else "")
@@ -868,6 +941,13 @@ def main():
                                  "single-wave samplers beside it: s_memtime ticks per s_memrealtime time)")
     if mhz_probe:
         roofline["clock_mhz_mfma_only"] = round(mhz_probe, 1)
+    staging = probe_staging(torch, dev)
+    if staging:
+        roofline["staging_probe"] = staging
+    if args.blas_reference and blas_ops is not None:
+        blas_ops = {n: o for n, o in blas_ops.items() if n in kinfo}
+        for name, v in blas_reference(torch, dev, blas_ops, work).items():
+            kinfo[name]["hipblaslt_plain_fp8"] = v
     quant_ms = sum(v for k, v in per_kernel_ms.items() if "bytes" in work[k])
     config.update({"gemm_flop_per_step": step_flop, "quant_bytes_per_step": quant_bytes,
                    "schedule": ("overlap: casts " + ", ".join(n for n, _, _, lane, _ in kernels if lane == 1)

@@ -83,6 +83,80 @@ __global__ __launch_bounds__(64) void k_clock_sample(unsigned long long window, 
     }
 }
 
+// Staging throughput: one 512-thread block per compute unit repeats, `iters`
+// times, the LDS traffic that the block-scaled GEMM's 256x256 tile has per
+// 128-deep block, with the GEMM's own instruction forms and layouts:
+//   MODE 1: the fragment reads -- each of the 8 waves reads its 128 A rows and
+//           64 B rows of the 128-byte stage rows, 24 ds_read_b128 at the GEMM's
+//           XOR-swizzled slots (192 KB per round and block);
+//   MODE 2: the direct-to-LDS loads of the next block's two 32 KB operand
+//           slices -- 8 global_load_lds_dwordx4 per wave from an L2-resident
+//           source (64 KB per round and block) into the other stage;
+//   MODE 3: both, as in the GEMM's main loop.
+// Each round ends as a GEMM block does: this wave's loads waited for, LDS
+// drained, barrier.  Thread 0 records the round loop's s_memtime ticks.
+typedef __attribute__((address_space(3))) uint8_t lds_u8_p;
+constexpr int kStage = 65536;                      // one stage: 256 A rows + 256 B rows of 128 bytes
+constexpr int kSrcBlocks = 8;                      // distinct 64 KB source blocks cycled through
+__device__ __forceinline__ void probe_dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "m0", "memory");
+}
+__device__ __forceinline__ int probe_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int MODE>
+__global__ __launch_bounds__(512) void k_staging_probe(int iters, const uint8_t* src, unsigned long long* out,
+                                                       uint32_t* sink)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+    const uint32_t base_lds = (uint32_t)(uintptr_t)(lds_u8_p*)smem;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = tid; i < 2 * kStage / 4; i += 512) reinterpret_cast<uint32_t*>(smem)[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    // fragment slots as in the GEMM (waves 2 x 4, 128 x 64 each)
+    const int frow = lane & 15, fg = lane >> 4, wm = wave & 1, wn = wave >> 1;
+    const uint32_t fo = (uint32_t)(((2 * fg) ^ probe_swz(frow)) << 4);
+    const uint32_t a_lo = (uint32_t)((wm * 128 + frow) * 128) + fo;
+    const uint32_t b_lo = (uint32_t)(kStage / 2) + (uint32_t)((wn * 64 + frow) * 128) + fo;
+    // load plan as in the GEMM: row group (wave + 8 i), lane -> row lane/8, chunk lane&7
+    uint32_t goff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        goff[i] = (uint32_t)(((wave + 8 * i) * 8 + (lane >> 3)) * 128 + (lane & 7) * 16);
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+        const int st = it & 1;
+        if (MODE & 2) {
+            const uint8_t* blk = src + (size_t)(it % kSrcBlocks) * kStage;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                probe_dma16(blk, goff[i], base_lds + (uint32_t)((st ^ 1) * kStage + (wave + 8 * i) * 1024));
+        }
+        if (MODE & 1) {
+            const uint8_t* sp = smem + st * kStage;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 l = *reinterpret_cast<const uint4*>(sp + a_lo + i * 2048);
+                const uint4 h = *reinterpret_cast<const uint4*>(sp + (a_lo ^ 16u) + i * 2048);
+                x.x ^= l.x ^ h.x; x.y ^= l.y ^ h.y; x.z ^= l.z ^ h.z; x.w ^= l.w ^ h.w;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 l = *reinterpret_cast<const uint4*>(sp + b_lo + j * 2048);
+                const uint4 h = *reinterpret_cast<const uint4*>(sp + (b_lo ^ 16u) + j * 2048);
+                x.x ^= l.x ^ h.x; x.y ^= l.y ^ h.y; x.z ^= l.z ^ h.z; x.w ^= l.w ^ h.w;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    if (tid == 0) out[blockIdx.x] = t1 - t0;
+    sink[(size_t)blockIdx.x * 512 + tid] = x.x ^ x.y ^ x.z ^ x.w;   // keeps the reads
+}
+
 struct Sample {
     unsigned long long* d = nullptr;
     int blocks = 0;
@@ -162,4 +236,42 @@ extern "C" int fgb_probe_clock(int iters, double* mhz, void* stream)
     std::sort(f.begin(), f.end());
     *mhz = f[f.size() / 2];
     return 0;
+}
+
+extern "C" int fgb_probe_staging(int iters, double* cycles, void* stream)
+{
+    if (cycles == nullptr || iters <= 0 || iters > 10000000) return -1;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -2;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -2;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the source: kSrcBlocks 64 KB blocks (512 KB, L2-resident), every block reads the same
+    uint8_t* src = nullptr;
+    unsigned long long* d = nullptr;
+    uint32_t* sink = nullptr;
+    const size_t src_bytes = (size_t)kSrcBlocks * kStage;
+    if (hipMalloc(&src, src_bytes) != hipSuccess) return -2;
+    if (hipMalloc(&d, sizeof(unsigned long long) * (size_t)cus) != hipSuccess) { hipFree(src); return -2; }
+    if (hipMalloc(&sink, sizeof(uint32_t) * 512 * (size_t)cus) != hipSuccess) { hipFree(src); hipFree(d); return -2; }
+    hipError_t e = hipMemsetAsync(src, 0x3C, src_bytes, s);
+    std::vector<unsigned long long> h((size_t)cus);
+    for (int mode = 1; mode <= 3 && e == hipSuccess; ++mode) {
+        for (int pass = 0; pass < 2 && e == hipSuccess; ++pass) {     // pass 0 warms caches and clocks
+            const int n = pass == 0 ? (iters < 100 ? iters : 100) : iters;
+            if (mode == 1) hipLaunchKernelGGL(k_staging_probe<1>, dim3((unsigned)cus), dim3(512), 0, s, n, src, d, sink);
+            else if (mode == 2) hipLaunchKernelGGL(k_staging_probe<2>, dim3((unsigned)cus), dim3(512), 0, s, n, src, d, sink);
+            else hipLaunchKernelGGL(k_staging_probe<3>, dim3((unsigned)cus), dim3(512), 0, s, n, src, d, sink);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) e = hipMemcpyAsync(h.data(), d, sizeof(unsigned long long) * h.size(), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e == hipSuccess) {
+            std::sort(h.begin(), h.end());
+            cycles[mode - 1] = (double)h[h.size() / 2] / (double)iters;
+        }
+    }
+    hipFree(src);
+    hipFree(d);
+    hipFree(sink);
+    return e == hipSuccess ? 0 : -2;
 }

@@ -22,6 +22,18 @@
  * process: begin returns -1 while one is running, as for a bad argument
  * (blocks outside 1..4096, window outside (0, 1e6] us); end returns -1 with no
  * sample running or mhz NULL; both return -2 for a HIP error.
+ *
+ * fgb_probe_staging: the per-compute-unit throughput of the GEMM's staging
+ * traffic.  One 512-thread block per compute unit repeats `iters` rounds of
+ * what the block-scaled GEMM's 256x256 tile moves per 128-deep block, with the
+ * same instructions and layouts: cycles[0] for the fragment reads alone
+ * (24 ds_read_b128 per wave, 192 KB per round), cycles[1] for the
+ * direct-to-LDS loads alone (8 global_load_lds_dwordx4 per wave from an
+ * L2-resident 512 KB source, 64 KB per round), cycles[2] for both together;
+ * each is the median over compute units of s_memtime ticks per round (shader
+ * clock cycles).  Allocates small device buffers, launches on `stream` and
+ * synchronizes it.  Returns 0, -1 for a bad argument (cycles NULL, iters
+ * outside 1..10^7), -2 for a HIP error.
  */
 #ifndef FGB_PROBE_H
 #define FGB_PROBE_H
@@ -33,6 +45,7 @@ extern "C" {
 int fgb_probe_clock(int iters, double* mhz, void* stream);
 int fgb_probe_clock_begin(int blocks, double window_us, void* stream);
 int fgb_probe_clock_end(double* mhz, void* stream);
+int fgb_probe_staging(int iters, double* cycles, void* stream);
 
 #ifdef __cplusplus
 }

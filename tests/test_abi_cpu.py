@@ -274,21 +274,26 @@ def test_quantize_128x128_batched_validation():
 
 
 def test_probe_library_exports_and_argument_errors():
-    """libfgb_probe.so (the benchmark's clock probe, include/fgb_probe.h): every
+    """libfgb_probe.so (the benchmark's clock and staging probes, include/fgb_probe.h): every
     declared function is exported, and bad arguments return -1 before any HIP call."""
     path = os.path.join(ROOT, "fine_grained_block_amd", "libfgb_probe.so")
     if not os.path.exists(path):
         pytest.skip("libfgb_probe.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "fgb_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fgb_\w+)\s*\(", text)))
-    assert names == ["fgb_probe_clock", "fgb_probe_clock_begin", "fgb_probe_clock_end"]
+    assert names == ["fgb_probe_clock", "fgb_probe_clock_begin", "fgb_probe_clock_end", "fgb_probe_staging"]
     L = ctypes.CDLL(path)
     for n in names:
         assert hasattr(L, n), n
     L.fgb_probe_clock.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), P]
     L.fgb_probe_clock_begin.argtypes = [ctypes.c_int, ctypes.c_double, P]
     L.fgb_probe_clock_end.argtypes = [ctypes.POINTER(ctypes.c_double), P]
+    L.fgb_probe_staging.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), P]
     mhz = ctypes.c_double(0.0)
+    cyc = (ctypes.c_double * 3)()
+    assert L.fgb_probe_staging(0, cyc, None) == -1
+    assert L.fgb_probe_staging(10**7 + 1, cyc, None) == -1
+    assert L.fgb_probe_staging(10, None, None) == -1
     assert L.fgb_probe_clock(0, ctypes.byref(mhz), None) == -1
     assert L.fgb_probe_clock(10, None, None) == -1
     assert L.fgb_probe_clock_begin(0, 100.0, None) == -1
