@@ -283,19 +283,20 @@ __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) {
 // Vector global memory access
 // ---------------------------------------------------------------------------
 // Blocks of a grid of nrb row blocks x ncb column blocks, launched as one
-// dimension.  COLS_FAST: the column blocks vary fastest, so the blocks resident
+// dimension.  cols_fast: the column blocks vary fastest, so the blocks resident
 // together cover whole rows of the tensor, whose bytes spread over every HBM
 // channel; ordered row blocks first, they read one column band of many rows, at
-// addresses that repeat with the row pitch -- for a power-of-two pitch (2048 or
-// 8192 bytes) on a few channels only (MoE weight cast 8% faster, 1x128 cast
-// 10%).  Kernels that write a transposed output keep the row blocks fastest:
-// consecutive blocks then extend the same transposed rows (measured 7% faster).
+// addresses that repeat with the row pitch -- for a pitch that is a multiple of
+// 8 KB on a few channels only (MoE weight cast, pitch 8 KB: 11% faster cold;
+// 1x128 cast 5-7%).  With the row blocks fastest, consecutive blocks extend the
+// same transposed output rows, which kernels with a transposed output prefer
+// at other pitches (128x128 cast at a 14 KB pitch 5% faster cold; the 128x1
+// cast and the requant 7-8% faster).
 struct BlockRC { int64_t r, c; };
-template <bool COLS_FAST>
-__device__ __forceinline__ BlockRC block_rc(int64_t nrb, int64_t ncb) {
+__device__ __forceinline__ BlockRC block_rc(bool cols_fast, int64_t nrb, int64_t ncb) {
     const uint32_t b = blockIdx.x;
-    if constexpr (COLS_FAST) return {(int64_t)(b / (uint32_t)ncb), (int64_t)(b % (uint32_t)ncb)};
-    else return {(int64_t)(b % (uint32_t)nrb), (int64_t)(b / (uint32_t)nrb)};
+    if (cols_fast) return {(int64_t)(b / (uint32_t)ncb), (int64_t)(b % (uint32_t)ncb)};
+    return {(int64_t)(b % (uint32_t)nrb), (int64_t)(b / (uint32_t)nrb)};
 }
 // The one-dimensional grid for nrb x ncb blocks; 0 when it exceeds the launch limit.
 inline unsigned grid_rc(int64_t nrb, int64_t ncb) {

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void k_quantize_1x128(
     static_assert(!(PO2 && SR), "stochastic rounding uses absmax/448 scales");
     const int lane16 = threadIdx.x & 15;
     const int grp = threadIdx.x >> 4;
-    const BlockRC bl = block_rc<true>((R + kQ1Rows - 1) / kQ1Rows, (C + kTile - 1) / kTile);
+    const BlockRC bl = block_rc(true, (R + kQ1Rows - 1) / kQ1Rows, (C + kTile - 1) / kTile);
     const int64_t rb = bl.r * kQ1Rows;
     const int64_t j = bl.c;
     const int64_t c = j * kTile + lane16 * 8;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void k_tile128(
     const float* __restrict__ s_in, int64_t lds_in, float amax_floor,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
     float* __restrict__ s_out, int64_t lds_out, float* __restrict__ s_row, int64_t lds_row, SrArgs sr,
-    TileBatch bt)
+    TileBatch bt, int cols_fast)
 {
     static_assert(!(SR && (PO2 || MODE == kTileRequant || MODE == kTileRequant128x128)),
                   "stochastic rounding: absmax/448 scales, no requant");
@@ -200,8 +200,7 @@ __global__ __launch_bounds__(256) void k_tile128(
 
     const int t = threadIdx.x;
     const int cg = t & 15, rg = t >> 4, wave = t >> 6;
-    constexpr bool kColsFast = MODE == kTile128x128 || MODE == kTileDual || MODE == kTileRequant128x128;
-    const BlockRC bl = block_rc<kColsFast>((R + kTile - 1) / kTile, (C + kTile - 1) / kTile);
+    const BlockRC bl = block_rc(cols_fast != 0, (R + kTile - 1) / kTile, (C + kTile - 1) / kTile);
     const int64_t r0 = bl.r * kTile;
     const int64_t c0 = bl.c * kTile;
     const int64_t cc = c0 + cg * 8;
@@ -508,30 +507,30 @@ static void launch_tile128_t(TileMode mode, dim3 grid, const void* in, int64_t R
                              const float* s_in, int64_t lds_in, float amax_floor,
                              uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                              float* s_out, int64_t lds_out, hipStream_t stream, float* s_row, int64_t lds_row,
-                             SrArgs a, TileBatch bt)
+                             SrArgs a, TileBatch bt, int cols_fast)
 {
     switch (mode) {
     case kTile128x1:
         hipLaunchKernelGGL((k_tile128<kTile128x1, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt, cols_fast);
         break;
     case kTile128x128:
         hipLaunchKernelGGL((k_tile128<kTile128x128, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt, cols_fast);
         break;
     case kTileRequant:
         if constexpr (!SR)
             hipLaunchKernelGGL((k_tile128<kTileRequant, PO2, false>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                               s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
+                               s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt, cols_fast);
         break;
     case kTileDual:
         hipLaunchKernelGGL((k_tile128<kTileDual, PO2, SR>), grid, dim3(256), 0, stream, in, R, C, ldin,
-                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
+                           s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt, cols_fast);
         break;
     case kTileRequant128x128:
         if constexpr (!SR)
             hipLaunchKernelGGL((k_tile128<kTileRequant128x128, PO2, false>), grid, dim3(256), 0, stream, in, R, C,
-                               ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt);
+                               ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT, s_out, lds_out, s_row, lds_row, a, bt, cols_fast);
         break;
     }
 }
@@ -547,15 +546,20 @@ hipError_t launch_tile128(TileMode mode, const void* in, int64_t R, int64_t C, i
     const dim3 grid(grid_rc((R + kTile - 1) / kTile, (C + kTile - 1) / kTile), 1, (unsigned)batch);
     if (grid.x == 0) return hipErrorInvalidValue;
     const SrArgs a = sr_args(sr);
+    // block order (block_rc): column blocks fastest for the row-major-output
+    // tilings when the input pitch is a multiple of 8 KB, row blocks otherwise
+    const int64_t pitch = ldin * (mode == kTileRequant || mode == kTileRequant128x128 ? 1 : 2);
+    const int cols_fast = (mode == kTile128x128 || mode == kTileDual || mode == kTileRequant128x128) &&
+                          pitch % 8192 == 0;
     if (po2)
         launch_tile128_t<true, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                      s_out, lds_out, stream, s_row, lds_row, a, bt);
+                                      s_out, lds_out, stream, s_row, lds_row, a, bt, cols_fast);
     else if (sr)
         launch_tile128_t<false, true>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                      s_out, lds_out, stream, s_row, lds_row, a, bt);
+                                      s_out, lds_out, stream, s_row, lds_row, a, bt, cols_fast);
     else
         launch_tile128_t<false, false>(mode, grid, in, R, C, ldin, s_in, lds_in, amax_floor, q, ldq, qT, ldqT,
-                                       s_out, lds_out, stream, s_row, lds_row, a, bt);
+                                       s_out, lds_out, stream, s_row, lds_row, a, bt, cols_fast);
     return hipGetLastError();
 }
 

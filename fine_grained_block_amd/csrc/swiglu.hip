@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(
     const int lane16 = threadIdx.x & 15;
     const int grp = threadIdx.x >> 4;
     const int64_t nb = F / kTile;
-    const BlockRC bl = block_rc<true>((R + kSwRows - 1) / kSwRows, nb);
+    const BlockRC bl = block_rc(true, (R + kSwRows - 1) / kSwRows, nb);
     const int64_t b = bl.c;
     const int64_t c = b * kTile + lane16 * 8;          // column in H and G; U at F + c
     for (int it = 0; it < 4; ++it) {
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void k_swiglu_bwd(
     const int t = threadIdx.x;
     const int cg = t & 15, rg = t >> 4, wave = t >> 6;
     const int64_t nb = F / kTile;
-    const BlockRC bl = block_rc<true>((R + kTile - 1) / kTile, nb);
+    const BlockRC bl = block_rc(true, (R + kTile - 1) / kTile, nb);
     const int64_t r0 = bl.r * kTile;
     const int64_t j = bl.c;
     const int64_t cc = j * kTile + cg * 8;             // gate column; up column F + cc
