@@ -148,6 +148,54 @@ def test_strided_operands(orc):
     assert np.all(host(sbuf[:, R:]) == 0) and np.all(host(sTbuf[:, C:]) == 0)
 
 
+@pytest.mark.parametrize("R,C,ld", [(300, 4096, 4096), (257, 8192, 8192), (200, 1000, 4096), (384, 4096, 4096),
+                                    (256, 1024, 4096)])
+def test_pitch_multiple_of_8k(orc, R, C, ld):
+    """Row pitches that are multiples of 8 KB, where the 128x128 and dual casts run
+    their blocks column-first (the other pitches run them row-first): ragged rows, and
+    a view of C columns of a wider buffer (ragged last column tile); the weight cast
+    where the shape is whole 128x128 tiles (it requires them).  Bit-exact."""
+    x = stress(R, C, 4100 + R + C)
+    buf = torch.zeros((R, ld), dtype=torch.bfloat16, device="cuda")
+    buf[:, :C] = bf16_dev(x)
+    xv = buf[:, :C]
+    oq, os_ = orc.quantize_1x128(x)
+    oqT, osT = orc.quantize_128x1(x)
+    q, s, qT, sT = fgb.quantize_dual(xv)
+    assert_codes_equal(q, oq, f"dual q[{R}x{C}/{ld}]")
+    assert_scales_equal(s, os_, f"dual s[{R}x{C}/{ld}]")
+    assert_codes_equal(qT, oqT, f"dual qT[{R}x{C}/{ld}]")
+    assert_scales_equal(sT, osT, f"dual sT[{R}x{C}/{ld}]")
+    q1, s1 = fgb.quantize_1x128(xv)
+    assert_codes_equal(q1, oq, f"1x128 q[{R}x{C}/{ld}]")
+    assert_scales_equal(s1, os_, f"1x128 s[{R}x{C}/{ld}]")
+    if R % 128 or C % 128:
+        return
+    wq, wqT, ws = fgb.quantize_128x128(xv)
+    owq, owqT, ows = orc.quantize_128x128(x)
+    assert_codes_equal(wq, owq, f"128x128 q[{R}x{C}/{ld}]")
+    assert_codes_equal(wqT, owqT, f"128x128 qT[{R}x{C}/{ld}]")
+    assert_scales_equal(ws, ows, f"128x128 s[{R}x{C}/{ld}]")
+
+
+def test_128x128_pitch_8k_single_and_batched(orc):
+    """The 128x128 cast at an 8 KB pitch (column-first blocks), one matrix and a stack."""
+    E, K, N = 2, 384, 4096
+    ws = [stress(K, N, 4200 + e) for e in range(E)]
+    for e in range(E):
+        q, qT, s = fgb.quantize_128x128(bf16_dev(ws[e]))
+        oq, oqT, os_ = orc.quantize_128x128(ws[e])
+        assert_codes_equal(q, oq, f"single q[{e}]")
+        assert_codes_equal(qT, oqT, f"single qT[{e}]")
+        assert_scales_equal(s, os_, f"single s[{e}]")
+    q, qT, s = fgb.quantize_128x128_batched(torch.stack([bf16_dev(x) for x in ws]))
+    for e in range(E):
+        oq, oqT, os_ = orc.quantize_128x128(ws[e])
+        assert_codes_equal(q[e], oq, f"batched q[{e}]")
+        assert_codes_equal(qT[e], oqT, f"batched qT[{e}]")
+        assert_scales_equal(s[e], os_, f"batched s[{e}]")
+
+
 def test_deterministic_repeat():
     x = bf16_dev(stress(512, 1024, 8))
     a = [fgb.quantize_1x128(x), fgb.quantize_1x128(x)]
