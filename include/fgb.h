@@ -290,6 +290,8 @@ int fgb_requant_128x128_ue8m0(const uint8_t* q, int64_t K, int64_t N, int64_t ld
  * s_a * s_b and promoted into an FP32 accumulator; [scratch]: all three
  * GEMMs of a linear in E4M3, Fprop/Dgrad to BF16, Wgrad to FP32).
  * Output BF16 is rounded to nearest even from the FP32 accumulator.
+ * Outputs are written with non-temporal stores: they are not left in L2 or
+ * the MALL, so a kernel that reads them next fetches them from HBM.
  * ---------------------------------------------------------------------- */
 
 /* Fprop: Y[m][n] = bf16( sum_b sx[b][m] * sw[b][n/128] *
