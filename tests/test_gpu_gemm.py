@@ -100,6 +100,37 @@ def test_tail_round_split(orc, M, N):
     check_gemm(host(dw), r, aabs, False, f"wgrad {M}x{N}x{Mc}", hw_bound_wgrad(qxT, sxT, qdyT, sdyT, Mc), 2, stated=False)
 
 
+@pytest.mark.parametrize("K,N,M", [(7168, 7168, 4096), (2432, 4608, 777)])
+def test_wgrad_accumulate_multi_tile(orc, K, N, M):
+    """Accumulating Wgrad over many tiles: at 7168 x 7168 over 4096 tokens (3
+    rounds of 256 x 224 tiles plus 128 tiles run as column halves) and on a
+    ragged 10 x 18 tile grid.  Sampled outputs against the oracle's X^T dY plus
+    the old contents; every output against the property that the accumulating
+    call adds the old value to the plain call's result in one fp32 addition."""
+    g = np.random.default_rng(K + 3 * N + 7 * M)
+    Mp = -(-M // T) * T
+    nb = Mp // T
+    qxT, qdyT = rand_codes(g, (K, Mp)), rand_codes(g, (N, Mp))
+    qxT[:, M:] = 0
+    qdyT[:, M:] = 0
+    sxT, sdyT = rand_scales(g, (nb, K)), rand_scales(g, (nb, N))
+    prev = g.standard_normal((K, N)).astype(np.float32)
+    a, sa, b, sb = u8_dev(qxT), f32_dev(sxT), u8_dev(qdyT), f32_dev(sdyT)
+    plain = fgb.gemm_wgrad(a, sa, b, sb, M)
+    acc = f32_dev(prev)
+    fgb.gemm_wgrad(a, sa, b, sb, M, dw=acc, accumulate=True)
+    torch.cuda.synchronize()
+    want = plain + f32_dev(prev)
+    bad = int((want.view(torch.int32) != acc.view(torch.int32)).sum())
+    assert bad == 0, f"{bad} outputs differ from the plain result plus the old value"
+    rows, cols = sample_idx(K, 80, K), sample_idx(N, 80, N)
+    r, aabs = orc.gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols)
+    hw = hw_bound_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols)
+    pv = prev[np.ix_(rows, cols)].astype(np.float64)
+    check_gemm(host(acc)[np.ix_(rows, cols)], r + pv, aabs + np.abs(pv), False,
+               f"wgrad accumulate {K}x{N}x{M}", hw, nb + 1, stated=False)
+
+
 SMALL_INT_CODES = np.array([0x00, 0x80, 0x38, 0xB8, 0x40, 0xC0, 0x44, 0xC4, 0x48, 0xC8, 0x4C, 0xCC, 0x50, 0xD0],
                            np.uint8)   # 0, -0, +-1, +-2, +-3, +-4, +-6, +-8
 

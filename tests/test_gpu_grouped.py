@@ -97,12 +97,16 @@ def test_grouped_small_full(orc, loads):
     for e, n in enumerate(loads):
         if n == 0:
             assert torch.all(dw[e] == 0)
-    # accumulate leaves empty experts unchanged
+    # accumulate leaves empty experts unchanged and adds the old value to every
+    # other output in one fp32 addition
     prev = torch.full_like(dw, 3.0)
     fgb.gemm_wgrad_grouped(od, qxT, sxT, qdyT, sdyT, dw=prev, accumulate=True)
     for e, n in enumerate(loads):
         if n == 0:
             assert torch.all(prev[e] == 3.0)
+    assert torch.equal((dw + 3.0).view(torch.int32), prev.view(torch.int32))
+    check_gemm(host(prev).reshape(r.shape), r + 3.0, aabs + 3.0, False, f"wgrad grouped accumulate {loads}", hww,
+               nbw + 1, stated=False)
 
 
 def test_single_expert_equals_dense_bitwise():
