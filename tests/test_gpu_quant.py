@@ -11,6 +11,7 @@ from fine_grained_block_amd import workloads as wl
 from parity import assert_codes_equal, assert_scales_equal, bf16_dev, u8_dev, f32_dev, host
 
 pytestmark = pytest.mark.gpu
+T = 128
 
 
 def stress(R, C, seed):
@@ -287,3 +288,72 @@ def test_128x128_batched_equals_single(orc, ue8m0):
         assert_codes_equal(q[e], oq, f"batched q[{e}]")
         assert_codes_equal(qT[e], oqT, f"batched qT[{e}]")
         assert_scales_equal(s[e], os_, f"batched s[{e}]")
+
+
+# ---------------------------------------------------------------------------
+# beyond 2^31 elements: the bf16 input is larger than 4 GiB
+# ---------------------------------------------------------------------------
+
+def wide_table():
+    """bf16 bit patterns of 16 magnitude decades x 4096 Gaussian quantiles (and
+    +-0): a uniformly drawn 16-bit index maps to a value of mixed magnitude."""
+    from scipy.special import ndtri
+    z = ndtri((np.arange(4096) + 0.5) / 4096.0)
+    t = (z[None, :] * np.power(10.0, np.linspace(-4.0, 2.0, 16))[:, None]).ravel().astype(np.float32)
+    t[0], t[1] = 0.0, -0.0
+    return wl.bf16_bits(t)
+
+
+def test_quantizers_beyond_2g_elements(orc):
+    """X [300001, 7168] bf16 (4.30 GB, 2.15e9 elements): 1x128, 128x1, dual and
+    requant on all of it, 128x128 on its first 299904 rows.  Bit-exact against
+    the oracle on sampled rows (1x128) and 128-row blocks (the rest): the row
+    that holds element 2^31, its neighbours and the ragged last block."""
+    g = np.random.default_rng(31)
+    R, C = 300001, 7168
+    assert R * C > (1 << 31) and 299904 * C > (1 << 31)
+    table = wide_table()
+    print(f"generating {R * C * 2 / 1e9:.2f} GB of bf16 input", flush=True)
+    x = np.empty((R, C), np.uint16)
+    for r0 in range(0, R, 1 << 14):
+        n = min(1 << 14, R - r0)
+        x[r0:r0 + n] = table[g.integers(0, 1 << 16, (n, C), dtype=np.uint16)]
+    rb = (1 << 31) // C                              # the row that holds element 2^31
+    rows = np.unique(np.concatenate([[0, 1, rb - 1, rb, rb + 1, R - 2, R - 1], g.choice(R, 40, replace=False)]))
+    blocks = sorted({0, rb // T, (R - 1) // T, *g.choice(R // T, 2, replace=False).tolist()})
+    xd = bf16_dev(x)
+    ri = torch.as_tensor(rows, device=xd.device)
+
+    def block_cols(t, b):                            # columns of one 128-row block of a [C, Rp] output
+        return t[:, b * T:(b + 1) * T]
+
+    q, s = fgb.quantize_1x128(xd)
+    oq, os_ = orc.quantize_1x128(x[rows])
+    assert_codes_equal(q[ri], oq, "1x128 q beyond 2^31")
+    assert_scales_equal(s[:, ri], os_, "1x128 s beyond 2^31")
+    rq, rs = fgb.requant_128x1(q, s)
+    for b in blocks:
+        xb = x[b * T:min((b + 1) * T, R)]
+        orq, ors = orc.requant_128x1(*orc.quantize_1x128(xb))
+        assert_codes_equal(block_cols(rq, b), orq, f"requant qT block {b}")
+        assert_scales_equal(rs[b:b + 1], ors, f"requant sT block {b}")
+    del q, s, rq, rs
+    qT, sT = fgb.quantize_128x1(xd)
+    dq, ds, dqT, dsT = fgb.quantize_dual(xd)
+    assert_codes_equal(dq[ri], oq, "dual q beyond 2^31")
+    assert_scales_equal(ds[:, ri], os_, "dual s beyond 2^31")
+    del dq, ds
+    for b in blocks:
+        oqT, osT = orc.quantize_128x1(x[b * T:min((b + 1) * T, R)])
+        assert_codes_equal(block_cols(qT, b), oqT, f"128x1 qT block {b}")
+        assert_scales_equal(sT[b:b + 1], osT, f"128x1 sT block {b}")
+        assert_codes_equal(block_cols(dqT, b), oqT, f"dual qT block {b}")
+        assert_scales_equal(dsT[b:b + 1], osT, f"dual sT block {b}")
+    del qT, sT, dqT, dsT
+    K = 299904
+    qw, qwT, sw = fgb.quantize_128x128(xd[:K])
+    for b in sorted({0, rb // T, K // T - 1}):
+        oqw, oqwT, osw = orc.quantize_128x128(x[b * T:(b + 1) * T])
+        assert_codes_equal(qw[b * T:(b + 1) * T], oqw, f"128x128 q block {b}")
+        assert_codes_equal(block_cols(qwT, b), oqwT, f"128x128 qT block {b}")
+        assert_scales_equal(sw[b:b + 1], osw, f"128x128 s block {b}")
