@@ -340,7 +340,11 @@ int fgb_gemm_wgrad(int64_t K, int64_t N, int64_t M,
  * quantization, so no grouped quantizer is needed.  `offsets` is a DEVICE
  * array of E+1 int32, read by the kernels (no host synchronization).  All
  * operands are dense (leading dimension = row length).  Rows at or beyond
- * offsets[E] are not written.
+ * offsets[E] are not written.  0 <= E <= 65535 (else FGB_E_SHAPE).  The
+ * kernels address an operand with 32-bit byte offsets: the token-side
+ * operand (all R_pad rows of qx or qdy, or the K or N rows of qxT or qdyT)
+ * and one expert's weight must each end within 4 GiB of their base, else
+ * FGB_E_UNSUPPORTED (nothing is launched).
  * ---------------------------------------------------------------------- */
 
 /* Y[r] = X[r] W_e for rows r of segment e.  qx [R_pad][K], sx [K/128][R_pad],

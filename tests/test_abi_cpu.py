@@ -162,11 +162,15 @@ def test_grouped_validation():
     assert g(off=P(0x60002)) == E_ALIGN
     assert g(E=0) == OK
     assert g(E=-1) == E_SHAPE
+    # operands whose byte offsets do not fit 32 bits; more than 65535 experts
+    assert g(R=1 << 20, K=8192) == E_UNSUP
+    assert g(E=1 << 16) == E_SHAPE
     w = lambda **k: L.fgb_gemm_wgrad_grouped(k.get("E", 4), P(0x60000), k.get("R", 512), 128, 128, A, B, C_, D,
                                              k.get("dw", P(0x50000)), 0, None)
     assert w(dw=P(0)) == E_NULL
     assert w(R=130) == E_SHAPE
     assert w(E=0) == OK
+    assert w(R=1 << 26) == E_UNSUP
 
 
 def test_binding_rejects_host_tensors():
