@@ -137,9 +137,9 @@ __device__ __forceinline__ int wave_scan(int v) {
 
 // Row-grouped (MoE) tiles: expert e owns rows [o(e), o(e+1)) of the output,
 // o(e) = offsets[e] clamped to [0, min(offsets[E], M)], and is cut into
-// ceil(len/256) row tiles of its own (the last one may hold 128 rows).  Every
-// wave of the block finds, for row-tile tm, the expert and its row range;
-// ntm is the number of row tiles over all experts.
+// ceil(len/256) row tiles of its own (the last one may hold 128 rows).  ntm is
+// the number of row tiles over all experts; the tiles are the experts' own
+// (row tiles x tiles_n) grids in expert order.
 struct RowTile { int e; int64_t m0, mend; };
 
 __device__ __forceinline__ int clamp_off(int v, int total) { return v < 0 ? 0 : (v > total ? total : v); }
@@ -159,9 +159,16 @@ __device__ int row_tiles_total(const GemmArgs& g, int total) {
     return ntm;
 }
 
-__device__ RowTile row_tile_of(const GemmArgs& g, int total, int tm) {
+// Tile t of the row-grouped sequence: every wave of the block finds the expert
+// whose tiles hold t (a 64-lane prefix scan over the offsets), and orders that
+// expert's tiles in groups of 8 row tiles, so that the tiles an XCD runs
+// together share one expert's weight columns (a group over all row tiles
+// would straddle experts; grouped Fprop 1.4-1.7% slower).  An empty result
+// (mend == m0) means t lies past the last tile.
+__device__ RowTile grouped_tile(const GemmArgs& g, int total, int t, int tiles_n, int& tn) {
     const int lane = threadIdx.x & 63;
     RowTile rt{0, 0, 0};
+    tn = 0;
     int before = 0;                                 // row tiles of the experts before this chunk
     for (int base = 0; base < g.E; base += 64) {
         const int e = base + lane;
@@ -171,13 +178,15 @@ __device__ RowTile row_tile_of(const GemmArgs& g, int total, int tm) {
             te = hi > lo ? (hi - lo + kTM - 1) / kTM : 0;
         }
         const int incl = wave_scan(te), excl = incl - te;
-        const bool mine = te > 0 && before + excl <= tm && tm < before + incl;
+        const bool mine = te > 0 && (before + excl) * tiles_n <= t && t < (before + incl) * tiles_n;
         const uint64_t hit = __ballot(mine);
         if (hit) {
             const int j = __builtin_ctzll(hit);
+            int tm;
+            group_order(t - (before + __builtin_amdgcn_readlane(excl, j)) * tiles_n, __builtin_amdgcn_readlane(te, j),
+                        tiles_n, tm, tn);
             rt.e = base + j;
-            rt.m0 = (int64_t)__builtin_amdgcn_readlane(lo, j) +
-                    (int64_t)kTM * (tm - before - __builtin_amdgcn_readlane(excl, j));
+            rt.m0 = (int64_t)__builtin_amdgcn_readlane(lo, j) + (int64_t)kTM * tm;
             rt.mend = __builtin_amdgcn_readlane(hi, j);
             return rt;
         }
@@ -275,9 +284,8 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
         total = total < 0 ? 0 : (total > g.M ? (int)g.M : total);     // never past the rows that exist
         const int ntm = row_tiles_total(g, total);
         if ((int)blockIdx.x >= ntm * tiles_n) return;                  // the grid is an upper bound
-        group_order(xcd_order(blockIdx.x, ntm * tiles_n), ntm, tiles_n, tm, tn);
-        const RowTile rt = row_tile_of(g, total, tm);
-        if (rt.mend <= rt.m0) return;                                  // tm < ntm always finds one
+        const RowTile rt = grouped_tile(g, total, xcd_order(blockIdx.x, ntm * tiles_n), tiles_n, tn);
+        if (rt.mend <= rt.m0) return;                                  // t < ntm * tiles_n always finds one
         m0 = rt.m0; mend = rt.mend;
         Bp += rt.e * g.b_expert_stride;
         sbp += rt.e * g.sb_expert_stride;
