@@ -292,10 +292,14 @@ __global__ __launch_bounds__(kV1Threads) void k_gemm_block_scaled(GemmArgs g)
     } else {
         // experts in order, each expert's tiles spread over all 8 XCDs (experts
         // differ in contraction length, so whole experts per XCD would leave
-        // the XCDs unevenly loaded)
+        // the XCDs unevenly loaded).  Block b runs on XCD b % 8: each expert's
+        // blocks start at a multiple of 8 (the grid pads every expert to one),
+        // so that its tile order meets the XCDs it assumes.
         const int tiles_m = (int)((g.M + kTM - 1) / kTM), per_e = tiles_m * tiles_n;
-        const int e = (int)blockIdx.x / per_e;
-        group_order(xcd_order((int)blockIdx.x - e * per_e, per_e), tiles_m, tiles_n, tm, tn);
+        const int per_pad = (per_e + 7) & ~7;
+        const int e = (int)blockIdx.x / per_pad, local = (int)blockIdx.x - e * per_pad;
+        if (local >= per_e) return;                                    // padding block
+        group_order(xcd_order(local, per_e), tiles_m, tiles_n, tm, tn);
         m0 = (int64_t)tm * kTM;
         // contraction blocks of expert e, clamped to the nkb blocks that exist
         int64_t b0 = g.offsets[e] / kTile, b1 = g.offsets[e + 1] / kTile;
@@ -820,7 +824,7 @@ static void launch_v1(GemmKind kind, bool grouped, const GemmArgs& a, hipStream_
             hipLaunchKernelGGL((k_gemm_block_scaled<TN, false, true, kDense, PO2>), grid, block, 0, stream, p);
         }
     } else if (kind == kWgrad) {
-        const dim3 grid((unsigned)(tiles_m * tiles_n * a.E));
+        const dim3 grid((unsigned)(((tiles_m * tiles_n + 7) & ~7ll) * a.E));   // every expert padded to 8 blocks
         hipLaunchKernelGGL((k_gemm_block_scaled<TN, true, false, kGroupK, PO2>), grid, block, 0, stream, a);
     } else {
         // upper bound on the row tiles: sum over experts of ceil(len/256) <= ceil(M/256) + E
@@ -851,9 +855,19 @@ static int64_t dense_col_step(const GemmArgs& a)
     return a.N <= max_cols ? a.N : (max_cols / 1792) * 1792;
 }
 
+// Grouped grids (one block per tile, an upper bound on the row tiles for
+// row-grouped GEMMs, every expert padded to 8 blocks for contraction-grouped
+// ones) must fit the kernels' int block indices, at either tile width.
+static bool grouped_grid_fits(const GemmArgs& a)
+{
+    const int64_t tiles_m = (a.M + kTM - 1) / kTM, tiles_n = (a.N + 223) / 224;
+    const int64_t lim = (1ll << 31) - 1;
+    return (tiles_m + a.E) * tiles_n <= lim && ((tiles_m * tiles_n + 7) & ~7ll) * a.E <= lim;
+}
+
 bool gemm_supported(const GemmArgs& a, bool grouped)
 {
-    if (grouped) return gemm_offsets_fit(a) && a.M < (1ll << 31) && a.E < (1ll << 16);
+    if (grouped) return gemm_offsets_fit(a) && a.M < (1ll << 31) && a.E < (1ll << 16) && grouped_grid_fits(a);
     return dense_row_step(a) > 0 && dense_col_step(a) > 0;
 }
 

@@ -164,6 +164,8 @@ def test_grouped_validation():
     assert g(E=-1) == E_SHAPE
     # operands whose byte offsets do not fit 32 bits; more than 65535 experts
     assert g(R=1 << 20, K=8192) == E_UNSUP
+    # every offset fits, but the grid (one block per tile) would not fit an int
+    assert g(E=65535, R=1 << 25, N=1 << 25, K=128) == E_UNSUP
     assert g(E=1 << 16) == E_SHAPE
     w = lambda **k: L.fgb_gemm_wgrad_grouped(k.get("E", 4), P(0x60000), k.get("R", 512), 128, 128, A, B, C_, D,
                                              k.get("dw", P(0x50000)), 0, None)
