@@ -51,8 +51,11 @@ __device__ uint32_t bf16_rne_f64(double v) {
 // from every midpoint, so below |c| = 2^-36 the correction only breaks a tie;
 // above it hi + hi*c keeps the correction in fp64 (17 + 36 = 53 bits).
 __device__ uint32_t bf16_scaled_f64(double hi, double c, int c_sign) {
+    // a zero product keeps its sign (hi * (1 + c), 1 + c > 0); hi + hi*c would
+    // turn -0 into +0 where hi*c is +0
+    if (hi == 0.0) return bf16_rne_f64(hi);
     if (fabs(c) >= 0x1p-36) return bf16_rne_f64(hi + hi * c);
-    if (hi == 0.0 || c_sign == 0) return bf16_rne_f64(hi);
+    if (c_sign == 0) return bf16_rne_f64(hi);
     int ex;
     frexp(fabs(hi), &ex);
     ex -= 1;                                        // |hi| in [2^ex, 2^(ex+1))

@@ -834,8 +834,11 @@ static uint16_t bf16_round_ld(long double v)
  * relative) survives. */
 static uint16_t bf16_of_scaled(long double hi, long double c, int c_sign)
 {
+    /* an exact zero product keeps its sign, as hi * (1 + c) does with 1 + c > 0
+     * (hi + hi*c would turn -0 into +0 when hi*c is +0) */
+    if (hi == 0.0L) return bf16_round_ld(hi);
     if (fabsl(c) >= ldexpl(1.0L, -40)) return bf16_round_ld(hi + hi * c);
-    if (hi == 0.0L || c_sign == 0) return bf16_round_ld(hi);
+    if (c_sign == 0) return bf16_round_ld(hi);
     uint16_t sign = signbit(hi) ? 0x8000 : 0x0000;
     long double a = fabsl(hi);
     int e2;

@@ -241,3 +241,30 @@ def test_zero_gate_keeps_ties_to_even(orc):
     dgu = orc.swiglu_dgu(q, s, dh)
     assert list(dgu[:, 0]) == [0x4302, 0x4306]            # 130.0, 134.0
     assert np.all((dgu[:, F] & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("zero", [0x0000, 0x8000])
+def test_zero_products_take_the_ieee_sign(orc, zero):
+    """A product with a zero factor is a zero whose sign is the product's, as
+    float64 arithmetic in torch gives it: H = silu(g) * (+-0) at every finite
+    gate; in the backward dU = dH * silu(G~) and dG = dH * U~ * silu'(G~) with
+    dH = +-0 (torch's float64 silu and autograd derivative)."""
+    z = -0.0 if zero == 0x8000 else 0.0
+    g_all = all_finite_bf16()
+    gf = bf16_f64(g_all)
+    F = 128
+    n = g_all.size - g_all.size % F
+    gu = np.concatenate([g_all[:n].reshape(-1, F), np.full((n // F, F), zero, np.uint16)], axis=1)
+    h = orc.swiglu_h(gu).reshape(-1)
+    assert np.array_equal(h, bf16_exact(torch_silu(gf[:n]) * z))
+    R = g_all.size
+    q = np.zeros((R, 2 * F), np.uint8)
+    q[:, 0] = 0x38
+    q[:, F] = 0x38
+    s = np.zeros((2, R), np.float32)
+    s[0] = gf.astype(np.float32)
+    s[1] = 1.0
+    dh = np.full((R, F), zero, np.uint16)
+    dgu = orc.swiglu_dgu(q, s, dh)
+    assert np.array_equal(dgu[:, 0], bf16_exact(torch_dsilu(gf) * 1.0 * z))
+    assert np.array_equal(dgu[:, F], bf16_exact(torch_silu(gf) * z))
