@@ -200,9 +200,11 @@ int fgb_quantize_128x128_sr(const uint16_t* w, int64_t K, int64_t N, int64_t ldw
  * The gate/up output is ONE bf16 tensor gu [R][2F] (ldgu >= 2F): G is
  * columns 0..F-1, U columns F..2F-1; F % 128 == 0 so no tile straddles the
  * two halves.  silu(g) = g / (1 + exp(-g)).  Every bf16 result below is the
- * exact real value rounded ONCE to bf16 (to nearest, ties to even); the
- * quantizations are exactly fgb_quantize_1x128 / fgb_quantize_128x1 of the
- * bf16 tensors named.  Inputs and results must be finite.
+ * exact real value rounded ONCE to bf16 (to nearest, ties to even), and a
+ * zero result carries the sign the product has in IEEE arithmetic (e.g.
+ * silu(g) * (+0) = -0 for g < 0); the quantizations are exactly
+ * fgb_quantize_1x128 / fgb_quantize_128x1 of the bf16 tensors named.  Inputs
+ * and results must be finite.
  * ---------------------------------------------------------------------- */
 
 /* Forward: H = bf16(silu(G) * U) [R][F].  Writes the 1x128 stash of gu
