@@ -357,3 +357,17 @@ def test_quantizers_beyond_2g_elements(orc):
         assert_codes_equal(qw[b * T:(b + 1) * T], oqw, f"128x128 q block {b}")
         assert_codes_equal(block_cols(qwT, b), oqwT, f"128x128 qT block {b}")
         assert_scales_equal(sw[b:b + 1], osw, f"128x128 s block {b}")
+
+
+def test_128x128_batched_floor(orc):
+    """The batched weight cast with an absmax floor: every matrix as the oracle's
+    single-matrix quantization under the same floor."""
+    E, K, N = 3, 256, 384
+    ws = [stress(K, N, 9700 + e) for e in range(E)]
+    w = torch.stack([bf16_dev(x) for x in ws])
+    q, qT, s = fgb.quantize_128x128_batched(w, amax_floor=2.0)
+    for e in range(E):
+        oq, oqT, os_ = orc.quantize_128x128(ws[e], amax_floor=2.0)
+        assert_codes_equal(q[e], oq, f"batched floor q[{e}]")
+        assert_codes_equal(qT[e], oqT, f"batched floor qT[{e}]")
+        assert_scales_equal(s[e], os_, f"batched floor s[{e}]")

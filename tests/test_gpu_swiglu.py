@@ -26,9 +26,9 @@ def bits(t):
     return host(t.view(torch.int16)).view(np.uint16)
 
 
-def check_fwd(orc, gu, name):
-    q_gu, s_gu, q_h, s_h, h = fgb.swiglu_fwd_quant(bf16_dev(gu), want_h=True)
-    oq_gu, os_gu, oq_h, os_h, oh = orc.swiglu_fwd_quant(gu)
+def check_fwd(orc, gu, name, floor=0.0):
+    q_gu, s_gu, q_h, s_h, h = fgb.swiglu_fwd_quant(bf16_dev(gu), amax_floor=floor, want_h=True)
+    oq_gu, os_gu, oq_h, os_h, oh = orc.swiglu_fwd_quant(gu, amax_floor=floor)
     hb = bits(h)
     if not np.array_equal(hb, oh):
         bad = np.argwhere(hb != oh)
@@ -41,9 +41,10 @@ def check_fwd(orc, gu, name):
     return oq_gu, os_gu                                  # the backward's inputs come from the oracle
 
 
-def check_bwd(orc, q_gu, s_gu, dh, name):
-    q, s, qT, sT, dgu = fgb.swiglu_bwd_quant(u8_dev(q_gu), f32_dev(s_gu), bf16_dev(dh), want_dgu=True)
-    odgu, oq, os_, oqT, osT = orc.swiglu_bwd_quant(q_gu, s_gu, dh)
+def check_bwd(orc, q_gu, s_gu, dh, name, floor=0.0):
+    q, s, qT, sT, dgu = fgb.swiglu_bwd_quant(u8_dev(q_gu), f32_dev(s_gu), bf16_dev(dh), amax_floor=floor,
+                                             want_dgu=True)
+    odgu, oq, os_, oqT, osT = orc.swiglu_bwd_quant(q_gu, s_gu, dh, amax_floor=floor)
     db = bits(dgu)
     if not np.array_equal(db, odgu):
         bad = np.argwhere(db != odgu)
@@ -116,6 +117,18 @@ def test_ragged_round_trip(orc, R, F):
     q_gu, s_gu = check_fwd(orc, gu, f"fwd {R}x{F}")
     dh = wl.bf16_bits((rng.standard_normal((R, F)) * 1e-3).astype(np.float32))
     check_bwd(orc, q_gu, s_gu, dh, f"bwd {R}x{F}")
+
+
+@pytest.mark.parametrize("floor", [1e-4, 3.0])
+def test_amax_floor(orc, floor):
+    """The fused casts with an absmax floor: rows of magnitude 10^U(-6, 1), so that
+    some tiles of [G | U], H and [dG | dU] lie below the floor and others above."""
+    rng = np.random.default_rng(31)
+    R, F = 257, 256
+    gu = wl.bf16_bits((rng.standard_normal((R, 2 * F)) * np.power(10.0, rng.uniform(-6, 1, (R, 1)))).astype(np.float32))
+    q_gu, s_gu = check_fwd(orc, gu, f"fwd floor {floor}", floor)
+    dh = wl.bf16_bits((rng.standard_normal((R, F)) * np.power(10.0, rng.uniform(-4, 2, (R, 1)))).astype(np.float32))
+    check_bwd(orc, q_gu, s_gu, dh, f"bwd floor {floor}", floor)
 
 
 def test_stash_optional_and_strided(orc):
