@@ -375,3 +375,29 @@ def test_fprop_operand_beyond_4gib(orc, side):
     check_gemm(got, r, aabs, True, f"fprop beyond 4 GiB ({side})",
                hw_bound_fprop(qx, sx, qwT, sw, rows=rows, cols=cols), K // T,
                model=model_fprop(qx, sx, qwT, sw, rows, cols))
+
+
+def test_wgrad_operand_beyond_4gib(orc):
+    """Wgrad over 600000 tokens (4688 contraction blocks): X^T [7168, 600064] is
+    4.30 GB, so the host cuts dW's rows after 6912.  Sampled rows on both sides of
+    the cut and at the ends, sampled columns, against the oracle."""
+    g = np.random.default_rng(4343)
+    K, N, M = 7168, 256, 600000
+    Mp = -(-M // T) * T
+    nb = Mp // T
+    print(f"generating {K * Mp / 1e9:.2f} GB of codes", flush=True)
+    qxT, qdyT = big_codes(g, K, Mp), big_codes(g, N, Mp)
+    qxT[:, M:] = 0
+    qdyT[:, M:] = 0
+    assert (K - 1) * Mp + T > (1 << 32)
+    sxT, sdyT = rand_scales(g, (nb, K)), rand_scales(g, (nb, N))
+    dw = fgb.gemm_wgrad(u8_dev(qxT), f32_dev(sxT), u8_dev(qdyT), f32_dev(sdyT), M)
+    torch.cuda.synchronize()
+    cut = 6912
+    rows = np.unique(np.concatenate([[0, 1, cut - 2, cut - 1, cut, cut + 1, K - 2, K - 1], g.choice(K, 8, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, N - 1], g.choice(N, 11, replace=False)]))
+    r, aabs = orc.gemm_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols)
+    ri, ci = torch.as_tensor(rows, device=dw.device), torch.as_tensor(cols, device=dw.device)
+    got = host(dw[ri][:, ci].contiguous()).astype(np.float64)
+    check_gemm(got, r, aabs, False, "wgrad beyond 4 GiB", hw_bound_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols), nb,
+               model=model_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols))
