@@ -401,3 +401,25 @@ def test_wgrad_operand_beyond_4gib(orc):
     got = host(dw[ri][:, ci].contiguous()).astype(np.float64)
     check_gemm(got, r, aabs, False, "wgrad beyond 4 GiB", hw_bound_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols), nb,
                model=model_wgrad(qxT, sxT, qdyT, sdyT, M, rows, cols))
+
+
+def test_dgrad_operand_beyond_4gib(orc):
+    """Dgrad with W [540672, 8192] (4.43 GB): dX's columns are cut after 523264,
+    and each piece takes its own rows of W's 128x128 scale grid.  Sampled columns
+    on both sides of the cut, every row, against the oracle."""
+    g = np.random.default_rng(4444)
+    M, K, N = 256, 540672, 8192
+    print(f"generating {K * N / 1e9:.2f} GB of codes", flush=True)
+    qdy, qw = big_codes(g, M, N), big_codes(g, K, N)
+    assert (K - 1) * N + T > (1 << 32)
+    sdy, sw = rand_scales(g, (N // T, M)), rand_scales(g, (K // T, N // T))
+    dx = fgb.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw))
+    torch.cuda.synchronize()
+    cut = 523264
+    cols = np.unique(np.concatenate([[0, 1, cut - 2, cut - 1, cut, cut + 1, K - 2, K - 1], g.choice(K, 56, replace=False)]))
+    rows = np.arange(M, dtype=np.int64)[::8]
+    r, aabs = orc.gemm_dgrad(qdy, sdy, qw, sw, rows, cols)
+    ri, ci = torch.as_tensor(rows, device=dx.device), torch.as_tensor(cols, device=dx.device)
+    got = bf16_host_f64(dx[ri][:, ci].contiguous())
+    check_gemm(got, r, aabs, True, "dgrad beyond 4 GiB", hw_bound_dgrad(qdy, sdy, qw, sw, rows, cols), N // T,
+               model=model_dgrad(qdy, sdy, qw, sw, rows, cols))
