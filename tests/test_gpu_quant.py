@@ -371,3 +371,23 @@ def test_128x128_batched_floor(orc):
         assert_codes_equal(q[e], oq, f"batched floor q[{e}]")
         assert_codes_equal(qT[e], oqT, f"batched floor qT[{e}]")
         assert_scales_equal(s[e], os_, f"batched floor s[{e}]")
+
+
+def test_128x128_batched_beyond_4gib(orc):
+    """The batched weight cast over 80 experts of [7168, 4096] (4.70 GB of bf16,
+    2.35e9 elements): the first expert, the one that holds element 2^31 and the
+    last, bit-exact against the oracle's single-matrix quantization."""
+    g = np.random.default_rng(41)
+    E, K, N = 80, 7168, 4096
+    assert E * K * N > (1 << 31) and E * K * N * 2 > (1 << 32)
+    table = wide_table()
+    print(f"generating {E * K * N * 2 / 1e9:.2f} GB of bf16 weights", flush=True)
+    w = np.empty((E, K, N), np.uint16)
+    for e in range(E):
+        w[e] = table[g.integers(0, 1 << 16, (K, N), dtype=np.uint16)]
+    q, qT, s = fgb.quantize_128x128_batched(bf16_dev(w.reshape(E * K, N)).view(E, K, N))
+    for e in (0, (1 << 31) // (K * N), E - 1):
+        oq, oqT, os_ = orc.quantize_128x128(w[e])
+        assert_codes_equal(q[e], oq, f"batched q[{e}]")
+        assert_codes_equal(qT[e], oqT, f"batched qT[{e}]")
+        assert_scales_equal(s[e], os_, f"batched s[{e}]")
