@@ -86,8 +86,8 @@ MUTANTS = {
     "dsilu_large_gate_split_sign": ("return bf16_of_scaled(f, c, 1);", "return bf16_of_scaled(f, c, -1);"),
     "sigma_negative_branch": ("*sig = e / (1.0L + e);", "*sig = 1.0L / (1.0L + e);"),
     "bf16_ld_ties_up": ("(fmodl(lo, 2.0L) == 0.0L ? lo : lo + 1.0L)", "(lo + 1.0L)"),
-    "zero_gate_tie_broken": ("if (hi == 0.0L || c_sign == 0) return bf16_round_ld(hi);",
-                             "if (hi == 0.0L) return bf16_round_ld(hi);"),
+    "zero_gate_tie_broken": ("if (c_sign == 0) return bf16_round_ld(hi);", "/* tie at a zero gate broken */"),
+    "zero_product_sign_dropped": ("if (hi == 0.0L) return bf16_round_ld(hi);", "/* zero through hi + hi*c */"),
     "swiglu_up_read_from_gate": ("long double u = orc_bf16_to_float(gu[r * ldgu + F + c]);",
                                  "long double u = orc_bf16_to_float(gu[r * ldgu + c]);"),
     "swiglu_bwd_dequant_no_bf16": ("long double g = orc_bf16_to_float(orc_bf16_round((double)gq));",
